@@ -1,0 +1,151 @@
+"""Pins for the oracle's count-aware mean proxies (OpenAttention page, method
+stage 04: each cluster's unread tokens fold into one virtual token whose logit
+is the mean member logit plus log n_b and whose value is the members' mean).
+"""
+import numpy as np
+import pytest
+
+from long_context_sparse_gathered_amd import synth
+
+
+def _rand(rng, B, Hq, Hkv, n, d):
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    K = (rng.standard_normal((B, Hkv, n, d)) + 0.3).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, n, d)).astype(np.float32)
+    return q, K, V
+
+
+def test_hand_worked_single_proxy(orc):
+    """d = 1, scale = 1, q = 1. Rows: k = 0, 1, 2 with v = 1, 5, -1.
+    Row 0 is read; rows 1 and 2 form one cluster.  The proxy has mean key 1.5,
+    mean value 2 and logit 1.5 + ln 2, so
+        O = (e^0 * 1 + 2 e^1.5 * 2) / (e^0 + 2 e^1.5)."""
+    q = np.array([[[1.0]]], np.float32)
+    K = np.array([[[[0.0], [1.0], [2.0]]]], np.float32)
+    V = np.array([[[[1.0], [5.0], [-1.0]]]], np.float32)
+    cid = np.array([[[-1, 0, 0]]], np.int32)
+    idx = np.array([[[0]]], np.int32)
+    out, lse = orc.sparse_proxy_def(q, K, V, idx, cid, 1, scale=1.0)
+    e = np.exp(1.5)
+    assert out[0, 0, 0] == pytest.approx((1.0 + 4.0 * e) / (1.0 + 2.0 * e), rel=1e-15)
+    assert lse[0, 0] == pytest.approx(np.log(1.0 + 2.0 * e), rel=1e-15)
+    # equal keys inside the cluster make the proxy exact: dense result
+    K2 = np.array([[[[0.0], [1.0], [1.0]]]], np.float32)
+    out2, _ = orc.sparse_proxy_def(q, K2, V, idx, cid, 1, scale=1.0)
+    dense, _ = orc.dense(q, K2, V, scale=1.0)
+    assert out2[0, 0, 0] == pytest.approx(dense[0, 0, 0], rel=1e-15)
+    assert out2[0, 0, 0] == pytest.approx((1.0 + 4.0 * np.e) / (1.0 + 2.0 * np.e), rel=1e-15)
+
+
+def test_singleton_clusters_equal_dense(orc):
+    rng = np.random.default_rng(7)
+    B, Hq, Hkv, n, d, m = 2, 8, 2, 300, 128, 25
+    q, K, V = _rand(rng, B, Hq, Hkv, n, d)
+    cid = np.broadcast_to(np.arange(n, dtype=np.int32), (B, Hkv, n)).copy()
+    idx = np.stack([np.stack([np.sort(rng.choice(n, m, replace=False)) for _ in range(Hkv)]) for _ in range(B)])
+    idx = idx.astype(np.int32)
+    out, lse = orc.sparse_proxy_def(q, K, V, idx, cid, n)
+    o_d, l_d = orc.dense(q, K, V)
+    np.testing.assert_allclose(out, o_d, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, l_d, rtol=1e-13)
+    cnt, sK, sV = orc.proxy_build(K, V, cid, n)
+    out2, _ = orc.sparse_proxy(q, K, V, idx, cid, n, cnt, sK, sV)
+    np.testing.assert_allclose(out2, o_d, rtol=1e-12, atol=1e-13)
+
+
+def test_constant_clusters_equal_dense(orc):
+    """If every cluster's members share one key and one value, a proxy term
+    exp(s + ln n_b) v = n_b exp(s) v is exactly the members' contribution."""
+    rng = np.random.default_rng(8)
+    B, Hq, Hkv, n, d, C, m = 1, 4, 2, 240, 64, 12, 30
+    q = rng.standard_normal((B, Hq, d)).astype(np.float32)
+    cid = np.broadcast_to(np.repeat(np.arange(C), n // C).astype(np.int32), (B, Hkv, n)).copy()
+    ck = rng.standard_normal((B, Hkv, C, d)).astype(np.float32)
+    cv = rng.standard_normal((B, Hkv, C, d)).astype(np.float32)
+    K = np.take_along_axis(ck, cid[..., None].astype(np.int64), axis=2)
+    V = np.take_along_axis(cv, cid[..., None].astype(np.int64), axis=2)
+    idx = np.stack([np.stack([np.sort(rng.choice(n, m, replace=False)) for _ in range(Hkv)])]).astype(np.int32)
+    out, lse = orc.sparse_proxy_def(q, K, V, idx, cid, C)
+    o_d, l_d = orc.dense(q, K, V)
+    np.testing.assert_allclose(out, o_d, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, l_d, rtol=1e-12)
+
+
+def test_full_read_and_no_clusters(orc):
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, n, d = 1, 2, 1, 64, 32
+    q, K, V = _rand(rng, B, Hq, Hkv, n, d)
+    cid = (np.arange(n) // 8).astype(np.int32)[None, None]
+    full = np.arange(n, dtype=np.int32)[None, None]
+    o1, _ = orc.sparse_proxy_def(q, K, V, full, cid, 8)
+    o_d, _ = orc.dense(q, K, V)
+    np.testing.assert_allclose(o1, o_d, rtol=1e-12, atol=1e-13)
+    # no row in any cluster: plain sparse attention
+    idx = np.array([[[1, 5, 9, 40]]], np.int32)
+    none = np.full_like(cid, -1)
+    o2, _ = orc.sparse_proxy_def(q, K, V, idx, none, 8)
+    o3, _ = orc.sparse(q, K, V, idx)
+    np.testing.assert_allclose(o2, o3, rtol=1e-14, atol=1e-15)
+
+
+def test_build_matches_numpy_segment_sums(orc):
+    rng = np.random.default_rng(10)
+    B, Hkv, n, d, C = 2, 3, 500, 16, 7
+    K = rng.standard_normal((B, Hkv, n, d)).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, n, d)).astype(np.float32)
+    cid = rng.integers(-1, C, size=(B, Hkv, n)).astype(np.int32)
+    cnt, sK, sV = orc.proxy_build(K, V, cid, C)
+    for s in range(B):
+        for g in range(Hkv):
+            keep = cid[s, g] >= 0
+            c = cid[s, g][keep]
+            np.testing.assert_array_equal(cnt[s, g], np.bincount(c, minlength=C))
+            rK = np.zeros((C, d))
+            np.add.at(rK, c, K[s, g][keep].astype(np.float64))
+            rV = np.zeros((C, d))
+            np.add.at(rV, c, V[s, g][keep].astype(np.float64))
+            np.testing.assert_allclose(sK[s, g], rK, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(sV[s, g], rV, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_method_form_equals_definition_on_workload_units(orc, name):
+    """The O(|I|) subtraction form equals the O(n) definition (same math,
+    different order) on generated units, including general cluster ids."""
+    w = synth.WORKLOADS[name]
+    for (s, g) in [(0, 0)] if w.Hkv == 1 else [(0, 0), (0, 5)]:
+        c = synth.unit_case(w, s, g)
+        cnt, sK, sV = orc.proxy_build(c.K, c.V, c.cid, w.C)
+        o_def, l_def = orc.sparse_proxy_def(c.q, c.K, c.V, c.idx, c.cid, w.C)
+        o_fast, l_fast = orc.sparse_proxy(c.q, c.K, c.V, c.idx, c.cid, w.C, cnt, sK, sV)
+        np.testing.assert_allclose(o_fast, o_def, rtol=1e-10, atol=1e-11)
+        np.testing.assert_allclose(l_fast, l_def, rtol=1e-12)
+    # a random (non-contiguous) clustering with ragged lists
+    rng = np.random.default_rng(12)
+    cid = rng.integers(-1, 9, size=c.cid.shape).astype(np.int32)
+    lens = np.array([[c.idx.shape[-1] // 2]], np.int32)
+    cnt, sK, sV = orc.proxy_build(c.K, c.V, cid, 9)
+    o_def, _ = orc.sparse_proxy_def(c.q, c.K, c.V, c.idx, cid, 9, idx_len=lens)
+    o_fast, _ = orc.sparse_proxy(c.q, c.K, c.V, c.idx, cid, 9, cnt, sK, sV, idx_len=lens)
+    np.testing.assert_allclose(o_fast, o_def, rtol=1e-10, atol=1e-11)
+
+
+def test_method_form_rejects_duplicates(orc):
+    q = np.ones((1, 1, 4), np.float32)
+    K = np.ones((1, 1, 8, 4), np.float32)
+    cid = np.zeros((1, 1, 8), np.int32)
+    cnt, sK, sV = orc.proxy_build(K, K, cid, 1)
+    with pytest.raises(ValueError):
+        orc.sparse_proxy(q, K, K, np.array([[[2, 2]]], np.int32), cid, 1, cnt, sK, sV)
+
+
+def test_proxy_moves_output_towards_dense(orc):
+    """On the generated 4K workload the proxies recover most of the error that
+    dropping the tail makes (the pages' motivation; a sanity check, not a bound)."""
+    c = synth.make_case(synth.WORKLOADS["c1"])
+    o_d, _ = orc.dense(c.q, c.K, c.V)
+    o_s, _ = orc.sparse(c.q, c.K, c.V, c.idx)
+    o_p, _ = orc.sparse_proxy_def(c.q, c.K, c.V, c.idx, c.cid, c.w.C)
+    err_drop = np.abs(o_s - o_d).max()
+    err_proxy = np.abs(o_p - o_d).max()
+    assert err_proxy < err_drop

@@ -1,0 +1,173 @@
+"""Pins for the oracle's sampled tail (vAttention page, method sections 1-3):
+the counter-based generator, the rank -> position map, the CLT budget, and the
+estimator's unbiasedness."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from long_context_sparse_gathered_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_splitmix64_known_answers(orc):
+    kat = json.load(open(os.path.join(GOLDEN, "splitmix64_kat.json")))
+    got = orc.splitmix64_stream(kat["seed"], len(kat["outputs"]))
+    assert got == [int(x) for x in kat["outputs"]]
+
+
+def test_unit_key_and_draws_are_stream_outputs(orc):
+    """unit_key(seed, u) is output u of the generator seeded with seed; draw k
+    maps output k of the key's stream to floor(x * n_s / 2^64)."""
+    seed = 0xDEADBEEF12345678
+    stream = orc.splitmix64_stream(seed, 40)
+    for u in (0, 1, 17, 39):
+        assert orc.unit_key(seed, u) == stream[u]
+    key = orc.unit_key(seed, 5)
+    ks = orc.splitmix64_stream(key, 30)
+    for n_s in (1, 7, 64748, 2**31 - 1):
+        for k in (0, 3, 29):
+            assert orc.draw_rank(key, k, n_s) == (ks[k] * n_s) >> 64
+
+
+def test_draw_ranks_are_uniform(orc):
+    """Chi-square test of 20000 draws over 50 equal bins (fixed seed)."""
+    key = orc.unit_key(4004, 3)
+    n_s = 1000
+    r = np.array([orc.draw_rank(key, k, n_s) for k in range(20000)])
+    assert r.min() >= 0 and r.max() < n_s
+    hist = np.bincount(r // 20, minlength=50)
+    chi2 = ((hist - 400.0) ** 2 / 400.0).sum()
+    assert chi2 < 100.0  # 49 dof: P(chi2 > 100) ~ 2e-5
+
+
+@pytest.mark.parametrize("n,If", [
+    (10, []), (10, [0]), (10, [9]), (10, [0, 1, 2]), (12, [3, 4, 8, 11]),
+    (50, sorted(np.random.default_rng(1).choice(50, 20, replace=False).tolist())),
+])
+def test_tail_pos_is_enumeration_of_the_unread_positions(orc, n, If):
+    T = np.setdiff1d(np.arange(n), np.array(If, dtype=np.int64))
+    If = np.array(If, np.int32)
+    for u in range(len(T)):
+        assert orc.tail_pos(If, u) == T[u]
+
+
+def test_budget_closed_forms(orc):
+    doc = json.load(open(os.path.join(GOLDEN, "budget_closed_forms.json")))
+    for case in doc["cases"]:
+        b = orc.budget_from_terms(case["rD"], case["rN"], case["Df"], case["Nf"], case["n_s"],
+                                  case["eps"], case["z"])
+        expect = case["bstar_num"] / case["bstar_den"]
+        assert b == pytest.approx(expect, rel=1e-13, abs=1e-12), case["name"]
+        rounded = int(min(case["n_s"], max(1, np.ceil(b))))
+        assert rounded == case["b"], case["name"]
+
+
+def _small_workload(**kw):
+    base = synth.WORKLOADS["c4"].replace(B=1, Hkv=2, Hq=8, n=4096, n_sink=4, n_local=64, n_top=60)
+    return base.replace(**kw)
+
+
+def test_constant_tail_needs_one_sample_and_is_exact(orc):
+    """All unread rows identical: both variances vanish, b = 1, and the single
+    weighted sample reproduces the tail exactly."""
+    w = _small_workload()
+    c = synth.make_case(w)
+    K, V = c.K.copy(), c.V.copy()
+    for g in range(w.Hkv):
+        mask = np.ones(w.n, bool)
+        mask[c.idx[0, g]] = False
+        K[0, g, mask] = K[0, g, 5 if mask[5] else np.argmax(mask)]
+        V[0, g, mask] = V[0, g, 5 if mask[5] else np.argmax(mask)]
+    r = orc.sampled(c.q, K, V, c.idx, w.eps, w.z, w.b0, w.sampler_seed, b_cap=8)
+    # zero up to the rounding of the mean of 64 equal terms
+    assert (r["b"] == 1).all() and (r["bstar"] < 1e-20).all()
+    o_d, l_d = orc.dense(c.q, K, V)
+    np.testing.assert_allclose(r["out"], o_d, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(r["lse"], l_d, rtol=1e-12)
+
+
+def test_no_tail_left_is_exact(orc):
+    w = _small_workload(n=200, n_top=50)
+    c = synth.make_case(w)
+    full = np.broadcast_to(np.arange(w.n, dtype=np.int32), (1, w.Hkv, w.n)).copy()
+    r = orc.sampled(c.q, c.K, c.V, full, w.eps, w.z, w.b0, 1, b_cap=4)
+    assert (r["b"] == 0).all()
+    o_d, _ = orc.dense(c.q, c.K, c.V)
+    np.testing.assert_allclose(r["out"], o_d, rtol=1e-13, atol=1e-14)
+
+
+def test_budget_and_samples_follow_the_stream(orc):
+    """The sampled estimator's b is the rounded maximum over the group's heads
+    of the per-head budget, and its samples are draws b0.. of the unit stream."""
+    w = _small_workload()
+    c = synth.make_case(w)
+    r = orc.sampled(c.q, c.K, c.V, c.idx, w.eps, w.z, w.b0, w.sampler_seed, b_cap=4096)
+    n_s = w.n - w.m
+    qf = synth.bf16_bits_to_f32(c.q).astype(np.float64)
+    Kf = synth.bf16_bits_to_f32(c.K).astype(np.float64)
+    Vf = synth.bf16_bits_to_f32(c.V).astype(np.float64)
+    scale = np.float64(np.float32(1 / np.sqrt(w.d)))
+    for g in range(w.Hkv):
+        key = orc.unit_key(w.sampler_seed, g)
+        If = c.idx[0, g]
+        jb = [orc.tail_pos(If, orc.draw_rank(key, k, n_s)) for k in range(w.b0)]
+        best = 0.0
+        for hh in range(w.G):
+            h = g * w.G + hh
+            sI = Kf[0, g, If] @ qf[0, h] * scale
+            sB = Kf[0, g, jb] @ qf[0, h] * scale
+            M = max(sI.max(), sB.max())
+            eI, eB = np.exp(sI - M), np.exp(sB - M)
+            bh = orc.budget_from_terms(eB, eB[:, None] * Vf[0, g, jb], eI.sum(), eI @ Vf[0, g, If],
+                                       n_s, w.eps, w.z)
+            best = max(best, bh)
+        assert r["bstar"][0, g] == pytest.approx(best, rel=1e-12)
+        b = int(r["b"][0, g])
+        assert b == min(n_s, max(1, int(np.ceil(best))))
+        dyn = [orc.tail_pos(If, orc.draw_rank(key, w.b0 + k, n_s)) for k in range(b)]
+        assert r["samples"][0, g, :b].tolist() == dyn
+        assert not set(dyn) & set(If.tolist())
+
+
+@pytest.mark.slow
+def test_estimator_is_unbiased_over_seeds(orc):
+    """Mean over 1000 seeds of the estimated numerator N and denominator D
+    (fixed b) is within 5 standard errors of the exact sums (the inverse-
+    probability weight n_s/b makes the sampled sum unbiased)."""
+    w = _small_workload(B=1, Hkv=1, Hq=4, n=2048, n_top=40)
+    c = synth.make_case(w)
+    o_d, l_d = orc.dense(c.q, c.K, c.V)
+    D_exact = np.exp(l_d)                       # [1, Hq]
+    N_exact = o_d * D_exact[..., None]
+    S, b = 1000, 32
+    Ds, Ns = [], []
+    for seed in range(S):
+        Dh, Nh = orc.sampled_fixed_b(c.q, c.K, c.V, c.idx, w.b0, b, seed)
+        Ds.append(Dh)
+        Ns.append(Nh)
+    Ds, Ns = np.array(Ds), np.array(Ns)
+    zD = (Ds.mean(0) - D_exact) / (Ds.std(0, ddof=1) / np.sqrt(S))
+    zN = (Ns.mean(0) - N_exact) / (Ns.std(0, ddof=1) / np.sqrt(S))
+    assert np.abs(zD).max() < 5.0
+    assert np.abs(zN).max() < 5.0
+
+
+@pytest.mark.slow
+def test_ratio_error_coverage_is_reported(orc):
+    """Fraction of seeds whose output misses the dense one by more than
+    4*eps relative (Lemma 4.2 with eps1 = eps2 = eps) stays near or below
+    2*delta.  The CLT budget is approximate at small samples, so the bound
+    here is loose: at most 3 * 2 * delta."""
+    w = _small_workload(B=1, Hkv=1, Hq=4, n=4096, n_top=20)
+    c = synth.make_case(w)
+    o_d, _ = orc.dense(c.q, c.K, c.V)
+    miss = 0
+    S = 200
+    for seed in range(S):
+        r = orc.sampled(c.q, c.K, c.V, c.idx, w.eps, w.z, w.b0, seed, b_cap=0)
+        err = np.linalg.norm(r["out"] - o_d, axis=-1) / np.linalg.norm(o_d, axis=-1)
+        miss += int((err > 4 * w.eps).any())
+    assert miss / S <= 3 * 2 * w.delta
