@@ -1,0 +1,219 @@
+/*
+ * sda.h -- C ABI of libsda: sparse decode attention with a tail estimate,
+ * hand-written HIP kernels for MI355X (gfx950).
+ *
+ * One decode step of attention reads only a listed subset I of the KV cache
+ * (attention sinks + local window + selected top-k rows) and adds back an
+ * estimate of the unread tail in the same softmax, in one of three forms:
+ *   PROXY   count-aware mean proxies, one virtual token per cluster
+ *           ("OpenAttention: One Percent Is Enough with Tail Proxies",
+ *           abstract and method stages 04-05);
+ *   SAMPLED inverse-probability-weighted uniform samples of the unread rows
+ *           with a CLT-sized budget ("vAttention: Verified Sparse Attention
+ *           via Sampling", method sections 1-3, eq. 3);
+ *   PRIOR   a rank-1 prior O_Est, Z built once from the mean query and merged
+ *           in O(|I|) ("RESA: Bringing Back What Sparse Attention Ignores
+ *           with Residual Estimation", sections Prior Estimator and Online
+ *           Aggregator).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The
+ *     library never allocates device memory, keeps no state between calls
+ *     and is reentrant.  Scratch memory comes in through (ws, ws_bytes); ask
+ *     sda_workspace_bytes() for the size.  Workspace contents need not be
+ *     initialised and are not preserved.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Nothing synchronises the host.
+ *   - Arguments are validated on the host before any launch; a failed check
+ *     returns an error status and launches nothing.  A failed launch returns
+ *     SDA_EHIP.  Nothing aborts or throws across the ABI.
+ *   - Data errors only the device can see (an index out of range, a list
+ *     that is not strictly increasing where it must be, an inconsistent
+ *     cluster count, samples beyond the caller's buffer) are reported per
+ *     (sequence, KV head) unit in the optional `dev_flags` array as the
+ *     SDA_FLAG_* bits, OR-ed into the word (clear the array before the
+ *     call); the offending entry is skipped, so no access ever leaves the
+ *     caller's buffers.  Read the flags after synchronising.
+ *   - Layouts (row-major, innermost last):
+ *       q        [B, Hq, d]       in dims.dtype
+ *       K, V     [B, Hkv, n, d]   in dims.dtype, element strides in dims
+ *                                 (stride along d is 1; K and V share the
+ *                                 strides, so one interleaved KV buffer
+ *                                 [B, Hkv, n, 2, d] works with V = K + d)
+ *       idx      [B, Hkv, m] int32 row positions; idx_len [B, Hkv] (or NULL)
+ *                 is the number of valid leading entries of each row
+ *       logw     [B, Hkv, m] fp32 natural-log weight added to each listed
+ *                 row's logit (NULL = 0)
+ *       out      [B, Hq, d] fp32;  lse [B, Hq] fp32 = ln(softmax
+ *                 denominator), or NULL
+ *     Query head h attends with KV head h / (Hq / Hkv).
+ *   - The logit of query head h and row j is scale * <q_h, k_j>.
+ *   - Supported: d == 128; Hq / Hkv in {1, 2, 4, 8}; dtype bf16 or fp32.
+ */
+#ifndef SDA_H
+#define SDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SDA_OK = 0,
+  SDA_EINVAL = -1,        /* null pointer, bad scalar parameter, bad kind */
+  SDA_ESHAPE = -2,        /* inconsistent or non-positive sizes/strides   */
+  SDA_EDTYPE = -3,        /* unknown element type                          */
+  SDA_EWORKSPACE = -4,    /* workspace missing or smaller than required    */
+  SDA_EUNSUPPORTED = -5,  /* valid but not implemented (e.g. d != 128)     */
+  SDA_EHIP = -6           /* a HIP call or kernel launch failed            */
+} sda_status;
+
+typedef enum { SDA_BF16 = 0, SDA_F32 = 1 } sda_dtype;
+
+typedef enum {
+  SDA_TAIL_NONE = 0,
+  SDA_TAIL_PROXY = 1,
+  SDA_TAIL_PRIOR = 2,
+  SDA_TAIL_SAMPLED = 3
+} sda_tail_kind;
+
+/* Device-side data error bits, one int32 word per (sequence, KV head). */
+enum {
+  SDA_FLAG_IDX_RANGE = 1,    /* a listed position outside [0, n): skipped  */
+  SDA_FLAG_IDX_ORDER = 2,    /* list not strictly increasing (PROXY, PRIOR,
+                                SAMPLED need distinct sorted positions)     */
+  SDA_FLAG_SAMPLE_CAP = 4,   /* budget b exceeded b_cap: samples_out holds
+                                only the first b_cap draws (the result
+                                itself uses all b)                           */
+  SDA_FLAG_CLUSTER = 8,      /* cluster id outside [-1, C), or more listed
+                                rows in a cluster than its count            */
+  SDA_FLAG_LEN = 16          /* idx_len outside [0, m]: clamped            */
+};
+
+typedef struct {
+  int32_t B, Hq, Hkv, n, d;
+  int32_t dtype;                 /* sda_dtype of q, K and V                 */
+  int64_t kv_stride_b;           /* element strides of K and V; all three   */
+  int64_t kv_stride_h;           /* zero means contiguous [B, Hkv, n, d]    */
+  int64_t kv_stride_n;
+  float scale;                   /* logit scale; 0 means 1/sqrt(d)          */
+} sda_dims;
+
+/* Tail description for sda_sparse_decode_attn.  Fields of kinds other than
+ * `kind` are ignored. */
+typedef struct {
+  int32_t kind;                  /* sda_tail_kind */
+
+  /* PROXY (OpenAttention, method stage 04): per-cluster state from
+   * sda_build_tail_proxies.  Every cluster b with n_b = count[b] - (listed
+   * rows in b) > 0 adds one entry with key sumK_b' / n_b, value
+   * sumV_b' / n_b and logit scale*<q, key> + ln n_b, where the primes
+   * denote the sums without the listed rows.  The list must hold distinct
+   * positions in increasing order. */
+  int32_t C;                     /* clusters per unit, 1 <= C <= 64         */
+  const int32_t* idx_cluster;    /* [B,Hkv,m] cluster of each listed row (as
+                                    a per-cluster selector emits it), or
+                                    NULL to look it up in cluster_id        */
+  const int32_t* cluster_id;     /* [B,Hkv,n] cluster of every row, -1 =
+                                    none; used when idx_cluster is NULL      */
+  const int32_t* count;          /* [B,Hkv,C]                               */
+  const float* sumK;             /* [B,Hkv,C,d]                             */
+  const float* sumV;             /* [B,Hkv,C,d]                             */
+
+  /* PRIOR (RESA): state from sda_build_prior.  With
+   * c_h = scale*<q_h - mu_Q_h, mu_K> every unlisted row j weighs
+   * lambda*exp(scale*<mu_Q_h, k_j> + c_h); listed rows weigh exp(logit).
+   * Evaluated in O(|I|) by the delta merge.  The list must hold distinct
+   * positions in increasing order. */
+  const float* mu_Q;             /* [B,Hq,d]  mean (prefill) query          */
+  const float* mu_K;             /* [B,Hkv,d] key mean                      */
+  const float* O_est;            /* [B,Hq,d]                                */
+  const float* maxP;             /* [B,Hq]                                  */
+  const float* sumP;             /* [B,Hq]                                  */
+  float lambda;                  /* prior weight, >= 0 (0 = plain sparse)   */
+
+  /* SAMPLED (vAttention): idx/idx_len carry the deterministic set I_f
+   * (distinct, increasing).  b0 base draws from the unread rows estimate
+   * the statistics; the budget is b = min(n_s, max(1, ceil(max over the
+   * group's query heads of max(b_D, b_N)))), b_X = (z n_s sigma_X /
+   * (eps |X_hat|))^2; b fresh draws are added with weight n_s / b.
+   * Draw k of unit u = s*Hkv + g is the k-th output of SplitMix64 seeded
+   * with the u-th output of SplitMix64 seeded with `seed`, mapped to the
+   * unread rank floor(x * n_s / 2^64).  Statistics are fp64. */
+  double eps;                    /* relative error target, > 0              */
+  double z;                      /* Phi^-1(1 - delta/2), > 0                */
+  int32_t b0;                    /* base draws, 2 <= b0 <= 1024             */
+  uint64_t seed;
+  int32_t b_cap;                 /* capacity of samples_out per unit        */
+  int32_t* b_out;                /* [B,Hkv] budget b, or NULL               */
+  double* bstar_out;             /* [B,Hkv] real budget before rounding, or
+                                    NULL                                     */
+  int32_t* samples_out;          /* [B,Hkv,b_cap] drawn positions, or NULL  */
+} sda_tail;
+
+typedef enum {
+  SDA_OP_SPARSE = 0,
+  SDA_OP_DENSE = 1,
+  SDA_OP_BUILD_PROXIES = 2,
+  SDA_OP_BUILD_PRIOR = 3
+} sda_op;
+
+/* Workspace bytes an entry point needs for these sizes (m: entries per unit
+ * of the index list, C: clusters; ignored where they do not apply).
+ * Returns 0 for invalid dims. */
+size_t sda_workspace_bytes(const sda_dims* dims, int32_t op, int32_t tail_kind,
+                           int32_t m, int32_t C);
+
+/* Count-aware mean proxy state (OpenAttention, method stage 01: the
+ * per-cluster count and mean tokens cached once per request; here as sums).
+ * For each unit and cluster b: count[b] = #{j : cluster_id[j] == b},
+ * sumK[b] = sum of those keys, sumV[b] = sum of those values (fp32).
+ * cluster_id [B,Hkv,n] int32 in [-1, C); -1 = the row is in no cluster.
+ * Ids outside [-1, C) are ignored and flagged in dev_flags. */
+sda_status sda_build_tail_proxies(const sda_dims* dims, const void* K, const void* V,
+                                  const int32_t* cluster_id, int32_t C,
+                                  int32_t* count, float* sumK, float* sumV,
+                                  int32_t* dev_flags, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* Rank-1 prior state (RESA, Prior Estimator): one extra "typical query"
+ * mu_Q [B,Hq,d] (fp32) attends over the whole cache.  Writes
+ * mu_K [B,Hkv,d] = key mean, maxP [B,Hq] = max_j scale*<mu_Q_h, k_j>,
+ * sumP [B,Hq] = sum_j exp(P_hj - maxP_h) and O_est [B,Hq,d] =
+ * sum_j exp(P_hj - maxP_h) v_j / sumP_h (all fp32).  Requires n >= 1. */
+sda_status sda_build_prior(const sda_dims* dims, const void* K, const void* V,
+                           const float* mu_Q, float* mu_K, float* O_est,
+                           float* maxP, float* sumP, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* One decode step of sparse attention over the listed rows plus the tail
+ * estimate described by `tail` (NULL or kind NONE = no tail: plain sparse
+ * attention with log-weights, duplicates counted as separate terms).
+ * A unit whose softmax is empty gets out = 0 and lse = -inf. */
+sda_status sda_sparse_decode_attn(const sda_dims* dims, const void* q,
+                                  const void* K, const void* V,
+                                  const int32_t* idx, const int32_t* idx_len,
+                                  const float* logw, int32_t m,
+                                  const sda_tail* tail, float* out, float* lse,
+                                  int32_t* dev_flags, void* ws, size_t ws_bytes,
+                                  void* stream);
+
+/* Dense decode attention over all n rows (the speedup reference):
+ * out = softmax(scale * q K^T) V per query head, lse = ln denominator. */
+sda_status sda_dense_decode_attn(const sda_dims* dims, const void* q,
+                                 const void* K, const void* V, float* out,
+                                 float* lse, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* Static description of a status code. */
+const char* sda_status_str(int32_t status);
+
+/* Library version, "major.minor.patch". */
+const char* sda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SDA_H */

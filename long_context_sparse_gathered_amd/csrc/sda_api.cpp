@@ -1,0 +1,351 @@
+// sda_api.cpp -- C ABI entry points of libsda: argument validation,
+// workspace sizing, launch-shape selection and dispatch.  Nothing here
+// allocates device memory or synchronises the host.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "sda.h"
+#include "sda_kernels.hpp"
+
+#define SDA_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using namespace sda;
+
+struct Resolved {
+  int32_t B, Hq, Hkv, n, d, G, dtype;
+  int64_t sb, sh, sn;
+  size_t esize;
+  float scale;
+};
+
+sda_status resolve(const sda_dims* dims, Resolved* r) {
+  if (!dims) return SDA_EINVAL;
+  if (dims->dtype != SDA_BF16 && dims->dtype != SDA_F32) return SDA_EDTYPE;
+  if (dims->B < 1 || dims->Hq < 1 || dims->Hkv < 1 || dims->n < 1 || dims->d < 1) return SDA_ESHAPE;
+  if (dims->Hq % dims->Hkv != 0) return SDA_ESHAPE;
+  if (dims->d != kD) return SDA_EUNSUPPORTED;
+  const int G = dims->Hq / dims->Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return SDA_EUNSUPPORTED;
+  r->B = dims->B;
+  r->Hq = dims->Hq;
+  r->Hkv = dims->Hkv;
+  r->n = dims->n;
+  r->d = dims->d;
+  r->G = G;
+  r->dtype = dims->dtype;
+  r->esize = dims->dtype == SDA_BF16 ? 2 : 4;
+  const bool contiguous = dims->kv_stride_b == 0 && dims->kv_stride_h == 0 && dims->kv_stride_n == 0;
+  if (contiguous) {
+    r->sn = kD;
+    r->sh = (int64_t)dims->n * kD;
+    r->sb = r->sh * dims->Hkv;
+  } else {
+    r->sb = dims->kv_stride_b;
+    r->sh = dims->kv_stride_h;
+    r->sn = dims->kv_stride_n;
+    if (r->sn < kD || r->sh < 0 || r->sb < 0) return SDA_ESHAPE;
+    if (dims->Hkv > 1 && r->sh == 0) return SDA_ESHAPE;
+    if (dims->B > 1 && r->sb == 0) return SDA_ESHAPE;
+  }
+  // rows are read as 16-byte vectors
+  const int64_t align = 16 / (int64_t)r->esize;
+  if (r->sn % align || r->sh % align || r->sb % align) return SDA_ESHAPE;
+  // a unit's rows are addressed with 32-bit byte offsets
+  const int64_t unit_bytes = ((int64_t)(dims->n - 1) * r->sn + kD) * (int64_t)r->esize;
+  if (unit_bytes >= (int64_t)1 << 31) return SDA_EUNSUPPORTED;
+  float scale = dims->scale;
+  if (scale == 0.f) scale = 1.0f / sqrtf((float)kD);
+  if (!(scale > 0.f) || !isfinite(scale)) return SDA_EINVAL;
+  r->scale = scale;
+  return SDA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// Split-K shape for the streaming kernel: enough workgroups to fill the chip
+// several times over, chunks a multiple of one batch of rows (64).
+void stream_shape(int units, int len, int min_chunk, int* splits, int* chunk) {
+  const int target_wgs = 2048;
+  int sp = ceil_div(target_wgs, units);
+  const int max_sp = len > 0 ? ceil_div(len, min_chunk) : 1;
+  if (sp > max_sp) sp = max_sp;
+  if (sp < 1) sp = 1;
+  int ch = ceil_div(len > 0 ? len : 1, sp);
+  ch = ceil_div(ch, 64) * 64;
+  sp = len > 0 ? ceil_div(len, ch) : 1;
+  *splits = sp;
+  *chunk = ch;
+}
+
+struct SparsePlan {
+  bool unit;      // one workgroup per unit
+  int ns;         // slots per wave (unit kernel)
+  int splits, chunk;
+  size_t ws;
+};
+
+sda_status plan_sparse(const Resolved& r, int kind, int m, SparsePlan* pl) {
+  const int units = r.B * r.Hkv;
+  pl->unit = false;
+  pl->ns = 0;
+  pl->splits = 1;
+  pl->chunk = m;
+  pl->ws = 0;
+  if (kind == SDA_TAIL_PROXY) {
+    const int ns = unit_slots_for(m);
+    if (ns == 0) return SDA_EUNSUPPORTED;
+    pl->unit = true;
+    pl->ns = ns;
+    return SDA_OK;
+  }
+  if (kind == SDA_TAIL_NONE) {
+    const int ns = unit_slots_for(m);
+    if (ns != 0 && units >= 128) {
+      pl->unit = true;
+      pl->ns = ns;
+      return SDA_OK;
+    }
+  }
+  if (kind == SDA_TAIL_NONE || kind == SDA_TAIL_PRIOR) {
+    stream_shape(units, m, 256, &pl->splits, &pl->chunk);
+    if (pl->splits > 1) pl->ws = (size_t)units * pl->splits * r.G * kPartStride * sizeof(float);
+    return SDA_OK;
+  }
+  return SDA_EUNSUPPORTED;
+}
+
+void dense_shape(const Resolved& r, int* splits, int* chunk) {
+  stream_shape(r.B * r.Hkv, r.n, 512, splits, chunk);
+}
+
+size_t dense_ws(const Resolved& r, bool build) {
+  int splits, chunk;
+  dense_shape(r, &splits, &chunk);
+  if (splits <= 1) return 0;
+  size_t ws = (size_t)r.B * r.Hkv * splits * r.G * kPartStride * sizeof(float);
+  if (build) ws += (size_t)r.B * r.Hkv * splits * kD * sizeof(float);
+  return ws;
+}
+
+constexpr int kProxyRowsPerChunk = 4096;
+
+size_t proxy_ws(const Resolved& r, int C) {
+  const int chunks = ceil_div(r.n, kProxyRowsPerChunk);
+  const size_t units = (size_t)r.B * r.Hkv;
+  return units * chunks * C * (2 * kD * sizeof(float) + sizeof(int32_t));
+}
+
+void fill_common(const Resolved& r, AttnParams* p) {
+  memset(p, 0, sizeof(*p));
+  p->sb = r.sb;
+  p->sh = r.sh;
+  p->sn = r.sn;
+  p->B = r.B;
+  p->Hq = r.Hq;
+  p->Hkv = r.Hkv;
+  p->n = r.n;
+  p->qscale = r.scale * 1.4426950408889634f;
+  p->q_f32 = r.dtype == SDA_F32;
+  p->splits = 1;
+}
+
+sda_status hip_status(hipError_t e) { return e == hipSuccess ? SDA_OK : SDA_EHIP; }
+
+}  // namespace
+
+SDA_EXPORT const char* sda_version(void) { return "0.1.0"; }
+
+SDA_EXPORT const char* sda_status_str(int32_t status) {
+  switch (status) {
+    case SDA_OK: return "ok";
+    case SDA_EINVAL: return "invalid argument";
+    case SDA_ESHAPE: return "inconsistent shape or stride";
+    case SDA_EDTYPE: return "unknown element type";
+    case SDA_EWORKSPACE: return "workspace missing or too small";
+    case SDA_EUNSUPPORTED: return "unsupported configuration";
+    case SDA_EHIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+SDA_EXPORT size_t sda_workspace_bytes(const sda_dims* dims, int32_t op, int32_t tail_kind, int32_t m,
+                                      int32_t C) {
+  Resolved r;
+  if (resolve(dims, &r) != SDA_OK) return 0;
+  switch (op) {
+    case SDA_OP_SPARSE: {
+      if (m < 0) return 0;
+      SparsePlan pl;
+      if (plan_sparse(r, tail_kind, m, &pl) != SDA_OK) return 0;
+      return pl.ws;
+    }
+    case SDA_OP_DENSE: return dense_ws(r, false);
+    case SDA_OP_BUILD_PRIOR: return dense_ws(r, true);
+    case SDA_OP_BUILD_PROXIES: return (C >= 1 && C <= kCmax) ? proxy_ws(r, C) : 0;
+  }
+  return 0;
+}
+
+SDA_EXPORT sda_status sda_build_tail_proxies(const sda_dims* dims, const void* K, const void* V,
+                                             const int32_t* cluster_id, int32_t C, int32_t* count,
+                                             float* sumK, float* sumV, int32_t* dev_flags, void* ws,
+                                             size_t ws_bytes, void* stream) {
+  Resolved r;
+  sda_status st = resolve(dims, &r);
+  if (st != SDA_OK) return st;
+  if (!K || !V || !cluster_id || !count || !sumK || !sumV) return SDA_EINVAL;
+  if (C < 1 || C > kCmax) return SDA_EUNSUPPORTED;
+  const size_t need = proxy_ws(r, C);
+  if (!ws || ws_bytes < need) return SDA_EWORKSPACE;
+  ProxyBuildParams p;
+  memset(&p, 0, sizeof(p));
+  p.K = K;
+  p.V = V;
+  p.cid = cluster_id;
+  p.sb = r.sb;
+  p.sh = r.sh;
+  p.sn = r.sn;
+  p.Hkv = r.Hkv;
+  p.n = r.n;
+  p.C = C;
+  p.rows_per_chunk = kProxyRowsPerChunk;
+  p.chunks = ceil_div(r.n, kProxyRowsPerChunk);
+  const int units = r.B * r.Hkv;
+  p.part = reinterpret_cast<float*>(ws);
+  p.pcount = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
+                                        (size_t)units * p.chunks * C * 2 * kD * sizeof(float));
+  p.count = count;
+  p.sumK = sumK;
+  p.sumV = sumV;
+  p.flags = dev_flags;
+  return hip_status(launch_proxy_build(p, r.dtype, units, reinterpret_cast<hipStream_t>(stream)));
+}
+
+SDA_EXPORT sda_status sda_build_prior(const sda_dims* dims, const void* K, const void* V, const float* mu_Q,
+                                      float* mu_K, float* O_est, float* maxP, float* sumP, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  Resolved r;
+  sda_status st = resolve(dims, &r);
+  if (st != SDA_OK) return st;
+  if (!K || !V || !mu_Q || !mu_K || !O_est || !maxP || !sumP) return SDA_EINVAL;
+  if (!aligned16(K) || !aligned16(V) || !aligned16(mu_Q)) return SDA_EINVAL;
+  const size_t need = dense_ws(r, true);
+  if (need && (!ws || ws_bytes < need)) return SDA_EWORKSPACE;
+  AttnParams p;
+  fill_common(r, &p);
+  p.q = mu_Q;
+  p.q_f32 = 1;
+  p.K = K;
+  p.V = V;
+  dense_shape(r, &p.splits, &p.chunk);
+  const size_t part_bytes = (size_t)r.B * r.Hkv * p.splits * r.G * kPartStride * sizeof(float);
+  p.part = reinterpret_cast<float*>(ws);
+  p.ksum = p.splits > 1 ? reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + part_bytes) : nullptr;
+  p.out = O_est;
+  p.lse = maxP;
+  p.aux = sumP;
+  p.aux2 = mu_K;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_stream(p, r.dtype, r.G, kModeBuildPrior, hs);
+  if (e == hipSuccess && p.splits > 1) e = launch_merge(p, r.G, kModeBuildPrior, hs);
+  return hip_status(e);
+}
+
+SDA_EXPORT sda_status sda_dense_decode_attn(const sda_dims* dims, const void* q, const void* K, const void* V,
+                                            float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Resolved r;
+  sda_status st = resolve(dims, &r);
+  if (st != SDA_OK) return st;
+  if (!q || !K || !V || !out) return SDA_EINVAL;
+  if (!aligned16(q) || !aligned16(K) || !aligned16(V)) return SDA_EINVAL;
+  const size_t need = dense_ws(r, false);
+  if (need && (!ws || ws_bytes < need)) return SDA_EWORKSPACE;
+  AttnParams p;
+  fill_common(r, &p);
+  p.q = q;
+  p.K = K;
+  p.V = V;
+  dense_shape(r, &p.splits, &p.chunk);
+  p.part = reinterpret_cast<float*>(ws);
+  p.out = out;
+  p.lse = lse;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = launch_stream(p, r.dtype, r.G, kModeDense, hs);
+  if (e == hipSuccess && p.splits > 1) e = launch_merge(p, r.G, kModeDense, hs);
+  return hip_status(e);
+}
+
+SDA_EXPORT sda_status sda_sparse_decode_attn(const sda_dims* dims, const void* q, const void* K, const void* V,
+                                             const int32_t* idx, const int32_t* idx_len, const float* logw,
+                                             int32_t m, const sda_tail* tail, float* out, float* lse,
+                                             int32_t* dev_flags, void* ws, size_t ws_bytes, void* stream) {
+  Resolved r;
+  sda_status st = resolve(dims, &r);
+  if (st != SDA_OK) return st;
+  if (!q || !K || !V || !out) return SDA_EINVAL;
+  if (!aligned16(q) || !aligned16(K) || !aligned16(V)) return SDA_EINVAL;
+  const int kind = tail ? tail->kind : SDA_TAIL_NONE;
+  if (kind < SDA_TAIL_NONE || kind > SDA_TAIL_SAMPLED) return SDA_EINVAL;
+  if (m < 0) return SDA_ESHAPE;
+  if (m > 0 && !idx) return SDA_EINVAL;
+  if (m == 0 && kind == SDA_TAIL_NONE) return SDA_EINVAL;
+
+  AttnParams p;
+  fill_common(r, &p);
+  p.q = q;
+  p.K = K;
+  p.V = V;
+  p.idx = idx;
+  p.idx_len = idx_len;
+  p.logw = logw;
+  p.m = m;
+  p.out = out;
+  p.lse = lse;
+  p.flags = dev_flags;
+
+  if (kind == SDA_TAIL_PROXY) {
+    if (tail->C < 1 || tail->C > kCmax) return SDA_EUNSUPPORTED;
+    if (!tail->count || !tail->sumK || !tail->sumV) return SDA_EINVAL;
+    if (!aligned16(tail->sumK) || !aligned16(tail->sumV)) return SDA_EINVAL;
+    if (m > 0 && !tail->idx_cluster && !tail->cluster_id) return SDA_EINVAL;
+    p.C = tail->C;
+    p.idx_cluster = tail->idx_cluster;
+    p.cluster_id = tail->cluster_id;
+    p.count = tail->count;
+    p.sumK = tail->sumK;
+    p.sumV = tail->sumV;
+  } else if (kind == SDA_TAIL_PRIOR) {
+    if (!tail->mu_Q || !tail->mu_K || !tail->O_est || !tail->maxP || !tail->sumP) return SDA_EINVAL;
+    if (!aligned16(tail->mu_Q) || !aligned16(tail->mu_K)) return SDA_EINVAL;
+    if (!(tail->lambda >= 0.f) || !isfinite(tail->lambda)) return SDA_EINVAL;
+    p.mu_Q = tail->mu_Q;
+    p.mu_K = tail->mu_K;
+    p.O_est = tail->O_est;
+    p.maxP = tail->maxP;
+    p.sumP = tail->sumP;
+    p.lambda = tail->lambda;
+  } else if (kind == SDA_TAIL_SAMPLED) {
+    return SDA_EUNSUPPORTED;
+  }
+
+  SparsePlan pl;
+  st = plan_sparse(r, kind, m, &pl);
+  if (st != SDA_OK) return st;
+  if (pl.ws && (!ws || ws_bytes < pl.ws)) return SDA_EWORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (pl.unit) return hip_status(launch_sparse_unit(p, r.dtype, r.G, kind == SDA_TAIL_PROXY, pl.ns, hs));
+  p.splits = pl.splits;
+  p.chunk = pl.chunk;
+  p.part = reinterpret_cast<float*>(ws);
+  const int mode = kind == SDA_TAIL_PRIOR ? kModePrior : kModeSparse;
+  hipError_t e = launch_stream(p, r.dtype, r.G, mode, hs);
+  if (e == hipSuccess && p.splits > 1) e = launch_merge(p, r.G, mode, hs);
+  return hip_status(e);
+}

@@ -1,0 +1,97 @@
+// sda_kernels.hpp -- kernel parameter blocks and host launchers (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sda.h"
+
+namespace sda {
+
+constexpr int kD = 128;          // head dimension supported by the kernels
+constexpr int kCmax = 64;        // clusters per unit supported by the kernels
+constexpr int kPartStride = 264; // floats per (unit, split, head) partial
+
+// One parameter block for the attention kernels (passed by value).
+struct AttnParams {
+  const void* q;               // [B,Hq,d] dims.dtype, or fp32 when q_f32
+  const void* K;
+  const void* V;
+  const int32_t* idx;          // [B,Hkv,m]        (sparse modes)
+  const int32_t* idx_len;      // [B,Hkv] or null
+  const float* logw;           // [B,Hkv,m] or null
+  int64_t sb, sh, sn;          // K/V element strides
+  int32_t B, Hq, Hkv, n, m;
+  float qscale;                // scale * log2(e)
+  int32_t q_f32;
+
+  // PROXY
+  int32_t C;
+  const int32_t* idx_cluster;
+  const int32_t* cluster_id;
+  const int32_t* count;
+  const float* sumK;
+  const float* sumV;
+
+  // PRIOR
+  const float* mu_Q;
+  const float* mu_K;
+  const float* O_est;
+  const float* maxP;
+  const float* sumP;
+  float lambda;
+
+  // split-K
+  int32_t splits;              // WGs per unit
+  int32_t chunk;               // entries (rows) per split
+  float* part;                 // [units, splits, G, kPartStride]
+  float* ksum;                 // [units, splits, d] (prior build)
+
+  // outputs
+  float* out;                  // [B,Hq,d]   (prior build: O_est)
+  float* lse;                  // [B,Hq]     (prior build: maxP)
+  float* aux;                  // prior build: sumP
+  float* aux2;                 // prior build: mu_K
+  int32_t* flags;              // [B,Hkv] or null
+};
+
+// Stream-kernel modes.
+enum StreamMode { kModeSparse = 0, kModePrior = 1, kModeDense = 2, kModeBuildPrior = 3 };
+
+struct ProxyBuildParams {
+  const void* K;
+  const void* V;
+  const int32_t* cid;          // [B,Hkv,n]
+  int64_t sb, sh, sn;
+  int32_t Hkv, n, C;
+  int32_t rows_per_chunk;
+  int32_t chunks;
+  float* part;                 // [units, chunks, C, 2*d]
+  int32_t* pcount;             // [units, chunks, C]
+  int32_t* count;              // outputs
+  float* sumK;
+  float* sumV;
+  int32_t* flags;
+};
+
+// Host launchers (return hipSuccess or the launch error).
+hipError_t launch_sparse_unit(const AttnParams& p, int dtype, int G, bool proxy, int ns,
+                              hipStream_t st);
+hipError_t launch_stream(const AttnParams& p, int dtype, int G, int mode, hipStream_t st);
+hipError_t launch_merge(const AttnParams& p, int G, int mode, hipStream_t st);
+hipError_t launch_proxy_build(const ProxyBuildParams& p, int dtype, int units, hipStream_t st);
+
+// Largest slot count the one-workgroup-per-unit kernel is built for.
+constexpr int kUnitWaves = 8;
+constexpr int kUnitMaxSlots = 16;
+inline int unit_slots_for(int m) {
+  const int need = (m + 4 * kUnitWaves - 1) / (4 * kUnitWaves);
+  if (need <= 4) return 4;
+  if (need <= 8) return 8;
+  if (need <= 12) return 12;
+  if (need <= 16) return 16;
+  return 0;
+}
+
+}  // namespace sda

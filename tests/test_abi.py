@@ -1,0 +1,148 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects malformed arguments on the host before any
+launch (these calls return before touching HIP, so fake pointers are safe)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_sparse_gathered_amd import sda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x100000)      # never dereferenced on these paths
+FAKE2 = ctypes.c_void_p(0x200000)
+MISALIGNED = ctypes.c_void_p(0x100004)
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(sda.LIB_PATH):
+        pytest.skip("libsda.so not built")
+    return sda.lib()
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"^\s*(?:sda_status|size_t|const char\*)\s+(sda_\w+)\s*\(", text, re.M))
+    return names
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared()
+    assert {"sda_build_tail_proxies", "sda_build_prior", "sda_sparse_decode_attn",
+            "sda_dense_decode_attn", "sda_workspace_bytes"} <= names
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(sda.EXPORTED) == names
+
+
+def test_status_strings_and_version(L):
+    assert sda.status_str(0) == "ok"
+    assert "workspace" in sda.status_str(-4)
+    assert re.match(r"\d+\.\d+\.\d+", sda.version())
+
+
+def _dims(**kw):
+    d = dict(B=2, Hq=8, Hkv=2, n=1024, d=128, dtype=sda.SDA_BF16, kv_stride_b=0, kv_stride_h=0,
+             kv_stride_n=0, scale=0.0)
+    d.update(kw)
+    return sda.Dims(**d)
+
+
+def _sparse(L, dims, tail=None, m=16, q=FAKE, K=FAKE, V=FAKE, idx=FAKE2, ws=None, ws_bytes=0, out=FAKE):
+    t = tail if tail is not None else sda.Tail()
+    return L.sda_sparse_decode_attn(ctypes.byref(dims) if dims is not None else None, q, K, V, idx, None, None,
+                                    m, ctypes.byref(t), out, None, None, ws, ws_bytes, None)
+
+
+def test_dims_validation(L):
+    assert _sparse(L, None) == sda.SDA_EINVAL
+    assert _sparse(L, _dims(dtype=7)) == sda.SDA_EDTYPE
+    assert _sparse(L, _dims(d=64)) == sda.SDA_EUNSUPPORTED
+    assert _sparse(L, _dims(Hq=6, Hkv=4)) == sda.SDA_ESHAPE
+    assert _sparse(L, _dims(Hq=6, Hkv=2)) == sda.SDA_EUNSUPPORTED     # group of 3
+    assert _sparse(L, _dims(n=0)) == sda.SDA_ESHAPE
+    assert _sparse(L, _dims(B=0)) == sda.SDA_ESHAPE
+    # explicit strides: row stride below d, or misaligned for 16-byte loads
+    assert _sparse(L, _dims(kv_stride_b=2 * 1024 * 128, kv_stride_h=1024 * 128, kv_stride_n=64)) == sda.SDA_ESHAPE
+    assert _sparse(L, _dims(kv_stride_b=2 * 1024 * 136, kv_stride_h=1024 * 136, kv_stride_n=132)) == sda.SDA_ESHAPE
+    # a unit too large for 32-bit row offsets
+    assert _sparse(L, _dims(n=1 << 24, dtype=sda.SDA_F32)) == sda.SDA_EUNSUPPORTED
+    assert _sparse(L, _dims(scale=-1.0)) == sda.SDA_EINVAL
+
+
+def test_argument_validation(L):
+    dims = _dims()
+    assert _sparse(L, dims, q=None) == sda.SDA_EINVAL
+    assert _sparse(L, dims, out=None) == sda.SDA_EINVAL
+    assert _sparse(L, dims, K=MISALIGNED) == sda.SDA_EINVAL
+    assert _sparse(L, dims, m=-1) == sda.SDA_ESHAPE
+    assert _sparse(L, dims, m=0) == sda.SDA_EINVAL                    # nothing to attend to
+    assert _sparse(L, dims, idx=None) == sda.SDA_EINVAL
+    bad = sda.Tail()
+    bad.kind = 9
+    assert _sparse(L, dims, tail=bad) == sda.SDA_EINVAL
+
+
+def test_proxy_tail_validation(L):
+    dims = _dims()
+    t = sda.Tail()
+    t.kind = sda.TAIL_PROXY
+    t.C = 0
+    assert _sparse(L, dims, tail=t) == sda.SDA_EUNSUPPORTED
+    t.C = 65
+    assert _sparse(L, dims, tail=t) == sda.SDA_EUNSUPPORTED
+    t.C = 32
+    assert _sparse(L, dims, tail=t) == sda.SDA_EINVAL                 # no state
+    t.count, t.sumK, t.sumV = FAKE, FAKE, FAKE
+    assert _sparse(L, dims, tail=t) == sda.SDA_EINVAL                 # no cluster lookup
+    t.cluster_id = FAKE2
+    assert _sparse(L, dims, tail=t, m=600) == sda.SDA_EUNSUPPORTED    # list longer than one workgroup holds
+
+
+def test_prior_tail_validation(L):
+    dims = _dims()
+    t = sda.Tail()
+    t.kind = sda.TAIL_PRIOR
+    assert _sparse(L, dims, tail=t) == sda.SDA_EINVAL
+    t.mu_Q, t.mu_K, t.O_est, t.maxP, t.sumP = FAKE, FAKE, FAKE, FAKE, FAKE
+    t.lam = -0.5
+    assert _sparse(L, dims, tail=t) == sda.SDA_EINVAL
+    t.lam = float("nan")
+    assert _sparse(L, dims, tail=t) == sda.SDA_EINVAL
+    t.lam = 1.0
+    # B*Hkv = 4 units: the split-K path needs a workspace
+    need = L.sda_workspace_bytes(ctypes.byref(dims), sda.OP_SPARSE, sda.TAIL_PRIOR, 2000, 0)
+    assert need > 0
+    assert _sparse(L, dims, tail=t, m=2000) == sda.SDA_EWORKSPACE
+    assert _sparse(L, dims, tail=t, m=2000, ws=FAKE2, ws_bytes=need - 1) == sda.SDA_EWORKSPACE
+
+
+def test_builder_and_dense_validation(L):
+    dims = _dims()
+    assert L.sda_build_tail_proxies(ctypes.byref(dims), FAKE, FAKE, FAKE, 100, FAKE, FAKE, FAKE, None, FAKE, 1 << 30,
+                                    None) == sda.SDA_EUNSUPPORTED
+    assert L.sda_build_tail_proxies(ctypes.byref(dims), FAKE, FAKE, None, 8, FAKE, FAKE, FAKE, None, FAKE, 1 << 30,
+                                    None) == sda.SDA_EINVAL
+    assert L.sda_build_tail_proxies(ctypes.byref(dims), FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, None, FAKE, 16,
+                                    None) == sda.SDA_EWORKSPACE
+    assert L.sda_build_prior(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, 0,
+                             None) == sda.SDA_EINVAL
+    assert L.sda_dense_decode_attn(ctypes.byref(dims), FAKE, FAKE, FAKE, None, None, None, 0, None) == sda.SDA_EINVAL
+    assert L.sda_dense_decode_attn(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, None, None, 0,
+                                   None) == sda.SDA_EWORKSPACE
+
+
+def test_workspace_sizes(L):
+    c3 = _dims(B=32, Hq=32, Hkv=8, n=32768)
+    assert L.sda_workspace_bytes(ctypes.byref(c3), sda.OP_SPARSE, sda.TAIL_PROXY, 328, 32) == 0
+    dense = L.sda_workspace_bytes(ctypes.byref(c3), sda.OP_DENSE, 0, 0, 0)
+    assert dense > 0 and dense % (4 * 264 * 4) == 0
+    assert L.sda_workspace_bytes(ctypes.byref(c3), sda.OP_BUILD_PRIOR, 0, 0, 0) > dense
+    assert L.sda_workspace_bytes(ctypes.byref(c3), sda.OP_BUILD_PROXIES, 0, 0, 32) > 0
+    assert L.sda_workspace_bytes(ctypes.byref(c3), sda.OP_BUILD_PROXIES, 0, 0, 99) == 0
+    assert L.sda_workspace_bytes(None, sda.OP_DENSE, 0, 0, 0) == 0
