@@ -57,7 +57,7 @@ sda_status resolve(const sda_dims* dims, Resolved* r) {
   if (r->sn % align || r->sh % align || r->sb % align) return SDA_ESHAPE;
   // a unit's rows are addressed with 32-bit byte offsets
   const int64_t unit_bytes = ((int64_t)(dims->n - 1) * r->sn + kD) * (int64_t)r->esize;
-  if (unit_bytes >= (int64_t)1 << 31) return SDA_EUNSUPPORTED;
+  if (unit_bytes > kMaxUnitBytes) return SDA_EUNSUPPORTED;
   float scale = dims->scale;
   if (scale == 0.f) scale = 1.0f / sqrtf((float)kD);
   if (!(scale > 0.f) || !isfinite(scale)) return SDA_EINVAL;
@@ -98,18 +98,36 @@ sda_status plan_sparse(const Resolved& r, int kind, int m, SparsePlan* pl) {
   pl->splits = 1;
   pl->chunk = m;
   pl->ws = 0;
+  // One workgroup per unit: each of its waves owns a contiguous run of
+  // `chunk` list entries.  bf16 takes the matrix-core kernel, whose waves
+  // work in tiles of 16 keys (chunk a multiple of 16, slots = 4 per tile);
+  // fp32 takes the vector kernel (chunk a multiple of 4).
+  int ns = 0, unit_chunk = 0;
+  if (r.dtype == SDA_BF16) {
+    const int tiles = ceil_div(ceil_div(m, kUnitWaves), 16);
+    if (m > 0 && tiles <= 4) {
+      ns = 4 * (tiles > 0 ? tiles : 1);
+      unit_chunk = 16 * tiles;
+    } else if (m == 0) {
+      ns = 4;
+      unit_chunk = 0;
+    }
+  } else {
+    ns = unit_slots_for(m);
+    unit_chunk = 4 * ceil_div(ceil_div(m, kUnitWaves), 4);
+  }
   if (kind == SDA_TAIL_PROXY) {
-    const int ns = unit_slots_for(m);
     if (ns == 0) return SDA_EUNSUPPORTED;
     pl->unit = true;
     pl->ns = ns;
+    pl->chunk = unit_chunk;
     return SDA_OK;
   }
   if (kind == SDA_TAIL_NONE) {
-    const int ns = unit_slots_for(m);
     if (ns != 0 && units >= 128) {
       pl->unit = true;
       pl->ns = ns;
+      pl->chunk = unit_chunk;
       return SDA_OK;
     }
   }
@@ -340,7 +358,10 @@ SDA_EXPORT sda_status sda_sparse_decode_attn(const sda_dims* dims, const void* q
   if (st != SDA_OK) return st;
   if (pl.ws && (!ws || ws_bytes < pl.ws)) return SDA_EWORKSPACE;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if (pl.unit) return hip_status(launch_sparse_unit(p, r.dtype, r.G, kind == SDA_TAIL_PROXY, pl.ns, hs));
+  if (pl.unit) {
+    p.chunk = pl.chunk;
+    return hip_status(launch_sparse_unit(p, r.dtype, r.G, kind == SDA_TAIL_PROXY, pl.ns, hs));
+  }
   p.splits = pl.splits;
   p.chunk = pl.chunk;
   p.part = reinterpret_cast<float*>(ws);

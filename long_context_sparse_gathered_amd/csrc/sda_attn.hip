@@ -16,10 +16,12 @@
 #include "sda_device.hpp"
 #include "sda_kernels.hpp"
 
+#include <type_traits>
+
 namespace sda {
 
 constexpr int kRsrcFlags = 0x00020000;
-constexpr int kOOB = 0x7fffffff;   // byte offset outside every resource range
+constexpr int kOOB = kMaxUnitBytes;  // byte offset past every unit's rows (loads return 0)
 
 using rsrc_t = __amdgpu_buffer_rsrc_t;
 
@@ -37,7 +39,7 @@ __device__ __forceinline__ void buf_load(RowChunk<bf16_t>& c, rsrc_t r, int off)
 }
 __device__ __forceinline__ void buf_load(RowChunk<float>& c, rsrc_t r, int off) {
   auto a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  auto b = __builtin_amdgcn_raw_buffer_load_b128(r, off == kOOB ? kOOB : off + 16, 0, 0);
+  auto b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
   c.a = make_float4(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3]));
   c.b = make_float4(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3]));
 }
@@ -48,12 +50,11 @@ __device__ __forceinline__ int row_off(int64_t j, int64_t sn, int r16) {
 }
 
 // Load the G query heads of KV head g (dims 8*r16..) scaled to log2 units.
-template <int G>
-__device__ __forceinline__ void load_query(const void* q, bool is_f32, int64_t row0, int r16, float qscale,
-                                           float (&qf)[G][8]) {
+template <typename QT, int G>
+__device__ __forceinline__ void load_query(const void* q, int64_t row0, int r16, float qscale, float (&qf)[G][8]) {
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    load_q8(q, (row0 + h) * kD + 8 * r16, is_f32, qf[h]);
+    load_q8<QT>(q, (row0 + h) * kD + 8 * r16, qf[h]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) qf[h][i] *= qscale;
   }
@@ -70,20 +71,27 @@ __device__ __forceinline__ void dot_heads(const float (&qf)[G][8], const float (
   }
 }
 
+__device__ __forceinline__ int shfl_i(int v, int src) { return __shfl(v, src, 64); }
+__device__ __forceinline__ float shfl_f(float v, int src) { return __shfl(v, src, 64); }
+
 // ---------------------------------------------------------------------------
-// One workgroup per unit.  Slot k of wave w holds entries
-// t = 4*(k*W + w) + (lane >> 4): every load instruction fetches four
-// consecutive list entries.
+// One workgroup per unit.  Wave w owns list entries [w*CH, (w+1)*CH): lane l
+// loads entry w*CH + l, and slot k of the wave's row group `sub` takes entry
+// 4k + sub by a lane shuffle.  Every load that does not depend on another
+// load is issued in the prologue, the row gathers right after the list
+// arrives, and all checks run while the rows are in flight.
 template <typename T, int G, bool PROXY, int NS>
 __global__ __launch_bounds__(512) void sparse_unit_kernel(const AttnParams p) {
   constexpr int W = kUnitWaves;
   constexpr int PC = PROXY ? kCmax : 1;
   constexpr int PW = PROXY ? W : 1;
+  constexpr int R = PROXY ? (kCmax * G + 63) / 64 : 1;  // (cluster, head) pairs per lane in wave 0
   const int u = blockIdx.x;
   const int s = u / p.Hkv;
   const int g = u - s * p.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, sub = lane >> 4;
+  const int CH = p.chunk;
 
   __shared__ float s_wmax[W][G];
   __shared__ float s_M[G];
@@ -94,7 +102,41 @@ __global__ __launch_bounds__(512) void sparse_unit_kernel(const AttnParams p) {
   __shared__ int s_ccnt[PW][PC];
   __shared__ float s_qk[PC][G];
   __shared__ float s_cw[PC][G];
-  __shared__ __attribute__((aligned(16))) float s_sv[PC][PROXY ? kD : 1];
+
+  // ---- prologue ------------------------------------------------------------
+  float qf[G][8];
+  load_query<T, G>(p.q, (int64_t)s * p.Hq + (int64_t)g * G, r16, p.qscale, qf);
+
+  const int64_t lbase = (int64_t)u * p.m;
+  const int e = w * CH + lane;
+  const bool in_list = (lane < CH) && (e < p.m);
+  int li = -1, lp = -1, lc = -1;
+  float lwv = 0.f;
+  if (p.m > 0) {
+    const int64_t ea = lbase + (in_list ? e : 0);
+    li = p.idx[ea];
+    if constexpr (PROXY) {
+      lp = p.idx[lbase + ((in_list && e > 0) ? e - 1 : 0)];
+      if (p.idx_cluster) lc = p.idx_cluster[ea];
+    }
+    if (p.logw) lwv = p.logw[ea];
+  }
+
+  float skf[8], svf[8];
+  int cnt[R];
+  const int b0 = 4 * w + sub;  // this row group's first cluster slot
+  if constexpr (PROXY) {
+    const int64_t rb = ((int64_t)u * p.C + (b0 < p.C ? b0 : 0)) * kD + 8 * r16;
+    load8f(p.sumK + rb, skf);
+    load8f(p.sumV + rb, svf);
+    if (w == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int b = (lane + 64 * r) / G;
+        cnt[r] = p.count[(int64_t)u * p.C + (b < p.C ? b : 0)];
+      }
+    }
+  }
 
   int len = p.m;
   if (p.idx_len) {
@@ -105,80 +147,79 @@ __global__ __launch_bounds__(512) void sparse_unit_kernel(const AttnParams p) {
     }
     len = L;
   }
-  if constexpr (PROXY) {
-    // each wave clears its own slice, so program order alone orders the
-    // clears before that wave's accumulations
-#pragma unroll
-    for (int i = lane; i < PC * G; i += 64) (&s_csum[w][0][0])[i] = 0.f;
-    for (int i = lane; i < PC; i += 64) s_ccnt[w][i] = 0;
-  }
 
-  float qf[G][8];
-  load_query<G>(p.q, p.q_f32, (int64_t)s * p.Hq + (int64_t)g * G, r16, p.qscale, qf);
+  // ---- row addresses from the list ----------------------------------------
+  const bool live = in_list && e < len;
+  const bool in_range = (unsigned)li < (unsigned)p.n;
+  const bool valid = live && in_range;
+  const bool bad_cluster = PROXY && p.idx_cluster && valid && (lc < -1 || lc >= p.C);
+  if (bad_cluster) lc = -1;
 
-  const int64_t lbase = (int64_t)u * p.m;
-  const int64_t kvoff = (int64_t)s * p.sb + (int64_t)g * p.sh;
-  const rsrc_t rk = make_rsrc<T>(reinterpret_cast<const T*>(p.K) + kvoff, p.n, p.sn);
-  const rsrc_t rv = make_rsrc<T>(reinterpret_cast<const T*>(p.V) + kvoff, p.n, p.sn);
-
-  // ---- list entries -------------------------------------------------------
   int off[NS];
   float lw[NS];
   int cl[NS];
+  const bool lookup = PROXY && !p.idx_cluster;
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
-    const int t = 4 * (k * W + w) + sub;
-    int o = kOOB, c = -1;
-    float lwk = kNegInf;
-    if (t < len) {
-      const int j = p.idx[lbase + t];
-      if ((unsigned)j < (unsigned)p.n) {
-        o = row_off<T>(j, p.sn, r16);
-        lwk = p.logw ? p.logw[lbase + t] * kLog2e : 0.f;
-        if constexpr (PROXY) {
-          c = p.idx_cluster ? p.idx_cluster[lbase + t] : p.cluster_id[(int64_t)u * p.n + j];
-          if (c < -1 || c >= p.C) {
-            if (r16 == 0) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
-            c = -1;
-          }
-          if (t > 0 && r16 == 0 && p.idx[lbase + t - 1] >= j) flag_unit(p.flags, u, SDA_FLAG_IDX_ORDER);
-        }
-      } else if (r16 == 0) {
-        flag_unit(p.flags, u, SDA_FLAG_IDX_RANGE);
-      }
-    }
-    off[k] = o;
-    lw[k] = lwk;
-    cl[k] = c;
+    const int src = 4 * k + sub;
+    const int j = shfl_i(li, src);
+    const bool ok = shfl_i(valid ? 1 : 0, src) != 0;
+    off[k] = ok ? row_off<T>(j, p.sn, r16) : kOOB;
+    lw[k] = ok ? shfl_f(lwv, src) * kLog2e : kNegInf;
+    if constexpr (PROXY) cl[k] = ok ? (lookup ? j : shfl_i(lc, src)) : -1;
   }
-
-  // ---- proxy state: q . sumK per cluster, sumV staged in LDS ---------------
   if constexpr (PROXY) {
+    if (lookup) {
+      const int32_t* crow = p.cluster_id + (int64_t)u * p.n;
 #pragma unroll
-    for (int cp = 0; cp < kCmax / (4 * W); ++cp) {
-      const int b = 4 * (cp * W + w) + sub;
-      if (b < p.C) {
-        const int64_t rb = ((int64_t)u * p.C + b) * kD + 8 * r16;
-        float skf[8], svf[8];
-        load8f(p.sumK + rb, skf);
-        load8f(p.sumV + rb, svf);
-        float a[G];
-        dot_heads<G>(qf, skf, a);
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-          if (r16 == h) s_qk[b][h] = a[h];
-        *reinterpret_cast<float4*>(&s_sv[b][8 * r16]) = make_float4(svf[0], svf[1], svf[2], svf[3]);
-        *reinterpret_cast<float4*>(&s_sv[b][8 * r16 + 4]) = make_float4(svf[4], svf[5], svf[6], svf[7]);
+      for (int k = 0; k < NS; ++k) {
+        const int c = crow[cl[k] >= 0 ? cl[k] : 0];   // unconditional load, selected after
+        cl[k] = (off[k] != kOOB) ? c : -1;
       }
     }
   }
 
-  // ---- gather every listed row --------------------------------------------
+  // ---- gather every listed row ----------------------------------------------
+  const int64_t kvoff = (int64_t)s * p.sb + (int64_t)g * p.sh;
+  const rsrc_t rk = make_rsrc<T>(reinterpret_cast<const T*>(p.K) + kvoff, p.n, p.sn);
+  const rsrc_t rv = make_rsrc<T>(reinterpret_cast<const T*>(p.V) + kvoff, p.n, p.sn);
   RowChunk<T> kc[NS], vc[NS];
 #pragma unroll
   for (int k = 0; k < NS; ++k) buf_load(kc[k], rk, off[k]);
 #pragma unroll
   for (int k = 0; k < NS; ++k) buf_load(vc[k], rv, off[k]);
+
+  // ---- checks and proxy preparation while the rows are in flight ----------
+  {
+    int bad = 0;
+    if (live && !in_range) bad |= SDA_FLAG_IDX_RANGE;
+    if (PROXY && live && e > 0 && lp >= li) bad |= SDA_FLAG_IDX_ORDER;
+    if (bad_cluster) bad |= SDA_FLAG_CLUSTER;
+    if (bad) flag_unit(p.flags, u, bad);
+  }
+  if constexpr (PROXY) {
+#pragma unroll
+    for (int i = lane; i < PC * G; i += 64) (&s_csum[w][0][0])[i] = 0.f;
+    for (int i = lane; i < PC; i += 64) s_ccnt[w][i] = 0;
+    float a[G];
+    dot_heads<G>(qf, skf, a);
+    if (b0 < p.C) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if (r16 == h) s_qk[b0][h] = a[h];
+    }
+    if (p.C > 4 * W) {  // second cluster slot (C > 32)
+      const int b1 = b0 + 4 * W;
+      if (b1 < p.C) {
+        float sk1[8];
+        load8f(p.sumK + ((int64_t)u * p.C + b1) * kD + 8 * r16, sk1);
+        dot_heads<G>(qf, sk1, a);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          if (r16 == h) s_qk[b1][h] = a[h];
+      }
+    }
+  }
 
   // ---- logits ---------------------------------------------------------------
   float x[NS][G];
@@ -197,6 +238,10 @@ __global__ __launch_bounds__(512) void sparse_unit_kernel(const AttnParams p) {
       mx[h] = fmaxf(mx[h], x[k][h]);
     }
     if constexpr (PROXY) {
+      if (cl[k] < -1 || cl[k] >= p.C) {
+        if (r16 == 0) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
+        cl[k] = -1;
+      }
       if (cl[k] >= 0) {
         float mine = 0.f;
 #pragma unroll
@@ -217,15 +262,12 @@ __global__ __launch_bounds__(512) void sparse_unit_kernel(const AttnParams p) {
   // ---- tail preparation (wave 0): unit maximum, proxy logits ---------------
   if (w == 0) {
     if constexpr (PROXY) {
-      // lane handles (cluster, head) pairs e = lane + 64 r: head = lane % G
-      constexpr int R = (kCmax * G + 63) / 64;
       const int h = lane % G;
       float pi[R], nbf[R];
       float hm = kNegInf;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int e = lane + 64 * r;
-        const int b = e / G;
+        const int b = (lane + 64 * r) / G;
         pi[r] = kNegInf;
         nbf[r] = 0.f;
         if (b < p.C) {
@@ -236,7 +278,7 @@ __global__ __launch_bounds__(512) void sparse_unit_kernel(const AttnParams p) {
             ssum += s_csum[ww][b][h];
             rc += s_ccnt[ww][b];
           }
-          const int nb = p.count[(int64_t)u * p.C + b] - rc;
+          const int nb = cnt[r] - rc;
           if (nb < 0 && h == 0) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
           if (nb > 0) {
             nbf[r] = (float)nb;
@@ -245,7 +287,6 @@ __global__ __launch_bounds__(512) void sparse_unit_kernel(const AttnParams p) {
         }
         hm = fmaxf(hm, pi[r]);
       }
-      // max over lanes with the same head (lane bits above log2 G)
 #pragma unroll
       for (int msk = G; msk < 64; msk <<= 1) hm = fmaxf(hm, shfl_xor(hm, msk));
 #pragma unroll
@@ -254,8 +295,7 @@ __global__ __launch_bounds__(512) void sparse_unit_kernel(const AttnParams p) {
       float pe = 0.f;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int e = lane + 64 * r;
-        const int b = e / G;
+        const int b = (lane + 64 * r) / G;
         const float ev = (pi[r] == kNegInf) ? 0.f : fast_exp2(pi[r] - M);
         pe += ev;
         if (b < p.C) s_cw[b][h] = (nbf[r] > 0.f) ? ev / nbf[r] : 0.f;
@@ -294,13 +334,13 @@ __global__ __launch_bounds__(512) void sparse_unit_kernel(const AttnParams p) {
     float wt[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float e = fast_exp2(x[k][h] - M[h]);
-      l[h] += e;
-      wt[h] = e;
+      const float ev = fast_exp2(x[k][h] - M[h]);
+      l[h] += ev;
+      wt[h] = ev;
     }
     if constexpr (PROXY) {
-      // a read member leaves its cluster's proxy: subtract its share of the
-      // proxy value term (the proxy adds cw * sum of all member values)
+      // a read member leaves its cluster: subtract its share of the proxy's
+      // value term (the proxy below adds cw * the sum of all member values)
       if (cl[k] >= 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) wt[h] -= s_cw[cl[k]][h];
@@ -312,6 +352,30 @@ __global__ __launch_bounds__(512) void sparse_unit_kernel(const AttnParams p) {
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(wt[h], vf[i], acc[h][i]);
+  }
+  if constexpr (PROXY) {
+    // proxy value terms: cw_b * (sum of the cluster's values)
+    if (b0 < p.C) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float cw = s_cw[b0][h];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(cw, svf[i], acc[h][i]);
+      }
+    }
+    if (p.C > 4 * W) {
+      const int b1 = b0 + 4 * W;
+      if (b1 < p.C) {
+        float sv1[8];
+        load8f(p.sumV + ((int64_t)u * p.C + b1) * kD + 8 * r16, sv1);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float cw = s_cw[b1][h];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(cw, sv1[i], acc[h][i]);
+        }
+      }
+    }
   }
 
   // ---- reduce row groups, then waves ---------------------------------------
@@ -331,17 +395,372 @@ __global__ __launch_bounds__(512) void sparse_unit_kernel(const AttnParams p) {
   }
   __syncthreads();
 
-  for (int e = tid; e < G * kD; e += 512) {
-    const int h = e / kD, dim = e - h * kD;
-    float a = 0.f, L = 0.f;
+  for (int ei = tid; ei < G * kD; ei += 512) {
+    const int h = ei / kD, dim = ei - h * kD;
+    float a = 0.f, L = s_pl[h];
 #pragma unroll
     for (int ww = 0; ww < W; ++ww) {
       a += s_red[ww][h][dim];
       L += s_l[ww][h];
     }
+    const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
+    p.out[qh * kD + dim] = (L > 0.f) ? a / L : 0.f;
+    if (dim == 0 && p.lse) p.lse[qh] = (L > 0.f) ? (s_M[h] + log2f(L)) * kLn2 : kNegInf;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 variant of the one-workgroup-per-unit kernel with the q.K logits on
+// the matrix cores: v_mfma_f32_16x16x32_bf16 multiplies the (zero-padded)
+// 16 x 128 query block of the KV group by 16 gathered keys.  The 128-long
+// reduction is split into four steps; in step st, lane group qg = lane >> 4
+// supplies dims 32*st + 8*qg .. +8, so every load instruction reads 64
+// contiguous bytes of each of 16 keys.  Lane l then holds the logits of key
+// l & 15 for heads 4*(l >> 4) + i (accumulator element i).  The weighted
+// value sum stays on the vector ALUs in the row layout.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+template <int G, bool PROXY, int NT>
+__global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams p) {
+  constexpr int W = kUnitWaves;
+  constexpr int NS = 4 * NT;   // value slots per wave
+  constexpr int KW = 16 * NT;  // list entries per wave
+  constexpr int PC = PROXY ? kCmax : 1;
+  constexpr int PW = PROXY ? W : 1;
+  constexpr int R = PROXY ? (kCmax * G + 63) / 64 : 1;
+  const int u = blockIdx.x;
+  const int s = u / p.Hkv;
+  const int g = u - s * p.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, sub = lane >> 4;
+  const int CH = p.chunk;      // entries of this wave: [w*CH, (w+1)*CH), CH <= KW
+
+  __shared__ float s_x[W][KW][G];
+  __shared__ float s_wmax[W][G];
+  __shared__ float s_M[G];
+  __shared__ float s_pl[G];
+  __shared__ float s_l[W][G];
+  __shared__ __attribute__((aligned(16))) float s_red[W][G][kD];
+  __shared__ float s_csum[PW][PC][G];
+  __shared__ int s_ccnt[PW][PC];
+  __shared__ float s_qk[PC][G];
+  __shared__ float s_cw[PC][G];
+
+  // ---- prologue ------------------------------------------------------------
+  const int64_t qrow0 = (int64_t)s * p.Hq + (int64_t)g * G;
+  uint4 qa[4];  // MFMA A operand: head r16 (zero past G), dims 32*st + 8*sub
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    qa[st] = make_uint4(0, 0, 0, 0);
+    if (r16 < G)
+      qa[st] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(p.q) + (qrow0 + r16) * kD +
+                                                32 * st + 8 * sub);
+  }
+  float qf[PROXY ? G : 1][8];  // row-layout query for the cluster-sum logits
+  if constexpr (PROXY) load_query<bf16_t, G>(p.q, qrow0, r16, p.qscale, qf);
+
+  const int64_t lbase = (int64_t)u * p.m;
+  const int e = w * CH + lane;
+  const bool in_list = (lane < CH) && (e < p.m);
+  int li = -1, lp = -1, lc = -1;
+  float lwv = 0.f;
+  if (p.m > 0) {
+    const int64_t ea = lbase + (in_list ? e : 0);
+    li = p.idx[ea];
     if constexpr (PROXY) {
-      for (int b = 0; b < p.C; ++b) a = fmaf(s_cw[b][h], s_sv[b][dim], a);
-      L += s_pl[h];
+      lp = p.idx[lbase + ((in_list && e > 0) ? e - 1 : 0)];
+      if (p.idx_cluster) lc = p.idx_cluster[ea];
+    }
+    if (p.logw) lwv = p.logw[ea];
+  }
+
+  float skf[8], svf[8];
+  int cnt[R];
+  const int b0 = 4 * w + sub;
+  if constexpr (PROXY) {
+    const int64_t rb = ((int64_t)u * p.C + (b0 < p.C ? b0 : 0)) * kD + 8 * r16;
+    load8f(p.sumK + rb, skf);
+    load8f(p.sumV + rb, svf);
+    if (w == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int b = (lane + 64 * r) / G;
+        cnt[r] = p.count[(int64_t)u * p.C + (b < p.C ? b : 0)];
+      }
+    }
+  }
+
+  int len = p.m;
+  if (p.idx_len) {
+    int L = p.idx_len[u];
+    if (L < 0 || L > p.m) {
+      if (tid == 0) flag_unit(p.flags, u, SDA_FLAG_LEN);
+      L = L < 0 ? 0 : p.m;
+    }
+    len = L;
+  }
+
+  // ---- addresses --------------------------------------------------------------
+  const bool live = in_list && e < len;
+  const bool in_range = (unsigned)li < (unsigned)p.n;
+  const bool valid = live && in_range;
+  const float lw_own = valid ? (p.logw ? lwv * kLog2e : 0.f) : kNegInf;
+  const bool bad_cluster = PROXY && p.idx_cluster && valid && (lc < -1 || lc >= p.C);
+  if (bad_cluster) lc = -1;
+
+  int koff[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int src = 16 * t + r16;
+    const int j = shfl_i(li, src);
+    const bool ok = shfl_i(valid ? 1 : 0, src) != 0;
+    koff[t] = ok ? (int)(((int64_t)j * p.sn + 8 * sub) * 2) : kOOB;
+  }
+  int voff[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const int src = 4 * k + sub;
+    const int j = shfl_i(li, src);
+    const bool ok = shfl_i(valid ? 1 : 0, src) != 0;
+    voff[k] = ok ? row_off<bf16_t>(j, p.sn, r16) : kOOB;
+  }
+
+  const int64_t kvoff = (int64_t)s * p.sb + (int64_t)g * p.sh;
+  const rsrc_t rk = make_rsrc<bf16_t>(reinterpret_cast<const bf16_t*>(p.K) + kvoff, p.n, p.sn);
+  const rsrc_t rv = make_rsrc<bf16_t>(reinterpret_cast<const bf16_t*>(p.V) + kvoff, p.n, p.sn);
+  uint4 kt[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[t] + 64 * st, 0, 0);
+      kt[t][st] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  if constexpr (PROXY) {
+    // cluster of each own list entry (after the keys so that waiting for it
+    // does not wait for the values)
+    if (!p.idx_cluster) lc = valid ? p.cluster_id[(int64_t)u * p.n + (valid ? li : 0)] : -1;
+  }
+  RowChunk<bf16_t> vc[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) buf_load(vc[k], rv, voff[k]);
+
+  // ---- checks and proxy preparation while the rows are in flight ----------
+  {
+    int bad = 0;
+    if (live && !in_range) bad |= SDA_FLAG_IDX_RANGE;
+    if (PROXY && live && e > 0 && lp >= li) bad |= SDA_FLAG_IDX_ORDER;
+    if (bad_cluster) bad |= SDA_FLAG_CLUSTER;
+    if (bad) flag_unit(p.flags, u, bad);
+  }
+  if constexpr (PROXY) {
+#pragma unroll
+    for (int i = lane; i < PC * G; i += 64) (&s_csum[w][0][0])[i] = 0.f;
+    for (int i = lane; i < PC; i += 64) s_ccnt[w][i] = 0;
+    float a[G];
+    dot_heads<G>(qf, skf, a);
+    if (b0 < p.C) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if (r16 == h) s_qk[b0][h] = a[h];
+    }
+    if (p.C > 4 * W) {
+      const int b1 = b0 + 4 * W;
+      if (b1 < p.C) {
+        float sk1[8];
+        load8f(p.sumK + ((int64_t)u * p.C + b1) * kD + 8 * r16, sk1);
+        dot_heads<G>(qf, sk1, a);
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          if (r16 == h) s_qk[b1][h] = a[h];
+      }
+    }
+  }
+
+  // ---- logits on the matrix cores ------------------------------------------
+  float mx[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    floatx4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
+                                                  __builtin_bit_cast(bf16x8_t, kt[t][st]), d, 0, 0, 0);
+    const int kk = 16 * t + r16;            // this lane's key within the wave's entries
+    const float lwk = shfl_f(lw_own, kk);
+    const int ck = PROXY ? shfl_i(lc, kk) : -1;
+    const bool key_ok = lwk != kNegInf;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * sub + i;
+      if (h < G) {
+        const float sv = d[i] * p.qscale;
+        const float xv = sv + lwk;
+        s_x[w][kk][h] = xv;
+        mx[i] = fmaxf(mx[i], xv);
+        if constexpr (PROXY) {
+          if (key_ok && ck >= 0 && ck < p.C) atomicAdd(&s_csum[w][ck][h], sv);
+        }
+      }
+    }
+    if constexpr (PROXY) {
+      if (key_ok && sub == 0 && ck >= 0 && ck < p.C) atomicAdd(&s_ccnt[w][ck], 1);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float v = max16(mx[i]);
+    const int h = 4 * sub + i;
+    if (r16 == 0 && h < G) s_wmax[w][h] = v;
+  }
+  __syncthreads();
+
+  // ---- tail preparation (wave 0): unit maximum, proxy logits ---------------
+  if (w == 0) {
+    if constexpr (PROXY) {
+      const int h = lane % G;
+      float pi[R], nbf[R];
+      float hm = kNegInf;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int b = (lane + 64 * r) / G;
+        pi[r] = kNegInf;
+        nbf[r] = 0.f;
+        if (b < p.C) {
+          float ssum = 0.f;
+          int rc = 0;
+#pragma unroll
+          for (int ww = 0; ww < W; ++ww) {
+            ssum += s_csum[ww][b][h];
+            rc += s_ccnt[ww][b];
+          }
+          const int nb = cnt[r] - rc;
+          if (nb < 0 && h == 0) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
+          if (nb > 0) {
+            nbf[r] = (float)nb;
+            pi[r] = (s_qk[b][h] - ssum) / nbf[r] + __builtin_amdgcn_logf(nbf[r]);
+          }
+        }
+        hm = fmaxf(hm, pi[r]);
+      }
+#pragma unroll
+      for (int msk = G; msk < 64; msk <<= 1) hm = fmaxf(hm, shfl_xor(hm, msk));
+#pragma unroll
+      for (int ww = 0; ww < W; ++ww) hm = fmaxf(hm, s_wmax[ww][h]);
+      const float M = (hm == kNegInf) ? 0.f : hm;
+      float pe = 0.f;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int b = (lane + 64 * r) / G;
+        const float ev = (pi[r] == kNegInf) ? 0.f : fast_exp2(pi[r] - M);
+        pe += ev;
+        if (b < p.C) s_cw[b][h] = (nbf[r] > 0.f) ? ev / nbf[r] : 0.f;
+      }
+#pragma unroll
+      for (int msk = G; msk < 64; msk <<= 1) pe += shfl_xor(pe, msk);
+      if (lane < G) {
+        s_M[lane] = M;
+        s_pl[lane] = pe;
+      }
+    } else {
+      if (lane < G) {
+        float hm = kNegInf;
+#pragma unroll
+        for (int ww = 0; ww < W; ++ww) hm = fmaxf(hm, s_wmax[ww][lane]);
+        s_M[lane] = (hm == kNegInf) ? 0.f : hm;
+        s_pl[lane] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- weighted values (row layout) ----------------------------------------
+  float M[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) M[h] = s_M[h];
+  float acc[G][8], l[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    l[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+  }
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const int kk = 4 * k + sub;
+    int ck = -1;
+    if constexpr (PROXY) ck = shfl_i(lc, kk);
+    float wt[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float ev = fast_exp2(s_x[w][kk][h] - M[h]);
+      l[h] += ev;
+      wt[h] = ev;
+    }
+    if constexpr (PROXY) {
+      // a read member leaves its cluster: subtract its share of the proxy's
+      // value term (the proxy below adds cw * the sum of all member values)
+      if (ck >= 0 && ck < p.C && voff[k] != kOOB) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) wt[h] -= s_cw[ck][h];
+      }
+    }
+    float vf[8];
+    vc[k].unpack(vf);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(wt[h], vf[i], acc[h][i]);
+  }
+  if constexpr (PROXY) {
+    if (b0 < p.C) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float cw = s_cw[b0][h];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(cw, svf[i], acc[h][i]);
+      }
+    }
+    if (p.C > 4 * W) {
+      const int b1 = b0 + 4 * W;
+      if (b1 < p.C) {
+        float sv1[8];
+        load8f(p.sumV + ((int64_t)u * p.C + b1) * kD + 8 * r16, sv1);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const float cw = s_cw[b1][h];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(cw, sv1[i], acc[h][i]);
+        }
+      }
+    }
+  }
+
+  // ---- reduce row groups, then waves ---------------------------------------
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[h][i] = sum_rowgroups(acc[h][i]);
+    l[h] = sum_rowgroups(l[h]);
+  }
+  if (sub == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      *reinterpret_cast<float4*>(&s_red[w][h][8 * r16]) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      *reinterpret_cast<float4*>(&s_red[w][h][8 * r16 + 4]) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+      if (r16 == 0) s_l[w][h] = l[h];
+    }
+  }
+  __syncthreads();
+
+  for (int ei = tid; ei < G * kD; ei += 512) {
+    const int h = ei / kD, dim = ei - h * kD;
+    float a = 0.f, L = s_pl[h];
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww) {
+      a += s_red[ww][h][dim];
+      L += s_l[ww][h];
     }
     const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
     p.out[qh * kD + dim] = (L > 0.f) ? a / L : 0.f;
@@ -409,17 +828,30 @@ __device__ __forceinline__ void bias_shift(const AttnParams& p, int s, int g, in
   }
 }
 
+// Online-softmax combine of two partials (m, l, acc); both lanes of a row
+// pair compute the same bits.
+__device__ __forceinline__ void lse_factors(float ma, float mb, float& M, float& fa, float& fb) {
+  M = fmaxf(ma, mb);
+  fa = rescale(ma, M);
+  fb = rescale(mb, M);
+}
+
 // ---------------------------------------------------------------------------
 // Split-K streaming kernel.  Workgroup (u, split) covers list entries (or
 // rows, for the dense modes) [split*chunk, min(len, (split+1)*chunk)).  Each
 // 16-lane row group keeps its own online-softmax state; groups and waves are
-// merged at the end.
+// merged at the end.  A batch is NSB slots of 4 rows per wave; the list
+// entries of the next batch are fetched while the current batch's rows are
+// in flight.
 template <typename T, int G, int MODE, int NSB>
 __global__ __launch_bounds__(256) void stream_kernel(const AttnParams p) {
   constexpr int W = 4;
+  constexpr int STEP = 4 * W * NSB;
   constexpr bool DENSE = (MODE == kModeDense || MODE == kModeBuildPrior);
   constexpr bool PRIOR = (MODE == kModePrior);
   constexpr bool BUILD = (MODE == kModeBuildPrior);
+  using QT = typename std::conditional<BUILD, float, T>::type;
+  static_assert(4 * NSB <= 64, "one list entry per lane");
   const int u = blockIdx.x / p.splits;
   const int split = blockIdx.x - u * p.splits;
   const int s = u / p.Hkv;
@@ -433,6 +865,22 @@ __global__ __launch_bounds__(256) void stream_kernel(const AttnParams p) {
   __shared__ __attribute__((aligned(16))) float s_ks[BUILD ? W : 1][BUILD ? kD : 1];
   __shared__ float s_c[G];
 
+  float qf[G][8];
+  load_query<QT, G>(p.q, (int64_t)s * p.Hq + (int64_t)g * G, r16, p.qscale, qf);
+  float qp[PRIOR ? G : 1][8];
+  float mP[G];
+  if constexpr (PRIOR) {
+    // prior logits use the mean query, shifted by the stored maxP
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
+      load8f(p.mu_Q + qh * kD + 8 * r16, qp[h]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qp[h][i] *= p.qscale;
+      mP[h] = p.maxP[qh] * kLog2e;
+    }
+  }
+
   int len = DENSE ? p.n : p.m;
   if (!DENSE && p.idx_len) {
     int L = p.idx_len[u];
@@ -445,26 +893,25 @@ __global__ __launch_bounds__(256) void stream_kernel(const AttnParams p) {
   const int t0 = split * p.chunk;
   const int t1 = min(len, t0 + p.chunk);
 
-  float qf[G][8];
-  load_query<G>(p.q, p.q_f32, (int64_t)s * p.Hq + (int64_t)g * G, r16, p.qscale, qf);
-  float qp[PRIOR ? G : 1][8];
-  float mP[G];
-  if constexpr (PRIOR) {
-    // prior logits use the mean query; shifted by the stored maxP
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
-      load8f(p.mu_Q + qh * kD + 8 * r16, qp[h]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qp[h][i] *= p.qscale;
-      mP[h] = p.maxP[qh] * kLog2e;
-    }
-  }
-
   const int64_t lbase = (int64_t)u * p.m;
   const int64_t kvoff = (int64_t)s * p.sb + (int64_t)g * p.sh;
   const rsrc_t rk = make_rsrc<T>(reinterpret_cast<const T*>(p.K) + kvoff, p.n, p.sn);
   const rsrc_t rv = make_rsrc<T>(reinterpret_cast<const T*>(p.V) + kvoff, p.n, p.sn);
+
+  // lane l < 4*NSB of wave w holds list entry tb + 4*((l>>2)*W + w) + (l&3)
+  const int lk = lane >> 2, lsub = lane & 3;
+  auto list_t = [&](int tb) { return tb + 4 * (lk * W + w) + lsub; };
+  int li = -1, lp = -1;
+  float lwv = 0.f;
+  auto load_list = [&](int tb, int& vi, int& vp, float& vw) {
+    const int t = list_t(tb);
+    const bool in = lane < 4 * NSB && t < t1;
+    const int64_t a = lbase + (in ? t : 0);
+    vi = p.idx[a];
+    if (PRIOR) vp = p.idx[lbase + ((in && t > 0) ? t - 1 : 0)];
+    if (p.logw) vw = p.logw[a];
+  };
+  if (!DENSE && t0 < t1) load_list(t0, li, lp, lwv);
 
   float m[G], l[G], acc[G][8];
   float sp[PRIOR ? G : 1], spv[PRIOR ? G : 1][8];
@@ -487,37 +934,44 @@ __global__ __launch_bounds__(256) void stream_kernel(const AttnParams p) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) ks[i] = 0.f;
 
-  for (int tb = t0; tb < t1; tb += 4 * W * NSB) {
+  for (int tb = t0; tb < t1; tb += STEP) {
     int off[NSB];
     float lw[NSB];
+    bool lane_ok = false;
+    if constexpr (!DENSE) {
+      const int t = list_t(tb);
+      lane_ok = lane < 4 * NSB && t < t1 && (unsigned)li < (unsigned)p.n;
+    }
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
-      const int t = tb + 4 * (k * W + w) + sub;
-      int o = kOOB;
-      float lwk = kNegInf;
-      if (t < t1) {
-        if constexpr (DENSE) {
-          o = row_off<T>(t, p.sn, r16);
-          lwk = 0.f;
-        } else {
-          const int j = p.idx[lbase + t];
-          if ((unsigned)j < (unsigned)p.n) {
-            o = row_off<T>(j, p.sn, r16);
-            lwk = p.logw ? p.logw[lbase + t] * kLog2e : 0.f;
-            if (PRIOR && t > 0 && r16 == 0 && p.idx[lbase + t - 1] >= j) flag_unit(p.flags, u, SDA_FLAG_IDX_ORDER);
-          } else if (r16 == 0) {
-            flag_unit(p.flags, u, SDA_FLAG_IDX_RANGE);
-          }
-        }
+      if constexpr (DENSE) {
+        const int t = tb + 4 * (k * W + w) + sub;
+        off[k] = t < t1 ? row_off<T>(t, p.sn, r16) : kOOB;
+        lw[k] = t < t1 ? 0.f : kNegInf;
+      } else {
+        const int src = 4 * k + sub;
+        const int j = shfl_i(li, src);
+        const bool ok = shfl_i(lane_ok ? 1 : 0, src) != 0;
+        off[k] = ok ? row_off<T>(j, p.sn, r16) : kOOB;
+        lw[k] = ok ? shfl_f(lwv, src) * kLog2e : kNegInf;
       }
-      off[k] = o;
-      lw[k] = lwk;
     }
     RowChunk<T> kc[NSB], vc[NSB];
 #pragma unroll
     for (int k = 0; k < NSB; ++k) buf_load(kc[k], rk, off[k]);
 #pragma unroll
     for (int k = 0; k < NSB; ++k) buf_load(vc[k], rv, off[k]);
+
+    if constexpr (!DENSE) {
+      // checks of this batch's entries, then the next batch's list
+      const int t = list_t(tb);
+      const bool live = lane < 4 * NSB && t < t1;
+      int bad = 0;
+      if (live && (unsigned)li >= (unsigned)p.n) bad |= SDA_FLAG_IDX_RANGE;
+      if (PRIOR && live && t > 0 && lp >= li) bad |= SDA_FLAG_IDX_ORDER;
+      if (bad) flag_unit(p.flags, u, bad);
+      if (tb + STEP < t1) load_list(tb + STEP, li, lp, lwv);
+    }
 
     float x[NSB][G];
     float pl[PRIOR ? NSB : 1][G];
@@ -529,10 +983,8 @@ __global__ __launch_bounds__(256) void stream_kernel(const AttnParams p) {
       float kf[8];
       kc[k].unpack(kf);
       if constexpr (BUILD) {
-        if (off[k] != kOOB) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) ks[i] += kf[i];
-        }
+        for (int i = 0; i < 8; ++i) ks[i] += kf[i];   // rows outside the range load as zeros
       }
       float a[G];
       dot_heads<G>(qf, kf, a);
@@ -548,15 +1000,14 @@ __global__ __launch_bounds__(256) void stream_kernel(const AttnParams p) {
         for (int h = 0; h < G; ++h) pl[k][h] = (off[k] == kOOB) ? kNegInf : ap[h] - mP[h];
       }
     }
-    float alpha[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float mn = fmaxf(m[h], bm[h]);
-      alpha[h] = rescale(m[h], mn);
+      const float alpha = rescale(m[h], mn);
       m[h] = mn;
-      l[h] *= alpha[h];
+      l[h] *= alpha;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[h][i] *= alpha[h];
+      for (int i = 0; i < 8; ++i) acc[h][i] *= alpha;
     }
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
@@ -564,10 +1015,10 @@ __global__ __launch_bounds__(256) void stream_kernel(const AttnParams p) {
       vc[k].unpack(vf);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float e = (m[h] == kNegInf) ? 0.f : fast_exp2(x[k][h] - m[h]);
-        l[h] += e;
+        const float ev = (m[h] == kNegInf) ? 0.f : fast_exp2(x[k][h] - m[h]);
+        l[h] += ev;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(e, vf[i], acc[h][i]);
+        for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(ev, vf[i], acc[h][i]);
         if constexpr (PRIOR) {
           const float ep = fast_exp2(pl[k][h]);
           sp[h] += ep;
@@ -578,27 +1029,38 @@ __global__ __launch_bounds__(256) void stream_kernel(const AttnParams p) {
     }
   }
 
-  // ---- merge the four row groups of the wave ----------------------------
+  // ---- merge the four row groups of the wave ------------------------------
 #pragma unroll
-  for (int msk = 16; msk <= 32; msk <<= 1) {
+  for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float mo = shfl_xor(m[h], msk);
-      const float mn = fmaxf(m[h], mo);
-      const float fa = rescale(m[h], mn), fb = rescale(mo, mn);
-      l[h] = l[h] * fa + shfl_xor(l[h], msk) * fb;
+      const RowPair mm = pass ? swap32(m[h]) : swap16(m[h]);
+      float M, fa, fb;
+      lse_factors(mm.even, mm.odd, M, fa, fb);
+      const RowPair ll = pass ? swap32(l[h]) : swap16(l[h]);
+      l[h] = ll.even * fa + ll.odd * fb;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[h][i] = acc[h][i] * fa + shfl_xor(acc[h][i], msk) * fb;
-      m[h] = mn;
+      for (int i = 0; i < 8; ++i) {
+        const RowPair aa = pass ? swap32(acc[h][i]) : swap16(acc[h][i]);
+        acc[h][i] = aa.even * fa + aa.odd * fb;
+      }
+      m[h] = M;
       if constexpr (PRIOR) {
-        sp[h] += shfl_xor(sp[h], msk);
+        const RowPair ss = pass ? swap32(sp[h]) : swap16(sp[h]);
+        sp[h] = ss.even + ss.odd;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) spv[h][i] += shfl_xor(spv[h][i], msk);
+        for (int i = 0; i < 8; ++i) {
+          const RowPair vv = pass ? swap32(spv[h][i]) : swap16(spv[h][i]);
+          spv[h][i] = vv.even + vv.odd;
+        }
       }
     }
     if constexpr (BUILD) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ks[i] += shfl_xor(ks[i], msk);
+      for (int i = 0; i < 8; ++i) {
+        const RowPair kk = pass ? swap32(ks[i]) : swap16(ks[i]);
+        ks[i] = kk.even + kk.odd;
+      }
     }
   }
   if (sub == 0) {
@@ -622,7 +1084,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const AttnParams p) {
     }
   }
   if constexpr (PRIOR) {
-    if (p.splits == 1 && w == 0) {
+    if (split == 0 && w == 0) {
       float c[G];
       bias_shift<G>(p, s, g, r16, qf, c);
       if (lane == 0) {
@@ -633,8 +1095,8 @@ __global__ __launch_bounds__(256) void stream_kernel(const AttnParams p) {
   }
   __syncthreads();
 
-  for (int e = tid; e < G * kD; e += 256) {
-    const int h = e / kD, dim = e - h * kD;
+  for (int ei = tid; ei < G * kD; ei += 256) {
+    const int h = ei / kD, dim = ei - h * kD;
     float M = kNegInf;
 #pragma unroll
     for (int ww = 0; ww < W; ++ww) M = fmaxf(M, s_m[ww][h]);
@@ -656,6 +1118,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const AttnParams p) {
         rec[0] = M;
         rec[1] = L;
         rec[2] = SP;
+        rec[3] = (PRIOR && split == 0) ? s_c[h] : 0.f;
       }
       rec[4 + dim] = a;
       if constexpr (PRIOR) rec[4 + kD + dim] = SPV;
@@ -701,31 +1164,17 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnParams p) {
   const int u = blockIdx.x;
   const int s = u / p.Hkv;
   const int g = u - s * p.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  __shared__ float s_c[G];
+  const int tid = threadIdx.x;
 
-  if constexpr (PRIOR) {
-    if (w == 0) {
-      float qf[G][8];
-      const int r16 = lane & 15;
-      load_query<G>(p.q, p.q_f32, (int64_t)s * p.Hq + (int64_t)g * G, r16, p.qscale, qf);
-      float c[G];
-      bias_shift<G>(p, s, g, r16, qf, c);
-      if (lane == 0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) s_c[h] = c[h];
-      }
-    }
-    __syncthreads();
-  }
-
-  for (int e = tid; e < G * kD; e += 256) {
-    const int h = e / kD, dim = e - h * kD;
+  for (int ei = tid; ei < G * kD; ei += 256) {
+    const int h = ei / kD, dim = ei - h * kD;
     const float* base = p.part + ((int64_t)u * p.splits * G + h) * kPartStride;
     const int64_t stride = (int64_t)G * kPartStride;
     float M = kNegInf;
+#pragma unroll 8
     for (int sp = 0; sp < p.splits; ++sp) M = fmaxf(M, base[sp * stride]);
     float a = 0.f, L = 0.f, SP = 0.f, SPV = 0.f;
+#pragma unroll 8
     for (int sp = 0; sp < p.splits; ++sp) {
       const float* rec = base + sp * stride;
       const float f = rescale(rec[0], M);
@@ -739,7 +1188,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnParams p) {
     const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
     if constexpr (PRIOR) {
       const float mP = p.maxP[qh] * kLog2e;
-      const Fin f = finalize_prior(M, L, a, s_c[h], mP, p.sumP[qh], p.O_est[qh * kD + dim], SP, SPV, p.lambda);
+      const Fin f = finalize_prior(M, L, a, base[3], mP, p.sumP[qh], p.O_est[qh * kD + dim], SP, SPV, p.lambda);
       p.out[qh * kD + dim] = f.out;
       if (dim == 0 && p.lse) p.lse[qh] = f.lse;
     } else if constexpr (BUILD) {
@@ -797,8 +1246,37 @@ static hipError_t launch_unit_t(const AttnParams& p, int G, bool proxy, int ns, 
   return hipErrorInvalidValue;
 }
 
+template <int G, bool PROXY>
+static hipError_t launch_mfma_nt(const AttnParams& p, int nt, hipStream_t st) {
+  const dim3 grid(p.B * p.Hkv), block(512);
+  switch (nt) {
+    case 1: hipLaunchKernelGGL((sparse_unit_mfma_kernel<G, PROXY, 1>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((sparse_unit_mfma_kernel<G, PROXY, 2>), grid, block, 0, st, p); break;
+    case 3: hipLaunchKernelGGL((sparse_unit_mfma_kernel<G, PROXY, 3>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((sparse_unit_mfma_kernel<G, PROXY, 4>), grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int G>
+static hipError_t launch_mfma_g(const AttnParams& p, bool proxy, int nt, hipStream_t st) {
+  return proxy ? launch_mfma_nt<G, true>(p, nt, st) : launch_mfma_nt<G, false>(p, nt, st);
+}
+
 hipError_t launch_sparse_unit(const AttnParams& p, int dtype, int G, bool proxy, int ns, hipStream_t st) {
-  return dtype == SDA_BF16 ? launch_unit_t<bf16_t>(p, G, proxy, ns, st) : launch_unit_t<float>(p, G, proxy, ns, st);
+  if (dtype == SDA_BF16) {
+    // ns = 4 * tiles for the matrix-core kernel
+    const int nt = ns / 4;
+    switch (G) {
+      case 1: return launch_mfma_g<1>(p, proxy, nt, st);
+      case 2: return launch_mfma_g<2>(p, proxy, nt, st);
+      case 4: return launch_mfma_g<4>(p, proxy, nt, st);
+      case 8: return launch_mfma_g<8>(p, proxy, nt, st);
+    }
+    return hipErrorInvalidValue;
+  }
+  return launch_unit_t<float>(p, G, proxy, ns, st);
 }
 
 constexpr int kStreamSlots = 4;

@@ -73,15 +73,12 @@ __device__ __forceinline__ void load8f(const float* p, float (&f)[8]) {
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
 
-// Query chunk: 8 elements of q (bf16, fp32) widened to fp32.
-__device__ __forceinline__ void load_q8(const void* q, int64_t off, bool is_f32, float (&f)[8]) {
-  if (is_f32) {
-    load8f(reinterpret_cast<const float*>(q) + off, f);
-  } else {
-    RowChunk<bf16_t> c;
-    c.load_cached(reinterpret_cast<const bf16_t*>(q) + off);
-    c.unpack(f);
-  }
+// Query chunk: 8 elements (dims 8*r16 ..) of a bf16 or fp32 query, as fp32.
+template <typename QT>
+__device__ __forceinline__ void load_q8(const void* q, int64_t off, float (&f)[8]) {
+  RowChunk<QT> c;
+  c.load_cached(reinterpret_cast<const QT*>(q) + off);
+  c.unpack(f);
 }
 
 // ---- cross-lane --------------------------------------------------------------
@@ -101,23 +98,49 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
+// Max over the 16 lanes of a row group (same pattern as sum16).
+__device__ __forceinline__ float max16(float v) {
+  v = fmaxf(v, dpp<0xB1>(v));
+  v = fmaxf(v, dpp<0x4E>(v));
+  v = fmaxf(v, dpp<0x141>(v));
+  v = fmaxf(v, dpp<0x140>(v));
+  return v;
+}
+
 __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// max over the 4 row groups of a wave (lanes l, l^16, l^32, l^48)
+// The four 16-lane row groups of a wave hold partial results for the same
+// dims.  v_permlane16_swap / v_permlane32_swap exchange rows in one VALU op;
+// each combine takes (even-row value, odd-row value) in the same order on
+// both lanes, so every lane ends with bitwise-identical results.
+struct RowPair {
+  float even, odd;
+};
+__device__ __forceinline__ RowPair swap16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ RowPair swap32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+
 __device__ __forceinline__ float max_rowgroups(float v) {
-  v = fmaxf(v, shfl_xor(v, 16));
-  v = fmaxf(v, shfl_xor(v, 32));
-  return v;
+  RowPair a = swap16(v);
+  v = fmaxf(a.even, a.odd);
+  RowPair b = swap32(v);
+  return fmaxf(b.even, b.odd);
 }
 
 __device__ __forceinline__ float sum_rowgroups(float v) {
-  v += shfl_xor(v, 16);
-  v += shfl_xor(v, 32);
-  return v;
+  RowPair a = swap16(v);
+  v = a.even + a.odd;
+  RowPair b = swap32(v);
+  return b.even + b.odd;
 }
 
 // Scale factor exp2(m - M) that is 0 (not NaN) for an empty partial.

@@ -12,6 +12,9 @@ namespace sda {
 constexpr int kD = 128;          // head dimension supported by the kernels
 constexpr int kCmax = 64;        // clusters per unit supported by the kernels
 constexpr int kPartStride = 264; // floats per (unit, split, head) partial
+// Largest byte span of one unit's K (or V) rows: rows are addressed with
+// 32-bit buffer offsets, and offsets from here up are the "absent row" marker.
+constexpr int kMaxUnitBytes = 0x7ffffe00;
 
 // One parameter block for the attention kernels (passed by value).
 struct AttnParams {
