@@ -131,6 +131,13 @@ sda_status plan_sparse(const Resolved& r, int kind, int m, SparsePlan* pl) {
       return SDA_OK;
     }
   }
+  if (kind == SDA_TAIL_SAMPLED) {
+    // one workgroup per unit; scratch: fp64 logits/weights of the listed rows
+    // and base draws, and the positions of the fresh draws
+    if (m > kSampMaxList) return SDA_EUNSUPPORTED;
+    pl->ws = (size_t)units * ((size_t)(m + kSampMaxB0) * r.G * sizeof(double) + (size_t)r.n * sizeof(int32_t));
+    return SDA_OK;
+  }
   if (kind == SDA_TAIL_NONE || kind == SDA_TAIL_PRIOR) {
     stream_shape(units, m, 256, &pl->splits, &pl->chunk);
     if (pl->splits > 1) pl->ws = (size_t)units * pl->splits * r.G * kPartStride * sizeof(float);
@@ -350,7 +357,18 @@ SDA_EXPORT sda_status sda_sparse_decode_attn(const sda_dims* dims, const void* q
     p.sumP = tail->sumP;
     p.lambda = tail->lambda;
   } else if (kind == SDA_TAIL_SAMPLED) {
-    return SDA_EUNSUPPORTED;
+    if (!(tail->eps > 0.0) || !(tail->z > 0.0) || !isfinite(tail->eps) || !isfinite(tail->z)) return SDA_EINVAL;
+    if (tail->b0 < 2 || tail->b0 > kSampMaxB0) return SDA_EUNSUPPORTED;
+    if (tail->b_cap < 0 || (tail->samples_out && tail->b_cap == 0)) return SDA_EINVAL;
+    p.scale = r.scale;
+    p.eps = tail->eps;
+    p.z = tail->z;
+    p.b0 = tail->b0;
+    p.seed = tail->seed;
+    p.b_cap = tail->b_cap;
+    p.b_out = tail->b_out;
+    p.bstar_out = tail->bstar_out;
+    p.samples_out = tail->samples_out;
   }
 
   SparsePlan pl;
@@ -358,6 +376,13 @@ SDA_EXPORT sda_status sda_sparse_decode_attn(const sda_dims* dims, const void* q
   if (st != SDA_OK) return st;
   if (pl.ws && (!ws || ws_bytes < pl.ws)) return SDA_EWORKSPACE;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (kind == SDA_TAIL_SAMPLED) {
+    const size_t logit_bytes = (size_t)r.B * r.Hkv * (size_t)(m + kSampMaxB0) * r.G * sizeof(double);
+    p.wlog = reinterpret_cast<double*>(ws);
+    p.wpos = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + logit_bytes);
+    // the kernel indexes logits with a per-unit stride of (m + b0) rows
+    return hip_status(launch_sampled(p, r.dtype, r.G, hs));
+  }
   if (pl.unit) {
     p.chunk = pl.chunk;
     return hip_status(launch_sparse_unit(p, r.dtype, r.G, kind == SDA_TAIL_PROXY, pl.ns, hs));

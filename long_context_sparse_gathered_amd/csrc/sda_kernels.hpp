@@ -45,6 +45,18 @@ struct AttnParams {
   const float* sumP;
   float lambda;
 
+  // SAMPLED
+  float scale;                 // logit scale (fp32 value, widened for fp64 statistics)
+  double eps, z;
+  int32_t b0;
+  uint64_t seed;
+  int32_t b_cap;
+  int32_t* b_out;              // [B,Hkv] or null
+  double* bstar_out;           // [B,Hkv] or null
+  int32_t* samples_out;        // [B,Hkv,b_cap] or null
+  double* wlog;                // workspace: [units, m + b0, G] fp64 logits / weights
+  int32_t* wpos;               // workspace: [units, n] drawn positions
+
   // split-K
   int32_t splits;              // WGs per unit
   int32_t chunk;               // entries (rows) per split
@@ -83,6 +95,11 @@ hipError_t launch_sparse_unit(const AttnParams& p, int dtype, int G, bool proxy,
                               hipStream_t st);
 hipError_t launch_stream(const AttnParams& p, int dtype, int G, int mode, hipStream_t st);
 hipError_t launch_merge(const AttnParams& p, int G, int mode, hipStream_t st);
+hipError_t launch_sampled(const AttnParams& p, int dtype, int G, hipStream_t st);
+
+// Sampled tail limits: the deterministic list and the base draws live in LDS.
+constexpr int kSampMaxList = 4096;
+constexpr int kSampMaxB0 = 256;
 hipError_t launch_proxy_build(const ProxyBuildParams& p, int dtype, int units, hipStream_t st);
 
 // Largest slot count the one-workgroup-per-unit kernel is built for.

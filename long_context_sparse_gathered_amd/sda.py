@@ -291,6 +291,14 @@ def sparse_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: O
     dev = q.device
     if m is None:
         m = 0 if idx is None else idx.shape[-1]
+    if isinstance(tail, SampledTail):
+        Hkv = K.shape[1]
+        if tail.b is None:
+            tail.b = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
+        if tail.bstar is None:
+            tail.bstar = torch.empty((B, Hkv), dtype=torch.float64, device=dev)
+        if tail.samples is None and tail.b_cap > 0:
+            tail.samples = torch.full((B, Hkv, tail.b_cap), -1, dtype=torch.int32, device=dev)
     keep = []
     t = _tail_struct(tail, idx_cluster, cluster_id, lam, keep)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev) if out is None else out
