@@ -410,14 +410,22 @@ __global__ __launch_bounds__(512) void sparse_unit_kernel(const AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 variant of the one-workgroup-per-unit kernel with the q.K logits on
-// the matrix cores: v_mfma_f32_16x16x32_bf16 multiplies the (zero-padded)
-// 16 x 128 query block of the KV group by 16 gathered keys.  The 128-long
-// reduction is split into four steps; in step st, lane group qg = lane >> 4
-// supplies dims 32*st + 8*qg .. +8, so every load instruction reads 64
-// contiguous bytes of each of 16 keys.  Lane l then holds the logits of key
-// l & 15 for heads 4*(l >> 4) + i (accumulator element i).  The weighted
-// value sum stays on the vector ALUs in the row layout.
+// bf16 variant of the one-workgroup-per-unit kernel, both products on the
+// matrix cores.
+//
+// Logits: v_mfma_f32_16x16x32_bf16 multiplies the (zero-padded) 16 x 128
+// query block of the KV group by 16 gathered keys.  The 128-long reduction is
+// split into four steps; in step st, lane group qg = lane >> 4 supplies dims
+// 32*st + 8*qg .. +8, so every load instruction reads 64 contiguous bytes of
+// each of 16 keys.  Lane l then holds the logits of key l & 15 for heads
+// 4*(l >> 4) + i (accumulator element i).
+//
+// Tail preparation is spread over the waves: wave w owns clusters 4w + qg and
+// 4w + qg + 32 and computes their mean logits; the unit maximum comes from the
+// per-wave maxima of the read logits and of the proxy logits.
+//
+// Weighted values: one v_mfma_f32_16x16x32_bf16 per 16 keys and 16 dims (see
+// the value phase below).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
@@ -428,24 +436,29 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   constexpr int KW = 16 * NT;  // list entries per wave
   constexpr int PC = PROXY ? kCmax : 1;
   constexpr int PW = PROXY ? W : 1;
-  constexpr int R = PROXY ? (kCmax * G + 63) / 64 : 1;
   const int u = blockIdx.x;
   const int s = u / p.Hkv;
   const int g = u - s * p.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, sub = lane >> 4;
   const int CH = p.chunk;      // entries of this wave: [w*CH, (w+1)*CH), CH <= KW
+  const int hr = r16 < G ? r16 : 0;  // head of this lane in the [head][..] layouts (clamped)
 
-  __shared__ float s_x[W][KW][G];
+  __shared__ __attribute__((aligned(16))) float s_x[W][G][KW];  // logits (log2 units), per wave
+  __shared__ __attribute__((aligned(16))) int s_kc[PW][PROXY ? KW : 4];  // cluster of each key, -1 if none
   __shared__ float s_wmax[W][G];
+  __shared__ float s_pmax[PW][G];
   __shared__ float s_M[G];
-  __shared__ float s_pl[G];
   __shared__ float s_l[W][G];
-  __shared__ __attribute__((aligned(16))) float s_red[W][G][kD];
   __shared__ float s_csum[PW][PC][G];
   __shared__ int s_ccnt[PW][PC];
-  __shared__ float s_qk[PC][G];
-  __shared__ float s_cw[PC][G];
+  __shared__ float s_mu[PC][G];  // mean logit of a cluster's unread members (-inf if none)
+  // Per wave: one 16-row value tile for the transposed reads (rows padded to
+  // 288 bytes against bank conflicts), then the wave's [G][kD] partial sums.
+  constexpr int kVRow = 144;  // bf16 elements per staged row
+  constexpr int kWaveLds = 16 * kVRow * 2;
+  static_assert(G * kD * 4 <= kWaveLds, "partials must fit the tile");
+  __shared__ __attribute__((aligned(16))) unsigned char s_pool[W * kWaveLds];
 
   // ---- prologue ------------------------------------------------------------
   const int64_t qrow0 = (int64_t)s * p.Hq + (int64_t)g * G;
@@ -475,19 +488,25 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     if (p.logw) lwv = p.logw[ea];
   }
 
-  float skf[8], svf[8];
-  int cnt[R];
-  const int b0 = 4 * w + sub;
+  // cluster sums and counts of the two clusters this lane owns: b0 = 4w + sub
+  // and b1 = b0 + 32 (dims 8*r16 .. +8 of the sums)
+  const int b0 = 4 * w + sub, b1 = b0 + 4 * W;
+  const bool has0 = PROXY && b0 < p.C, has1 = PROXY && b1 < p.C;
+  float skf[8], svf[8], sk1[8], sv1[8];
+  int cnt0 = 0, cnt1 = 0;
   if constexpr (PROXY) {
-    const int64_t rb = ((int64_t)u * p.C + (b0 < p.C ? b0 : 0)) * kD + 8 * r16;
+    const int64_t rb = ((int64_t)u * p.C + (has0 ? b0 : 0)) * kD + 8 * r16;
     load8f(p.sumK + rb, skf);
     load8f(p.sumV + rb, svf);
-    if (w == 0) {
+    cnt0 = p.count[(int64_t)u * p.C + (has0 ? b0 : 0)];
+    if (has1) {
+      const int64_t rb1 = ((int64_t)u * p.C + b1) * kD + 8 * r16;
+      load8f(p.sumK + rb1, sk1);
+      load8f(p.sumV + rb1, sv1);
+      cnt1 = p.count[(int64_t)u * p.C + b1];
+    } else {
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int b = (lane + 64 * r) / G;
-        cnt[r] = p.count[(int64_t)u * p.C + (b < p.C ? b : 0)];
-      }
+      for (int i = 0; i < 8; ++i) sk1[i] = sv1[i] = 0.f;
     }
   }
 
@@ -554,27 +573,21 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     if (bad_cluster) bad |= SDA_FLAG_CLUSTER;
     if (bad) flag_unit(p.flags, u, bad);
   }
+  float qk0 = 0.f, qk1 = 0.f;  // q . (sum of keys) of clusters b0, b1 for head r16
   if constexpr (PROXY) {
 #pragma unroll
     for (int i = lane; i < PC * G; i += 64) (&s_csum[w][0][0])[i] = 0.f;
     for (int i = lane; i < PC; i += 64) s_ccnt[w][i] = 0;
     float a[G];
     dot_heads<G>(qf, skf, a);
-    if (b0 < p.C) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      if (r16 == h) qk0 = a[h];
+    if (has1) {
+      dot_heads<G>(qf, sk1, a);
 #pragma unroll
       for (int h = 0; h < G; ++h)
-        if (r16 == h) s_qk[b0][h] = a[h];
-    }
-    if (p.C > 4 * W) {
-      const int b1 = b0 + 4 * W;
-      if (b1 < p.C) {
-        float sk1[8];
-        load8f(p.sumK + ((int64_t)u * p.C + b1) * kD + 8 * r16, sk1);
-        dot_heads<G>(qf, sk1, a);
-#pragma unroll
-        for (int h = 0; h < G; ++h)
-          if (r16 == h) s_qk[b1][h] = a[h];
-      }
+        if (r16 == h) qk1 = a[h];
     }
   }
 
@@ -597,7 +610,7 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
       if (h < G) {
         const float sv = d[i] * p.qscale;
         const float xv = sv + lwk;
-        s_x[w][kk][h] = xv;
+        s_x[w][h][kk] = xv;
         mx[i] = fmaxf(mx[i], xv);
         if constexpr (PROXY) {
           if (key_ok && ck >= 0 && ck < p.C) atomicAdd(&s_csum[w][ck][h], sv);
@@ -605,7 +618,9 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
       }
     }
     if constexpr (PROXY) {
-      if (key_ok && sub == 0 && ck >= 0 && ck < p.C) atomicAdd(&s_ccnt[w][ck], 1);
+      const bool member = key_ok && ck >= 0 && ck < p.C;
+      if (member && sub == 0) atomicAdd(&s_ccnt[w][ck], 1);
+      if (sub == 0) s_kc[w][kk] = member ? ck : -1;
     }
   }
 #pragma unroll
@@ -616,155 +631,173 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   }
   __syncthreads();
 
-  // ---- tail preparation (wave 0): unit maximum, proxy logits ---------------
-  if (w == 0) {
-    if constexpr (PROXY) {
-      const int h = lane % G;
-      float pi[R], nbf[R];
-      float hm = kNegInf;
+  // ---- proxy logits of the clusters this wave owns ------------------------
+  // Unread members of cluster b: n_b = count - (read members); their mean
+  // logit mu_b = (q.sumK_b - sum of the read members' logits) / n_b; the
+  // proxy logit is mu_b + log2(n_b).
+  float pi0 = kNegInf, pi1 = kNegInf;
+  if constexpr (PROXY) {
+    auto mean_logit = [&](int b, float qk, int cntb, float& pi) {
+      float ssum = 0.f;
+      int rc = 0;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int b = (lane + 64 * r) / G;
-        pi[r] = kNegInf;
-        nbf[r] = 0.f;
-        if (b < p.C) {
-          float ssum = 0.f;
-          int rc = 0;
-#pragma unroll
-          for (int ww = 0; ww < W; ++ww) {
-            ssum += s_csum[ww][b][h];
-            rc += s_ccnt[ww][b];
-          }
-          const int nb = cnt[r] - rc;
-          if (nb < 0 && h == 0) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
-          if (nb > 0) {
-            nbf[r] = (float)nb;
-            pi[r] = (s_qk[b][h] - ssum) / nbf[r] + __builtin_amdgcn_logf(nbf[r]);
-          }
-        }
-        hm = fmaxf(hm, pi[r]);
+      for (int ww = 0; ww < W; ++ww) {
+        ssum += s_csum[ww][b][hr];
+        rc += s_ccnt[ww][b];
       }
-#pragma unroll
-      for (int msk = G; msk < 64; msk <<= 1) hm = fmaxf(hm, shfl_xor(hm, msk));
-#pragma unroll
-      for (int ww = 0; ww < W; ++ww) hm = fmaxf(hm, s_wmax[ww][h]);
-      const float M = (hm == kNegInf) ? 0.f : hm;
-      float pe = 0.f;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int b = (lane + 64 * r) / G;
-        const float ev = (pi[r] == kNegInf) ? 0.f : fast_exp2(pi[r] - M);
-        pe += ev;
-        if (b < p.C) s_cw[b][h] = (nbf[r] > 0.f) ? ev / nbf[r] : 0.f;
+      const int nb = cntb - rc;
+      if (nb < 0 && r16 == 0) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
+      float mu = kNegInf;
+      if (nb > 0) {
+        const float nbf = (float)nb;
+        mu = (qk - ssum) / nbf;
+        pi = mu + __builtin_amdgcn_logf(nbf);
       }
-#pragma unroll
-      for (int msk = G; msk < 64; msk <<= 1) pe += shfl_xor(pe, msk);
-      if (lane < G) {
-        s_M[lane] = M;
-        s_pl[lane] = pe;
-      }
-    } else {
-      if (lane < G) {
-        float hm = kNegInf;
-#pragma unroll
-        for (int ww = 0; ww < W; ++ww) hm = fmaxf(hm, s_wmax[ww][lane]);
-        s_M[lane] = (hm == kNegInf) ? 0.f : hm;
-        s_pl[lane] = 0.f;
-      }
-    }
+      if (r16 < G) s_mu[b][r16] = mu;
+    };
+    if (has0) mean_logit(b0, qk0, cnt0, pi0);
+    if (has1) mean_logit(b1, qk1, cnt1, pi1);
+    if (r16 >= G) pi0 = pi1 = kNegInf;
+    const float pm = max_rowgroups(fmaxf(pi0, pi1));
+    if (sub == 0 && r16 < G) s_pmax[w][r16] = pm;
+    __syncthreads();
   }
-  __syncthreads();
 
-  // ---- weighted values (row layout) ----------------------------------------
-  float M[G];
+  // ---- unit maximum (every wave, same value) --------------------------------
+  float Mh = kNegInf;
 #pragma unroll
-  for (int h = 0; h < G; ++h) M[h] = s_M[h];
-  float acc[G][8], l[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    l[h] = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+  for (int ww = 0; ww < W; ++ww) {
+    Mh = fmaxf(Mh, s_wmax[ww][hr]);
+    if constexpr (PROXY) Mh = fmaxf(Mh, s_pmax[ww][hr]);
   }
+  if (Mh == kNegInf) Mh = 0.f;
+  if (w == 0 && sub == 0 && r16 < G) s_M[r16] = Mh;
+  // the proxies' share of the normaliser (lane sums, combined below)
+  float lsum = 0.f;
+  if constexpr (PROXY) {
+    if (pi0 != kNegInf) lsum += fast_exp2(pi0 - Mh);
+    if (pi1 != kNegInf) lsum += fast_exp2(pi1 - Mh);
+  }
+
+  // ---- weighted values on the matrix cores ---------------------------------
+  // One v_mfma_f32_16x16x32_bf16 per 16 keys and 16 dims. The weights
+  // w = exp2(x - M) (minus exp2(mu_b - M) for a read member of cluster b,
+  // whose value the proxy term below counts in the cluster's sum) go in as a
+  // bf16 high part and a bf16 remainder: lane (m = r16, group sub) holds, for
+  // head m and keys 4*sub + j, the high parts as A elements j and the
+  // remainders as elements 4 + j; the B operand repeats the four value
+  // elements, so one product sums both parts (about 16 significant bits of
+  // each weight, exact bf16 x bf16 products, fp32 accumulation).
+  // The values pass through LDS: ds_read_b64_tr_b16 gives lane n of group sub
+  // the rows 4*sub .. 4*sub+3 at column 16*nb + n when lane s of the group
+  // points at row 4*sub + s/4, column 16*nb + 4*(s%4).
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  bf16_t* vt = reinterpret_cast<bf16_t*>(s_pool + w * kWaveLds);
+  floatx4_t oacc[8];
 #pragma unroll
-  for (int k = 0; k < NS; ++k) {
-    const int kk = 4 * k + sub;
-    int ck = -1;
-    if constexpr (PROXY) ck = shfl_i(lc, kk);
-    float wt[G];
+  for (int nb = 0; nb < 8; ++nb) oacc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  auto tile_products = [&](const bf16x8_t a) {
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float ev = fast_exp2(s_x[w][kk][h] - M[h]);
-      l[h] += ev;
-      wt[h] = ev;
+    for (int nb = 0; nb < 8; ++nb) {
+      auto src = (__attribute__((address_space(3))) bf16x4_t*)(vt + (4 * sub + (r16 >> 2)) * kVRow +
+                                                               16 * nb + 4 * (r16 & 3));
+      const bf16x4_t b4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(src);
+      const bf16x8_t b = {b4[0], b4[1], b4[2], b4[3], b4[0], b4[1], b4[2], b4[3]};
+      oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, oacc[nb], 0, 0, 0);
     }
+  };
+  auto split = [](bf16x8_t& a, int j, float v) {
+    const __bf16 hi = (__bf16)v;
+    a[j] = hi;
+    a[4 + j] = (__bf16)(v - (float)hi);
+  };
+  const bool head_lane = r16 < G;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    // tile rows 4*kq + sub are value slot 4*t + kq of the row layout
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq)
+      *reinterpret_cast<uint4*>(vt + (4 * kq + sub) * kVRow + 8 * r16) = vc[4 * t + kq].raw;
+    const float4 x4 = *reinterpret_cast<const float4*>(&s_x[w][hr][16 * t + 4 * sub]);
+    const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+    int kcs[4] = {-1, -1, -1, -1};
+    float mus[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
     if constexpr (PROXY) {
-      // a read member leaves its cluster: subtract its share of the proxy's
-      // value term (the proxy below adds cw * the sum of all member values)
-      if (ck >= 0 && ck < p.C && voff[k] != kOOB) {
+      const int4 k4 = *reinterpret_cast<const int4*>(&s_kc[w][16 * t + 4 * sub]);
+      kcs[0] = k4.x; kcs[1] = k4.y; kcs[2] = k4.z; kcs[3] = k4.w;
 #pragma unroll
-        for (int h = 0; h < G; ++h) wt[h] -= s_cw[ck][h];
-      }
+      for (int j = 0; j < 4; ++j) mus[j] = s_mu[kcs[j] >= 0 ? kcs[j] : 0][hr];
     }
-    float vf[8];
-    vc[k].unpack(vf);
+    bf16x8_t a;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(wt[h], vf[i], acc[h][i]);
+    for (int j = 0; j < 4; ++j) {
+      const float ev = head_lane ? fast_exp2(xs[j] - Mh) : 0.f;
+      lsum += ev;
+      float wv = ev;
+      if constexpr (PROXY) {
+        if (head_lane && kcs[j] >= 0) wv -= fast_exp2(mus[j] - Mh);
+      }
+      split(a, j, wv);
+    }
+    tile_products(a);
   }
   if constexpr (PROXY) {
-    if (b0 < p.C) {
+    // Proxy value terms exp2(mu_b - M) * (sum of cluster b's values), as one
+    // more tile: rows sub and 4 + sub hold the bf16 high part and remainder
+    // of cluster b0's value sum, rows 8 + sub and 12 + sub those of cluster
+    // b1 (zero when absent); each row's weight is split as above.
+    auto put = [&](int row, const float (&f)[8], bool lo) {
+      bf16x8_t v;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const float cw = s_cw[b0][h];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(cw, svf[i], acc[h][i]);
+      for (int i = 0; i < 8; ++i) {
+        const __bf16 hi = (__bf16)f[i];
+        v[i] = lo ? (__bf16)(f[i] - (float)hi) : hi;
       }
-    }
-    if (p.C > 4 * W) {
-      const int b1 = b0 + 4 * W;
-      if (b1 < p.C) {
-        float sv1[8];
-        load8f(p.sumV + ((int64_t)u * p.C + b1) * kD + 8 * r16, sv1);
+      *reinterpret_cast<bf16x8_t*>(vt + row * kVRow + 8 * r16) = v;
+    };
+    put(sub, svf, false);
+    put(4 + sub, svf, true);
+    put(8 + sub, sv1, false);
+    put(12 + sub, sv1, true);
+    float cws[4];
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float cw = s_cw[b1][h];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(cw, sv1[i], acc[h][i]);
-        }
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int b = 4 * w + j + (sub >= 2 ? 4 * W : 0);
+      cws[j] = s_mu[b][hr];
+      cws[j] = (head_lane && b < p.C && cws[j] != kNegInf) ? fast_exp2(cws[j] - Mh) : 0.f;
     }
+    bf16x8_t a;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) split(a, j, cws[j]);
+    tile_products(a);
   }
 
-  // ---- reduce row groups, then waves ---------------------------------------
+  // ---- per-wave partials, then the unit's combine ---------------------------
+  // accumulator element i of lane (n, group sub): head 4*sub + i, dim 16*nb + n
+  float* red = reinterpret_cast<float*>(s_pool + w * kWaveLds);
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * sub + i;
+    if (h < G) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[h][i] = sum_rowgroups(acc[h][i]);
-    l[h] = sum_rowgroups(l[h]);
-  }
-  if (sub == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      *reinterpret_cast<float4*>(&s_red[w][h][8 * r16]) = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-      *reinterpret_cast<float4*>(&s_red[w][h][8 * r16 + 4]) = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
-      if (r16 == 0) s_l[w][h] = l[h];
+      for (int nb = 0; nb < 8; ++nb) red[h * kD + 16 * nb + r16] = oacc[nb][i];
     }
   }
+  lsum = sum_rowgroups(lsum);  // all keys and owned proxies of the wave, head r16
+  if (sub == 0 && r16 < G) s_l[w][r16] = lsum;
   __syncthreads();
 
   for (int ei = tid; ei < G * kD; ei += 512) {
-    const int h = ei / kD, dim = ei - h * kD;
-    float a = 0.f, L = s_pl[h];
+    const int h = ei / kD;
+    float a = 0.f, L = 0.f;
 #pragma unroll
     for (int ww = 0; ww < W; ++ww) {
-      a += s_red[ww][h][dim];
+      a += reinterpret_cast<const float*>(s_pool + ww * kWaveLds)[ei];
       L += s_l[ww][h];
     }
     const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
-    p.out[qh * kD + dim] = (L > 0.f) ? a / L : 0.f;
-    if (dim == 0 && p.lse) p.lse[qh] = (L > 0.f) ? (s_M[h] + log2f(L)) * kLn2 : kNegInf;
+    p.out[qh * kD + (ei - h * kD)] = (L > 0.f) ? a / L : 0.f;
+    if (ei - h * kD == 0 && p.lse) p.lse[qh] = (L > 0.f) ? (s_M[h] + log2f(L)) * kLn2 : kNegInf;
   }
 }
 
