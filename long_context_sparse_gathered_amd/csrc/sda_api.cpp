@@ -132,10 +132,14 @@ sda_status plan_sparse(const Resolved& r, int kind, int m, SparsePlan* pl) {
     }
   }
   if (kind == SDA_TAIL_SAMPLED) {
-    // one workgroup per unit; scratch: fp64 logits/weights of the listed rows
-    // and base draws, and the positions of the fresh draws
-    if (m > kSampMaxList) return SDA_EUNSUPPORTED;
-    pl->ws = (size_t)units * ((size_t)(m + kSampMaxB0) * r.G * sizeof(double) + (size_t)r.n * sizeof(int32_t));
+    // scratch per unit: the fp64 exact part (M, D_f, N_f), the draw
+    // partials, the budget and the work-item numbering
+    if (m > kSampMaxList || units > kSampMaxUnits) return SDA_EUNSUPPORTED;
+    pl->splits = sampled_exact_splits(units);
+    pl->ws = (size_t)units * ((size_t)(1 + pl->splits) * r.G * (2 + kD) * sizeof(double) +
+                              (size_t)sampled_max_items(r.n) * r.G * kDrawRec * sizeof(float) +
+                              2 * sizeof(int32_t)) +
+             sizeof(int32_t);
     return SDA_OK;
   }
   if (kind == SDA_TAIL_NONE || kind == SDA_TAIL_PRIOR) {
@@ -377,10 +381,18 @@ SDA_EXPORT sda_status sda_sparse_decode_attn(const sda_dims* dims, const void* q
   if (pl.ws && (!ws || ws_bytes < pl.ws)) return SDA_EWORKSPACE;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (kind == SDA_TAIL_SAMPLED) {
-    const size_t logit_bytes = (size_t)r.B * r.Hkv * (size_t)(m + kSampMaxB0) * r.G * sizeof(double);
-    p.wlog = reinterpret_cast<double*>(ws);
-    p.wpos = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) + logit_bytes);
-    // the kernel indexes logits with a per-unit stride of (m + b0) rows
+    const size_t units = (size_t)r.B * r.Hkv;
+    char* w = reinterpret_cast<char*>(ws);
+    p.wstat = reinterpret_cast<double*>(w);
+    w += units * (size_t)r.G * (2 + kD) * sizeof(double);
+    p.splits = pl.splits;
+    p.wexact = reinterpret_cast<double*>(w);
+    w += units * (size_t)pl.splits * r.G * (2 + kD) * sizeof(double);
+    p.part = reinterpret_cast<float*>(w);
+    w += units * (size_t)sampled_max_items(r.n) * r.G * kDrawRec * sizeof(float);
+    p.wb = reinterpret_cast<int32_t*>(w);
+    w += units * sizeof(int32_t);
+    p.wsched = reinterpret_cast<int32_t*>(w);
     return hip_status(launch_sampled(p, r.dtype, r.G, hs));
   }
   if (pl.unit) {

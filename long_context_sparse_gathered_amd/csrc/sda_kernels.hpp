@@ -54,8 +54,10 @@ struct AttnParams {
   int32_t* b_out;              // [B,Hkv] or null
   double* bstar_out;           // [B,Hkv] or null
   int32_t* samples_out;        // [B,Hkv,b_cap] or null
-  double* wlog;                // workspace: [units, m + b0, G] fp64 logits / weights
-  int32_t* wpos;               // workspace: [units, n] drawn positions
+  double* wstat;               // workspace: [units, G*(2 + d)] fp64 M, D_f, N_f of the exact part
+  double* wexact;              // workspace: [units, splits, G*(2 + d)] fp64 records of the I_f shares
+  int32_t* wb;                 // workspace: [units] sample budget b
+  int32_t* wsched;             // workspace: [units + 1] first draw work item of each unit
 
   // split-K
   int32_t splits;              // WGs per unit
@@ -100,6 +102,18 @@ hipError_t launch_sampled(const AttnParams& p, int dtype, int G, hipStream_t st)
 // Sampled tail limits: the deterministic list and the base draws live in LDS.
 constexpr int kSampMaxList = 4096;
 constexpr int kSampMaxB0 = 256;
+// The fresh draws are cut into work items of kDrawChunk draws, numbered unit
+// by unit; each draw workgroup takes a contiguous range of work items.
+constexpr int kDrawChunk = 256;
+constexpr int kDrawRec = 4 + 128;        // floats per (work item, head) partial: m, l, -, -, acc[d]
+constexpr int kSampMaxUnits = 4096;
+constexpr int kDrawGrid = 768;           // draw workgroups (upper bound): three per CU
+__host__ __device__ inline int sampled_max_items(int n) { return (n + kDrawChunk - 1) / kDrawChunk; }
+// Workgroups per unit that share the exact pass over I_f (about 256 in all).
+inline int sampled_exact_splits(int units) {
+  const int s = 256 / units;
+  return s < 1 ? 1 : (s > 8 ? 8 : s);
+}
 hipError_t launch_proxy_build(const ProxyBuildParams& p, int dtype, int units, hipStream_t st);
 
 // Largest slot count the one-workgroup-per-unit kernel is built for.
