@@ -69,16 +69,15 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
-// Split-K shape for the streaming kernel: enough workgroups to fill the chip
-// several times over, chunks a multiple of one batch of rows (64).
-void stream_shape(int units, int len, int min_chunk, int* splits, int* chunk) {
-  const int target_wgs = 2048;
+// Split-K shape for the streaming kernels: enough workgroups to fill the chip
+// several times over, chunks a multiple of one batch of rows of either kernel.
+void stream_shape(int units, int len, int min_chunk, int target_wgs, int* splits, int* chunk) {
   int sp = ceil_div(target_wgs, units);
   const int max_sp = len > 0 ? ceil_div(len, min_chunk) : 1;
   if (sp > max_sp) sp = max_sp;
   if (sp < 1) sp = 1;
   int ch = ceil_div(len > 0 ? len : 1, sp);
-  ch = ceil_div(ch, 64) * 64;
+  ch = ceil_div(ch, kStreamMfmaStep) * kStreamMfmaStep;
   sp = len > 0 ? ceil_div(len, ch) : 1;
   *splits = sp;
   *chunk = ch;
@@ -143,15 +142,25 @@ sda_status plan_sparse(const Resolved& r, int kind, int m, SparsePlan* pl) {
     return SDA_OK;
   }
   if (kind == SDA_TAIL_NONE || kind == SDA_TAIL_PRIOR) {
-    stream_shape(units, m, 256, &pl->splits, &pl->chunk);
+    // the matrix-core kernel runs two workgroups per CU: one round of long
+    // workgroups beats several rounds of short ones
+    const bool mfma = r.dtype == SDA_BF16 && (kind == SDA_TAIL_NONE || 3 * r.G <= 16);
+    stream_shape(units, m, 256, mfma ? 512 : 2048, &pl->splits, &pl->chunk);
     if (pl->splits > 1) pl->ws = (size_t)units * pl->splits * r.G * kPartStride * sizeof(float);
     return SDA_OK;
   }
   return SDA_EUNSUPPORTED;
 }
 
+// bf16 streams run on the matrix-core kernel (the prior when 3G <= 16).
+hipError_t launch_stream_any(const AttnParams& p, const Resolved& r, int mode, hipStream_t hs) {
+  if (r.dtype == SDA_BF16 && (mode == kModeSparse || mode == kModeDense || (mode == kModePrior && 3 * r.G <= 16)))
+    return launch_stream_mfma(p, r.G, mode, hs);
+  return launch_stream(p, r.dtype, r.G, mode, hs);
+}
+
 void dense_shape(const Resolved& r, int* splits, int* chunk) {
-  stream_shape(r.B * r.Hkv, r.n, 512, splits, chunk);
+  stream_shape(r.B * r.Hkv, r.n, 512, 2048, splits, chunk);
 }
 
 size_t dense_ws(const Resolved& r, bool build) {
@@ -306,7 +315,7 @@ SDA_EXPORT sda_status sda_dense_decode_attn(const sda_dims* dims, const void* q,
   p.out = out;
   p.lse = lse;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = launch_stream(p, r.dtype, r.G, kModeDense, hs);
+  hipError_t e = launch_stream_any(p, r, kModeDense, hs);
   if (e == hipSuccess && p.splits > 1) e = launch_merge(p, r.G, kModeDense, hs);
   return hip_status(e);
 }
@@ -403,7 +412,7 @@ SDA_EXPORT sda_status sda_sparse_decode_attn(const sda_dims* dims, const void* q
   p.chunk = pl.chunk;
   p.part = reinterpret_cast<float*>(ws);
   const int mode = kind == SDA_TAIL_PRIOR ? kModePrior : kModeSparse;
-  hipError_t e = launch_stream(p, r.dtype, r.G, mode, hs);
+  hipError_t e = launch_stream_any(p, r, mode, hs);
   if (e == hipSuccess && p.splits > 1) e = launch_merge(p, r.G, mode, hs);
   return hip_status(e);
 }

@@ -1189,6 +1189,321 @@ __global__ __launch_bounds__(256) void stream_kernel(const AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// bf16 split-K streaming kernel with both products on the matrix cores.
+//
+// A workgroup (4 waves) takes entries [t0, t1) of one unit; per batch each
+// wave takes 16*NT consecutive entries.  The logits come from
+// v_mfma_f32_16x16x32_bf16 with the A operand rows holding the G query heads
+// and, for the prior, the G mean queries mu_Q split into a bf16 high part
+// (rows G..2G-1) and remainder (rows 2G..3G-1), so that sigma mu_Q.k keeps
+// fp32 accuracy.  An online softmax runs across batches: the batch maximum of
+// each head goes through LDS, the accumulator rows are rescaled in the
+// accumulator layout and the normaliser in the operand layout, from the same
+// values.  The weighted values use the same transposed-LDS products as the
+// one-workgroup-per-unit kernel, with the prior weights exp(P - maxP) as A
+// rows G..2G-1 (fixed shift, no rescaling).  Partial records and the merge
+// are those of stream_kernel.
+template <int G, int MODE, int NT>
+__global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
+  constexpr int W = 4;
+  constexpr bool DENSE = (MODE == kModeDense);
+  constexpr bool PRIOR = (MODE == kModePrior);
+  constexpr int RA = PRIOR ? 3 * G : G;  // A rows of the logits
+  constexpr int RP = PRIOR ? 2 * G : G;  // A rows of the weighted values
+  static_assert(RA <= 16, "the logit rows fit one 16-row block");
+  constexpr int KB = 16 * NT;            // entries per wave per batch
+  constexpr int STEP = W * KB;           // entries per workgroup per batch
+  constexpr int NS = 4 * NT;             // value slots per wave per batch
+  constexpr int kVRow = 144;             // bf16 elements per staged value row
+  constexpr int kTile = 16 * kVRow * 2;
+  constexpr int kWaveLds = kTile > RP * kD * 4 ? kTile : RP * kD * 4;
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  const int u = blockIdx.x / p.splits;
+  const int split = blockIdx.x - u * p.splits;
+  const int s = u / p.Hkv;
+  const int g = u - s * p.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, sub = lane >> 4;
+  const int hr = r16 < G ? r16 : 0;
+
+  __shared__ __attribute__((aligned(16))) float s_x[W][RA][KB];
+  __shared__ float s_bm[W][G];
+  __shared__ float s_m[W][G], s_l[W][G], s_sp[W][G];
+  __shared__ float s_c[G];
+  __shared__ __attribute__((aligned(16))) unsigned char s_pool[W * kWaveLds];
+
+  // ---- A operand: row r16, dims 32*st + 8*sub .. +8 ---------------------------
+  const int64_t qrow0 = (int64_t)s * p.Hq + (int64_t)g * G;
+  uint4 qa[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    qa[st] = make_uint4(0, 0, 0, 0);
+    if (r16 < G) {
+      qa[st] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(p.q) + (qrow0 + r16) * kD + 32 * st +
+                                                8 * sub);
+    } else if (PRIOR && r16 < 3 * G) {
+      const int h = (r16 - G) % G;
+      float mq[8];
+      load8f(p.mu_Q + (qrow0 + h) * kD + 32 * st + 8 * sub, mq);
+      bf16x8_t v;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const __bf16 hi = (__bf16)mq[i];
+        v[i] = r16 < 2 * G ? hi : (__bf16)(mq[i] - (float)hi);
+      }
+      qa[st] = __builtin_bit_cast(uint4, v);
+    }
+  }
+  // prior shift maxP (log2 units) of the operand-layout head r16 - G
+  float mPa = 0.f;
+  if (PRIOR && r16 >= G && r16 < 2 * G) mPa = p.maxP[qrow0 + r16 - G] * kLog2e;
+
+  int len = DENSE ? p.n : p.m;
+  if (!DENSE && p.idx_len) {
+    int L = p.idx_len[u];
+    if (L < 0 || L > p.m) {
+      if (tid == 0 && split == 0) flag_unit(p.flags, u, SDA_FLAG_LEN);
+      L = L < 0 ? 0 : p.m;
+    }
+    len = L;
+  }
+  const int t0 = split * p.chunk;
+  const int t1 = min(len, t0 + p.chunk);
+  const int64_t lbase = (int64_t)u * p.m;
+  const int64_t kvoff = (int64_t)s * p.sb + (int64_t)g * p.sh;
+  const rsrc_t rk = make_rsrc<bf16_t>(reinterpret_cast<const bf16_t*>(p.K) + kvoff, p.n, p.sn);
+  const rsrc_t rv = make_rsrc<bf16_t>(reinterpret_cast<const bf16_t*>(p.V) + kvoff, p.n, p.sn);
+
+  // list entry of this lane for the batch at tb: tb + w*KB + lane (lane < KB)
+  int li = -1, lp = -1;
+  float lwv = 0.f;
+  auto load_list = [&](int tb, int& vi, int& vp, float& vw) {
+    const int t = tb + w * KB + lane;
+    const bool in = lane < KB && t < t1;
+    const int64_t a = lbase + (in ? t : 0);
+    vi = p.idx[a];
+    if (PRIOR) vp = p.idx[lbase + ((in && t > 0) ? t - 1 : 0)];
+    if (p.logw) vw = p.logw[a];
+  };
+  if (!DENSE && t0 < t1) load_list(t0, li, lp, lwv);
+
+  floatx4_t oacc[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) oacc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float m_a = kNegInf;                                     // running max of head r16
+  float m_d[4] = {kNegInf, kNegInf, kNegInf, kNegInf};     // running max of rows 4*sub + i
+  float lsum = 0.f, spsum = 0.f;
+  bf16_t* vt = reinterpret_cast<bf16_t*>(s_pool + w * kWaveLds);
+
+  for (int tb = t0; tb < t1; tb += STEP) {
+    const int e = tb + w * KB + lane;  // this lane's entry
+    bool valid;
+    int row;
+    float lw_own;
+    if constexpr (DENSE) {
+      valid = lane < KB && e < t1;
+      row = valid ? e : 0;
+      lw_own = valid ? 0.f : kNegInf;
+    } else {
+      const bool live = lane < KB && e < t1;
+      valid = live && (unsigned)li < (unsigned)p.n;
+      row = li;
+      lw_own = valid ? (p.logw ? lwv * kLog2e : 0.f) : kNegInf;
+      int bad = 0;
+      if (live && (unsigned)li >= (unsigned)p.n) bad |= SDA_FLAG_IDX_RANGE;
+      if (PRIOR && live && e > 0 && lp >= li) bad |= SDA_FLAG_IDX_ORDER;
+      if (bad) flag_unit(p.flags, u, bad);
+    }
+    int koff[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int src = 16 * t + r16;
+      const int j = shfl_i(row, src);
+      const bool ok = shfl_i(valid ? 1 : 0, src) != 0;
+      koff[t] = ok ? (int)(((int64_t)j * p.sn + 8 * sub) * 2) : kOOB;
+    }
+    int voff[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int src = 4 * k + sub;
+      const int j = shfl_i(row, src);
+      const bool ok = shfl_i(valid ? 1 : 0, src) != 0;
+      voff[k] = ok ? row_off<bf16_t>(j, p.sn, r16) : kOOB;
+    }
+    uint4 kt[NT][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[t] + 64 * st, 0, 0);
+        kt[t][st] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+    RowChunk<bf16_t> vc[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) buf_load(vc[k], rv, voff[k]);
+    if constexpr (!DENSE) {
+      if (tb + STEP < t1) load_list(tb + STEP, li, lp, lwv);
+    }
+
+    // ---- logits ---------------------------------------------------------------
+    float bmx[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      floatx4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
+                                                    __builtin_bit_cast(bf16x8_t, kt[t][st]), d, 0, 0, 0);
+      const int kk = 16 * t + r16;
+      const float lwk = shfl_f(lw_own, kk);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * sub + i;
+        if (r < G) {
+          const float xv = d[i] * p.qscale + lwk;
+          s_x[w][r][kk] = xv;
+          bmx[i] = fmaxf(bmx[i], xv);
+        } else if (r < RA) {
+          s_x[w][r][kk] = lwk == kNegInf ? kNegInf : d[i];
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = max16(bmx[i]);
+      if (r16 == 0 && 4 * sub + i < G) s_bm[w][4 * sub + i] = v;
+    }
+    // ---- online rescale (same values in both layouts) --------------------------
+    {
+      const float mn = fmaxf(m_a, s_bm[w][hr]);
+      const float al = rescale(m_a, mn);
+      lsum *= al;
+      m_a = mn;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * sub + i;
+        if (r < G) {
+          const float mnd = fmaxf(m_d[i], s_bm[w][r]);
+          const float ad = rescale(m_d[i], mnd);
+          m_d[i] = mnd;
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) oacc[nb][i] *= ad;
+        }
+      }
+    }
+    // ---- weighted values ------------------------------------------------------
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int kq = 0; kq < 4; ++kq)
+        *reinterpret_cast<uint4*>(vt + (4 * kq + sub) * kVRow + 8 * r16) = vc[4 * t + kq].raw;
+      const float4 x4 = *reinterpret_cast<const float4*>(&s_x[w][r16 < RP ? r16 : 0][16 * t + 4 * sub]);
+      float4 y4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if constexpr (PRIOR) y4 = *reinterpret_cast<const float4*>(&s_x[w][r16 >= G && r16 < 2 * G ? r16 + G : 0][16 * t + 4 * sub]);
+      const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+      const float ys[4] = {y4.x, y4.y, y4.z, y4.w};
+      bf16x8_t a;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // one exp per lane: softmax rows (r16 < G) and prior rows (G <= r16 < 2G)
+        float arg;
+        if constexpr (PRIOR) {
+          arg = r16 < G ? xs[j] - m_a : (xs[j] + ys[j]) * p.qscale - mPa;
+        } else {
+          arg = xs[j] - m_a;
+        }
+        float wv = fast_exp2(arg);  // exp2(-inf) = 0 for absent keys
+        if (r16 >= RP || (r16 < G && m_a == kNegInf)) wv = 0.f;
+        if (r16 < G) lsum += wv;
+        if (PRIOR && r16 >= G) spsum += wv;
+        const __bf16 hi = (__bf16)wv;
+        a[j] = hi;
+        a[4 + j] = (__bf16)(wv - (float)hi);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        auto src = (__attribute__((address_space(3))) bf16x4_t*)(vt + (4 * sub + (r16 >> 2)) * kVRow + 16 * nb +
+                                                                 4 * (r16 & 3));
+        const bf16x4_t b4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(src);
+        const bf16x8_t b = {b4[0], b4[1], b4[2], b4[3], b4[0], b4[1], b4[2], b4[3]};
+        oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, oacc[nb], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- wave results -------------------------------------------------------------
+  float* red = reinterpret_cast<float*>(s_pool + w * kWaveLds);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * sub + i;
+    if (r < RP) {
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) red[r * kD + 16 * nb + r16] = oacc[nb][i];
+    }
+  }
+  lsum = sum_rowgroups(lsum);
+  spsum = sum_rowgroups(spsum);
+  if (sub == 0 && r16 < G) {
+    s_l[w][r16] = lsum;
+    s_m[w][r16] = m_a;
+  }
+  if (PRIOR && sub == 0 && r16 >= G && r16 < 2 * G) s_sp[w][r16 - G] = spsum;
+  if constexpr (PRIOR) {
+    if (split == 0 && w == 0) {
+      float qf[G][8];
+      load_query<bf16_t, G>(p.q, qrow0, r16, p.qscale, qf);
+      float c[G];
+      bias_shift<G>(p, s, g, r16, qf, c);
+      if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) s_c[h] = c[h];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int ei = tid; ei < G * kD; ei += 256) {
+    const int h = ei / kD, dim = ei - h * kD;
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww) M = fmaxf(M, s_m[ww][h]);
+    float a = 0.f, L = 0.f, SP = 0.f, SPV = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww) {
+      const float* rw = reinterpret_cast<const float*>(s_pool + ww * kWaveLds);
+      const float f = rescale(s_m[ww][h], M);
+      a = fmaf(rw[h * kD + dim], f, a);
+      L = fmaf(s_l[ww][h], f, L);
+      if constexpr (PRIOR) {
+        SP += s_sp[ww][h];
+        SPV += rw[(G + h) * kD + dim];
+      }
+    }
+    const int64_t qh = qrow0 + h;
+    if (p.splits > 1) {
+      float* rec = p.part + (((int64_t)u * p.splits + split) * G + h) * kPartStride;
+      if (dim == 0) {
+        rec[0] = M;
+        rec[1] = L;
+        rec[2] = SP;
+        rec[3] = (PRIOR && split == 0) ? s_c[h] : 0.f;
+      }
+      rec[4 + dim] = a;
+      if constexpr (PRIOR) rec[4 + kD + dim] = SPV;
+    } else if constexpr (PRIOR) {
+      const Fin f = finalize_prior(M, L, a, s_c[h], p.maxP[qh] * kLog2e, p.sumP[qh], p.O_est[qh * kD + dim],
+                                   SP, SPV, p.lambda);
+      p.out[qh * kD + dim] = f.out;
+      if (dim == 0 && p.lse) p.lse[qh] = f.lse;
+    } else {
+      const Fin f = finalize_plain(M, L, a);
+      p.out[qh * kD + dim] = f.out;
+      if (dim == 0 && p.lse) p.lse[qh] = f.lse;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Merge of split partials: one workgroup per unit, fixed split order.
 template <int G, int MODE>
 __global__ __launch_bounds__(256) void merge_kernel(const AttnParams p) {
@@ -1336,6 +1651,33 @@ static hipError_t launch_stream_t(const AttnParams& p, int G, int mode, hipStrea
     case 2: return launch_stream_g<T, 2>(p, mode, st);
     case 4: return launch_stream_g<T, 4>(p, mode, st);
     case 8: return launch_stream_g<T, 8>(p, mode, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int G>
+static hipError_t launch_stream_mfma_g(const AttnParams& p, int mode, hipStream_t st) {
+  const dim3 grid(p.B * p.Hkv * p.splits), block(256);
+  switch (mode) {
+    case kModeSparse: hipLaunchKernelGGL((stream_mfma_kernel<G, kModeSparse, kStreamMfmaTiles>), grid, block, 0, st, p); break;
+    case kModeDense: hipLaunchKernelGGL((stream_mfma_kernel<G, kModeDense, kStreamMfmaTiles>), grid, block, 0, st, p); break;
+    case kModePrior:
+      if constexpr (3 * G <= 16) {
+        hipLaunchKernelGGL((stream_mfma_kernel<G, kModePrior, kStreamMfmaTiles>), grid, block, 0, st, p);
+        break;
+      }
+      return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_mfma(const AttnParams& p, int G, int mode, hipStream_t st) {
+  switch (G) {
+    case 1: return launch_stream_mfma_g<1>(p, mode, st);
+    case 2: return launch_stream_mfma_g<2>(p, mode, st);
+    case 4: return launch_stream_mfma_g<4>(p, mode, st);
+    case 8: return launch_stream_mfma_g<8>(p, mode, st);
   }
   return hipErrorInvalidValue;
 }

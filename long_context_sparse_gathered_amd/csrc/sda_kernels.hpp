@@ -97,6 +97,11 @@ hipError_t launch_sparse_unit(const AttnParams& p, int dtype, int G, bool proxy,
                               hipStream_t st);
 hipError_t launch_stream(const AttnParams& p, int dtype, int G, int mode, hipStream_t st);
 hipError_t launch_merge(const AttnParams& p, int G, int mode, hipStream_t st);
+// bf16 split-K kernel on the matrix cores: entries per workgroup per batch
+// are 64 * kStreamMfmaTiles; the prior needs 3G <= 16.
+constexpr int kStreamMfmaTiles = 2;
+constexpr int kStreamMfmaStep = 64 * kStreamMfmaTiles;
+hipError_t launch_stream_mfma(const AttnParams& p, int G, int mode, hipStream_t st);
 hipError_t launch_sampled(const AttnParams& p, int dtype, int G, hipStream_t st);
 
 // Sampled tail limits: the deterministic list and the base draws live in LDS.
