@@ -104,7 +104,7 @@ sda_status plan_sparse(const Resolved& r, int kind, int m, SparsePlan* pl) {
   int ns = 0, unit_chunk = 0;
   if (r.dtype == SDA_BF16) {
     const int tiles = ceil_div(ceil_div(m, kUnitWaves), 16);
-    if (m > 0 && tiles <= 4) {
+    if (m > 0 && tiles <= unit_max_tiles(r.G)) {
       ns = 4 * (tiles > 0 ? tiles : 1);
       unit_chunk = 16 * tiles;
     } else if (m == 0) {

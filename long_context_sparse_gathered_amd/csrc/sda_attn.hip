@@ -429,6 +429,31 @@ __global__ __launch_bounds__(512) void sparse_unit_kernel(const AttnParams p) {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
+// Streaming cache policy for rows read once (the nt bit of the buffer load).
+constexpr int kLoadNT = 2;
+// s_waitcnt immediate: vector memory count 0, the other counters unrestricted.
+constexpr int kWaitVmem0 = 0x0F70;
+// A value tile: 16 rows of 128 bf16 (256 bytes) in LDS.
+constexpr int kVTile = 16 * 256;
+// Position of 16-byte chunk c of tile row r: rows 4q..4q+3 spread a chunk pair
+// over 4 x 32 bytes, and odd row quads use the other half of the banks.
+__device__ __forceinline__ int vt_chunk(int r, int c) { return c ^ (2 * (r & 3)) ^ (8 * ((r >> 2) & 1)); }
+// Workgroup barrier over LDS data only: each wave waits for its own LDS
+// operations, while loads that write LDS directly stay in flight (the fence of
+// __syncthreads would wait for those too).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// LDS atomic adds without a return value. Written out so that the compiler
+// does not order them behind the loads that fill the value tiles (it treats
+// any LDS atomic as possibly overlapping those); the targets here never do.
+__device__ __forceinline__ void lds_add(float* p, float v) {
+  const unsigned a = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)p;
+  asm volatile("ds_add_f32 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+__device__ __forceinline__ void lds_add(int* p, int v) {
+  const unsigned a = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int*)p;
+  asm volatile("ds_add_u32 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+
 template <int G, bool PROXY, int NT>
 __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams p) {
   constexpr int W = kUnitWaves;
@@ -453,12 +478,13 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   __shared__ float s_csum[PW][PC][G];
   __shared__ int s_ccnt[PW][PC];
   __shared__ float s_mu[PC][G];  // mean logit of a cluster's unread members (-inf if none)
-  // Per wave: one 16-row value tile for the transposed reads (rows padded to
-  // 288 bytes against bank conflicts), then the wave's [G][kD] partial sums.
-  constexpr int kVRow = 144;  // bf16 elements per staged row
-  constexpr int kWaveLds = 16 * kVRow * 2;
-  static_assert(G * kD * 4 <= kWaveLds, "partials must fit the tile");
-  __shared__ __attribute__((aligned(16))) unsigned char s_pool[W * kWaveLds];
+  // Value tiles, written by the row loads straight into LDS: per wave NT
+  // tiles of 16 rows x 256 bytes, 16-byte chunks swizzled (vt_chunk) so that
+  // the transposed reads are free of bank conflicts. After the products, tile
+  // 0 of each wave holds the cluster-sum tile and then the wave's [G][kD]
+  // partial sums.
+  static_assert(G * kD * 4 <= kVTile, "partials must fit a tile");
+  __shared__ __attribute__((aligned(16))) unsigned char s_vt[W][NT][kVTile];
 
   // ---- prologue ------------------------------------------------------------
   const int64_t qrow0 = (int64_t)s * p.Hq + (int64_t)g * G;
@@ -545,6 +571,19 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     voff[k] = ok ? row_off<bf16_t>(j, p.sn, r16) : kOOB;
   }
 
+  // ---- checks and cluster lookups, ahead of the row loads ------------------
+  {
+    int bad = 0;
+    if (live && !in_range) bad |= SDA_FLAG_IDX_RANGE;
+    if (PROXY && live && e > 0 && lp >= li) bad |= SDA_FLAG_IDX_ORDER;
+    if (bad_cluster) bad |= SDA_FLAG_CLUSTER;
+    if (bad) flag_unit(p.flags, u, bad);
+  }
+  if constexpr (PROXY) {
+    if (!p.idx_cluster) lc = valid ? p.cluster_id[(int64_t)u * p.n + (valid ? li : 0)] : -1;
+  }
+
+  // ---- row loads (streaming: read once) -------------------------------------
   const int64_t kvoff = (int64_t)s * p.sb + (int64_t)g * p.sh;
   const rsrc_t rk = make_rsrc<bf16_t>(reinterpret_cast<const bf16_t*>(p.K) + kvoff, p.n, p.sn);
   const rsrc_t rv = make_rsrc<bf16_t>(reinterpret_cast<const bf16_t*>(p.V) + kvoff, p.n, p.sn);
@@ -553,25 +592,18 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[t] + 64 * st, 0, 0);
+      auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[t] + 64 * st, 0, kLoadNT);
       kt[t][st] = make_uint4(v[0], v[1], v[2], v[3]);
     }
-  if constexpr (PROXY) {
-    // cluster of each own list entry (after the keys so that waiting for it
-    // does not wait for the values)
-    if (!p.idx_cluster) lc = valid ? p.cluster_id[(int64_t)u * p.n + (valid ? li : 0)] : -1;
-  }
-  RowChunk<bf16_t> vc[NS];
+  // value slot k = 4t + kq (entries 16t + 4kq + sub) fills tile t, rows
+  // 4kq .. 4kq+3: lane (sub, r16) lands at row 4kq + sub, chunk position r16,
+  // so it fetches the chunk that the swizzle puts there
 #pragma unroll
-  for (int k = 0; k < NS; ++k) buf_load(vc[k], rv, voff[k]);
-
-  // ---- checks and proxy preparation while the rows are in flight ----------
-  {
-    int bad = 0;
-    if (live && !in_range) bad |= SDA_FLAG_IDX_RANGE;
-    if (PROXY && live && e > 0 && lp >= li) bad |= SDA_FLAG_IDX_ORDER;
-    if (bad_cluster) bad |= SDA_FLAG_CLUSTER;
-    if (bad) flag_unit(p.flags, u, bad);
+  for (int k = 0; k < NS; ++k) {
+    const int t = k >> 2, kq = k & 3;
+    const int off = voff[k] == kOOB ? kOOB : voff[k] - 16 * r16 + 16 * vt_chunk(4 * kq + sub, r16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)&s_vt[w][t][kq * 1024], 16, off,
+                                             0, 0, kLoadNT);
   }
   float qk0 = 0.f, qk1 = 0.f;  // q . (sum of keys) of clusters b0, b1 for head r16
   if constexpr (PROXY) {
@@ -604,23 +636,29 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     const float lwk = shfl_f(lw_own, kk);
     const int ck = PROXY ? shfl_i(lc, kk) : -1;
     const bool key_ok = lwk != kNegInf;
+    float sv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h = 4 * sub + i;
+      sv[i] = d[i] * p.qscale;
       if (h < G) {
-        const float sv = d[i] * p.qscale;
-        const float xv = sv + lwk;
+        const float xv = sv[i] + lwk;
         s_x[w][h][kk] = xv;
         mx[i] = fmaxf(mx[i], xv);
-        if constexpr (PROXY) {
-          if (key_ok && ck >= 0 && ck < p.C) atomicAdd(&s_csum[w][ck][h], sv);
-        }
       }
     }
     if constexpr (PROXY) {
-      const bool member = key_ok && ck >= 0 && ck < p.C;
-      if (member && sub == 0) atomicAdd(&s_ccnt[w][ck], 1);
-      if (sub == 0) s_kc[w][kk] = member ? ck : -1;
+      // read members' logit sums and counts per cluster (this wave's slice):
+      // a segmented sum over runs of keys with the same cluster (consecutive
+      // lanes of the row group); the last lane of each run adds the run total
+      const int cm = (key_ok && ck >= 0 && ck < p.C) ? ck : -1;
+      if (sub == 0) s_kc[w][kk] = cm;
+      if (cm >= 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (4 * sub + i < G) lds_add(&s_csum[w][cm][4 * sub + i], sv[i]);
+        if (sub == 0) lds_add(&s_ccnt[w][cm], 1);
+      }
     }
   }
 #pragma unroll
@@ -629,7 +667,7 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     const int h = 4 * sub + i;
     if (r16 == 0 && h < G) s_wmax[w][h] = v;
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- proxy logits of the clusters this wave owns ------------------------
   // Unread members of cluster b: n_b = count - (read members); their mean
@@ -660,7 +698,7 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     if (r16 >= G) pi0 = pi1 = kNegInf;
     const float pm = max_rowgroups(fmaxf(pi0, pi1));
     if (sub == 0 && r16 < G) s_pmax[w][r16] = pm;
-    __syncthreads();
+    lds_barrier();
   }
 
   // ---- unit maximum (every wave, same value) --------------------------------
@@ -682,27 +720,34 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   // ---- weighted values on the matrix cores ---------------------------------
   // One v_mfma_f32_16x16x32_bf16 per 16 keys and 16 dims. The weights
   // w = exp2(x - M) (minus exp2(mu_b - M) for a read member of cluster b,
-  // whose value the proxy term below counts in the cluster's sum) go in as a
-  // bf16 high part and a bf16 remainder: lane (m = r16, group sub) holds, for
-  // head m and keys 4*sub + j, the high parts as A elements j and the
-  // remainders as elements 4 + j; the B operand repeats the four value
-  // elements, so one product sums both parts (about 16 significant bits of
-  // each weight, exact bf16 x bf16 products, fp32 accumulation).
-  // The values pass through LDS: ds_read_b64_tr_b16 gives lane n of group sub
-  // the rows 4*sub .. 4*sub+3 at column 16*nb + n when lane s of the group
-  // points at row 4*sub + s/4, column 16*nb + 4*(s%4).
+  // whose value the proxy term counts in the cluster's sum) go in as a bf16
+  // high part and a bf16 remainder: lane (m = r16, group sub) holds, for head
+  // m and keys 4*sub + j, the high parts as A elements j and the remainders
+  // as elements 4 + j; the B operand repeats the four value elements, so one
+  // product sums both parts (about 16 significant bits of each weight, exact
+  // bf16 x bf16 products, fp32 accumulation). The values pass through LDS:
+  // ds_read_b64_tr_b16 gives lane n of group sub the rows 4*sub .. 4*sub+3 at
+  // column 16*nb + n when lane s of the group points at row 4*sub + s/4,
+  // column 16*nb + 4*(s%4). Each wave batches its LDS traffic: logits and
+  // clusters of all tiles, then all weights, then all value reads.
   typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-  bf16_t* vt = reinterpret_cast<bf16_t*>(s_pool + w * kWaveLds);
   floatx4_t oacc[8];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) oacc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  auto tile_products = [&](const bf16x8_t a) {
+  const int tr_row = 4 * sub + (r16 >> 2);
+  auto tile_read = [&](const unsigned char* tile, bf16x4_t (&b)[8]) {
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      auto src = (__attribute__((address_space(3))) bf16x4_t*)(vt + (4 * sub + (r16 >> 2)) * kVRow +
-                                                               16 * nb + 4 * (r16 & 3));
-      const bf16x4_t b4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(src);
-      const bf16x8_t b = {b4[0], b4[1], b4[2], b4[3], b4[0], b4[1], b4[2], b4[3]};
+      auto src = (__attribute__((address_space(3))) bf16x4_t*)(tile + tr_row * 256 +
+                                                               16 * vt_chunk(tr_row, 2 * nb + ((r16 & 3) >> 1)) +
+                                                               8 * (r16 & 1));
+      b[nb] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(src);
+    }
+  };
+  auto tile_products = [&](const bf16x8_t a, const bf16x4_t (&b4)[8]) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const bf16x8_t b = {b4[nb][0], b4[nb][1], b4[nb][2], b4[nb][3], b4[nb][0], b4[nb][1], b4[nb][2], b4[nb][3]};
       oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, oacc[nb], 0, 0, 0);
     }
   };
@@ -712,40 +757,54 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     a[4 + j] = (__bf16)(v - (float)hi);
   };
   const bool head_lane = r16 < G;
+  float4 x4[NT];
+  int4 k4[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    // tile rows 4*kq + sub are value slot 4*t + kq of the row layout
+    x4[t] = *reinterpret_cast<const float4*>(&s_x[w][hr][16 * t + 4 * sub]);
+    if constexpr (PROXY) k4[t] = *reinterpret_cast<const int4*>(&s_kc[w][16 * t + 4 * sub]);
+  }
+  float mus[NT][4];
 #pragma unroll
-    for (int kq = 0; kq < 4; ++kq)
-      *reinterpret_cast<uint4*>(vt + (4 * kq + sub) * kVRow + 8 * r16) = vc[4 * t + kq].raw;
-    const float4 x4 = *reinterpret_cast<const float4*>(&s_x[w][hr][16 * t + 4 * sub]);
-    const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
-    int kcs[4] = {-1, -1, -1, -1};
-    float mus[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
-    if constexpr (PROXY) {
-      const int4 k4 = *reinterpret_cast<const int4*>(&s_kc[w][16 * t + 4 * sub]);
-      kcs[0] = k4.x; kcs[1] = k4.y; kcs[2] = k4.z; kcs[3] = k4.w;
+  for (int t = 0; t < NT; ++t) {
+    const int kc[4] = {PROXY ? k4[t].x : -1, PROXY ? k4[t].y : -1, PROXY ? k4[t].z : -1, PROXY ? k4[t].w : -1};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) mus[j] = s_mu[kcs[j] >= 0 ? kcs[j] : 0][hr];
+    for (int j = 0; j < 4; ++j) mus[t][j] = (PROXY && kc[j] >= 0) ? s_mu[kc[j]][hr] : kNegInf;
+  }
+  float cws[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (PROXY) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int b = 4 * w + j + (sub >= 2 ? 4 * W : 0);
+      const float mu = s_mu[b][hr];
+      cws[j] = (head_lane && b < p.C && mu != kNegInf) ? fast_exp2(mu - Mh) : 0.f;
     }
-    bf16x8_t a;
+  }
+  bf16x8_t aw[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const float xs[4] = {x4[t].x, x4[t].y, x4[t].z, x4[t].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const float ev = head_lane ? fast_exp2(xs[j] - Mh) : 0.f;
       lsum += ev;
-      float wv = ev;
-      if constexpr (PROXY) {
-        if (head_lane && kcs[j] >= 0) wv -= fast_exp2(mus[j] - Mh);
-      }
-      split(a, j, wv);
+      const float wv = (head_lane && mus[t][j] != kNegInf) ? ev - fast_exp2(mus[t][j] - Mh) : ev;
+      split(aw[t], j, wv);
     }
-    tile_products(a);
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // the value tiles have landed
+  bf16x4_t bv[NT][8];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) tile_read(&s_vt[w][t][0], bv[t]);
+  bf16x4_t bc[8];
+  bf16x8_t acl;
   if constexpr (PROXY) {
     // Proxy value terms exp2(mu_b - M) * (sum of cluster b's values), as one
-    // more tile: rows sub and 4 + sub hold the bf16 high part and remainder
-    // of cluster b0's value sum, rows 8 + sub and 12 + sub those of cluster
-    // b1 (zero when absent); each row's weight is split as above.
+    // more tile in the consumed tile 0: rows sub and 4 + sub hold the bf16
+    // high part and remainder of cluster b0's value sum, rows 8 + sub and
+    // 12 + sub those of cluster b1 (zero when absent); each row's weight is
+    // split as above. (The writes follow this wave's reads of tile 0.)
+    unsigned char* ct = &s_vt[w][0][0];
     auto put = [&](int row, const float (&f)[8], bool lo) {
       bf16x8_t v;
 #pragma unroll
@@ -753,28 +812,23 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
         const __bf16 hi = (__bf16)f[i];
         v[i] = lo ? (__bf16)(f[i] - (float)hi) : hi;
       }
-      *reinterpret_cast<bf16x8_t*>(vt + row * kVRow + 8 * r16) = v;
+      *reinterpret_cast<bf16x8_t*>(ct + row * 256 + 16 * vt_chunk(row, r16)) = v;
     };
     put(sub, svf, false);
     put(4 + sub, svf, true);
     put(8 + sub, sv1, false);
     put(12 + sub, sv1, true);
-    float cws[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int b = 4 * w + j + (sub >= 2 ? 4 * W : 0);
-      cws[j] = s_mu[b][hr];
-      cws[j] = (head_lane && b < p.C && cws[j] != kNegInf) ? fast_exp2(cws[j] - Mh) : 0.f;
-    }
-    bf16x8_t a;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) split(a, j, cws[j]);
-    tile_products(a);
+    for (int j = 0; j < 4; ++j) split(acl, j, cws[j]);
+    tile_read(ct, bc);
   }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) tile_products(aw[t], bv[t]);
+  if constexpr (PROXY) tile_products(acl, bc);
 
   // ---- per-wave partials, then the unit's combine ---------------------------
   // accumulator element i of lane (n, group sub): head 4*sub + i, dim 16*nb + n
-  float* red = reinterpret_cast<float*>(s_pool + w * kWaveLds);
+  float* red = reinterpret_cast<float*>(&s_vt[w][0][0]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * sub + i;
@@ -792,7 +846,7 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     float a = 0.f, L = 0.f;
 #pragma unroll
     for (int ww = 0; ww < W; ++ww) {
-      a += reinterpret_cast<const float*>(s_pool + ww * kWaveLds)[ei];
+      a += reinterpret_cast<const float*>(&s_vt[ww][0][0])[ei];
       L += s_l[ww][h];
     }
     const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
@@ -1601,7 +1655,12 @@ static hipError_t launch_mfma_nt(const AttnParams& p, int nt, hipStream_t st) {
     case 1: hipLaunchKernelGGL((sparse_unit_mfma_kernel<G, PROXY, 1>), grid, block, 0, st, p); break;
     case 2: hipLaunchKernelGGL((sparse_unit_mfma_kernel<G, PROXY, 2>), grid, block, 0, st, p); break;
     case 3: hipLaunchKernelGGL((sparse_unit_mfma_kernel<G, PROXY, 3>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((sparse_unit_mfma_kernel<G, PROXY, 4>), grid, block, 0, st, p); break;
+    case 4:
+      if constexpr (G < 8) {  // LDS: the value tiles of 8 waves x 4 tiles leave no room for G = 8
+        hipLaunchKernelGGL((sparse_unit_mfma_kernel<G, PROXY, 4>), grid, block, 0, st, p);
+        break;
+      }
+      return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

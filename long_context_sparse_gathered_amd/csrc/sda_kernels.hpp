@@ -123,6 +123,8 @@ hipError_t launch_proxy_build(const ProxyBuildParams& p, int dtype, int units, h
 
 // Largest slot count the one-workgroup-per-unit kernel is built for.
 constexpr int kUnitWaves = 8;
+// Tiles of 16 list entries per wave in the bf16 unit kernel (LDS-bound).
+inline int unit_max_tiles(int G) { return G >= 8 ? 3 : 4; }
 constexpr int kUnitMaxSlots = 16;
 inline int unit_slots_for(int m) {
   const int need = (m + 4 * kUnitWaves - 1) / (4 * kUnitWaves);
