@@ -130,7 +130,7 @@ def main():
         copy_calibration(dev)
         return
 
-    w = synth.WORKLOADS["c3"]
+    w = synth.WORKLOADS["proxy_bf16_b32_n32k"]
     t0 = time.time()
     c = synth.make_case(w)
     print(f"# generated {w.name} in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
@@ -194,7 +194,7 @@ def main():
     traffic = None
     if os.path.exists(COUNTERS):
         cnt = json.load(open(COUNTERS))
-        rec = cnt.get("sparse_proxy_c3")
+        rec = cnt.get("sparse_proxy_b32_n32k")
         if rec and rec.get("kernel_source_sha") == kernel_source_sha():
             traffic = rec["hbm_bytes_per_launch"]
 
@@ -285,7 +285,7 @@ def measure_rows(a, dev):
     out = {}
 
     # sampled tail
-    w = synth.WORKLOADS["c4"]
+    w = synth.WORKLOADS["sampled_bf16_b8_n64k"]
     c = synth.make_case(w)
     q, K, V, idx = to_dev(c.q, dev), to_dev(c.K, dev), to_dev(c.V, dev), to_dev(c.idx, dev)
     ncopy = 6
@@ -309,7 +309,7 @@ def measure_rows(a, dev):
     torch.cuda.empty_cache()
 
     # rank-1 prior
-    w = synth.WORKLOADS["c5"]
+    w = synth.WORKLOADS["prior_bf16_b16_n128k"]
     c = synth.make_case(w)
     q, K, V, idx, muQ = (to_dev(x, dev) for x in (c.q, c.K, c.V, c.idx, c.mu_Q))
     ws_p = torch.empty(sda.workspace_bytes(sda.make_dims(K, w.Hq), sda.OP_BUILD_PRIOR), dtype=torch.uint8, device=dev)

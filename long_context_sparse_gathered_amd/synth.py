@@ -93,17 +93,17 @@ def _pct(n: int, frac: float) -> int:
 
 WORKLOADS = {
     # single head, fp32, 4K: 4 sink + 64 local + top-128, 16 equal clusters
-    "c1": Workload("c1", 1, 1, 1, 4096, 128, "f32", 4, 64, 128, "proxy", seed=1, C=16, seg="equal"),
+    "proxy_f32_b1_n4k": Workload("proxy_f32_b1_n4k", 1, 1, 1, 4096, 128, "f32", 4, 64, 128, "proxy", seed=1, C=16, seg="equal"),
     # 8B decode shape, batch 1, 32K, 1% read (328), 32 random contiguous clusters
-    "c2": Workload("c2", 1, 32, 8, 32768, 128, "bf16", 4, 64, _pct(32768, 0.01) - 68, "proxy",
+    "proxy_bf16_b1_n32k": Workload("proxy_bf16_b1_n32k", 1, 32, 8, 32768, 128, "bf16", 4, 64, _pct(32768, 0.01) - 68, "proxy",
                    seed=2, C=32, seg="random"),
     # the same at batch 32
-    "c3": Workload("c3", 32, 32, 8, 32768, 128, "bf16", 4, 64, _pct(32768, 0.01) - 68, "proxy",
+    "proxy_bf16_b32_n32k": Workload("proxy_bf16_b32_n32k", 32, 32, 8, 32768, 128, "bf16", 4, 64, _pct(32768, 0.01) - 68, "proxy",
                    seed=3, C=32, seg="random"),
     # sampled tail: batch 8, 64K, I_f = 4 + 128 + 1% top-k
-    "c4": Workload("c4", 8, 32, 8, 65536, 128, "bf16", 4, 128, _pct(65536, 0.01), "sampled", seed=4),
+    "sampled_bf16_b8_n64k": Workload("sampled_bf16_b8_n64k", 8, 32, 8, 65536, 128, "bf16", 4, 128, _pct(65536, 0.01), "sampled", seed=4),
     # rank-1 prior: batch 16, 128K, 3% read
-    "c5": Workload("c5", 16, 32, 8, 131072, 128, "bf16", 4, 64, _pct(131072, 0.03) - 68, "prior", seed=5),
+    "prior_bf16_b16_n128k": Workload("prior_bf16_b16_n128k", 16, 32, 8, 131072, 128, "bf16", 4, 64, _pct(131072, 0.03) - 68, "prior", seed=5),
 }
 
 

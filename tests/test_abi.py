@@ -138,11 +138,11 @@ def test_builder_and_dense_validation(L):
 
 
 def test_workspace_sizes(L):
-    c3 = _dims(B=32, Hq=32, Hkv=8, n=32768)
-    assert L.sda_workspace_bytes(ctypes.byref(c3), sda.OP_SPARSE, sda.TAIL_PROXY, 328, 32) == 0
-    dense = L.sda_workspace_bytes(ctypes.byref(c3), sda.OP_DENSE, 0, 0, 0)
+    b32 = _dims(B=32, Hq=32, Hkv=8, n=32768)
+    assert L.sda_workspace_bytes(ctypes.byref(b32), sda.OP_SPARSE, sda.TAIL_PROXY, 328, 32) == 0
+    dense = L.sda_workspace_bytes(ctypes.byref(b32), sda.OP_DENSE, 0, 0, 0)
     assert dense > 0 and dense % (4 * 264 * 4) == 0
-    assert L.sda_workspace_bytes(ctypes.byref(c3), sda.OP_BUILD_PRIOR, 0, 0, 0) > dense
-    assert L.sda_workspace_bytes(ctypes.byref(c3), sda.OP_BUILD_PROXIES, 0, 0, 32) > 0
-    assert L.sda_workspace_bytes(ctypes.byref(c3), sda.OP_BUILD_PROXIES, 0, 0, 99) == 0
+    assert L.sda_workspace_bytes(ctypes.byref(b32), sda.OP_BUILD_PRIOR, 0, 0, 0) > dense
+    assert L.sda_workspace_bytes(ctypes.byref(b32), sda.OP_BUILD_PROXIES, 0, 0, 32) > 0
+    assert L.sda_workspace_bytes(ctypes.byref(b32), sda.OP_BUILD_PROXIES, 0, 0, 99) == 0
     assert L.sda_workspace_bytes(None, sda.OP_DENSE, 0, 0, 0) == 0

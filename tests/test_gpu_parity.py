@@ -31,8 +31,8 @@ def _proxy_case(orc, w, by_index=True):
     return c, d, st, out, lse, ref, ref_lse
 
 
-def test_c1_fp32_proxy(orc):
-    w = synth.WORKLOADS["c1"]
+def test_proxy_f32_single_head(orc):
+    w = synth.WORKLOADS["proxy_f32_b1_n4k"]
     c, d, st, out, lse, ref, ref_lse = _proxy_case(orc, w)
     assert rel_err(out, ref) <= TOL["f32"]
     assert lse_err(lse, ref_lse) <= LSE_TOL["f32"]
@@ -42,8 +42,8 @@ def test_c1_fp32_proxy(orc):
 
 
 @pytest.mark.parametrize("by_index", [True, False])
-def test_c2_bf16_proxy(orc, by_index):
-    w = synth.WORKLOADS["c2"]
+def test_proxy_bf16_b1_n32k(orc, by_index):
+    w = synth.WORKLOADS["proxy_bf16_b1_n32k"]
     c, d, st, out, lse, ref, ref_lse = _proxy_case(orc, w, by_index)
     assert rel_err(out, ref) <= TOL["bf16"]
     assert lse_err(lse, ref_lse) <= LSE_TOL["bf16"]
@@ -61,7 +61,7 @@ def test_c2_bf16_proxy(orc, by_index):
 def test_proxy_general_clusters_and_ragged(orc):
     """Non-contiguous cluster ids (with -1), ragged list lengths including an
     empty unit, log-weights, and C not a multiple of the kernel's slot size."""
-    w = synth.WORKLOADS["c2"].replace(B=2, n=3000, n_top=150, C=37)
+    w = synth.WORKLOADS["proxy_bf16_b1_n32k"].replace(B=2, n=3000, n_top=150, C=37)
     c = synth.make_case(w)
     rng = np.random.default_rng(5)
     cid = rng.integers(-1, w.C, size=c.cid.shape).astype(np.int32)
@@ -83,7 +83,7 @@ def test_proxy_general_clusters_and_ragged(orc):
 def test_none_tail_with_duplicates(orc, B):
     """Plain sparse attention: random lists with duplicates and log-weights.
     B = 1 takes the split-K kernel, B = 32 the one-workgroup-per-unit kernel."""
-    w = synth.WORKLOADS["c2"].replace(B=B, n=2048, n_top=100, C=0)
+    w = synth.WORKLOADS["proxy_bf16_b1_n32k"].replace(B=B, n=2048, n_top=100, C=0)
     c = synth.make_case(w)
     rng = np.random.default_rng(9)
     m = 300
@@ -129,7 +129,7 @@ def test_dense(orc, dtype, G):
 
 
 def test_prior_build_and_decode(orc):
-    w = synth.WORKLOADS["c5"].replace(B=2, n=8192, n_top=300)
+    w = synth.WORKLOADS["prior_bf16_b16_n128k"].replace(B=2, n=8192, n_top=300)
     c = synth.make_case(w)
     d = case_to_dev(c)
     ps = sda.build_prior(d["K"], d["V"], d["mu_Q"])
@@ -153,7 +153,7 @@ def test_prior_build_and_decode(orc):
 
 
 def test_device_flags(orc):
-    w = synth.WORKLOADS["c2"].replace(B=1, n=2048, n_top=60, C=8)
+    w = synth.WORKLOADS["proxy_bf16_b1_n32k"].replace(B=1, n=2048, n_top=60, C=8)
     c = synth.make_case(w)
     idx = c.idx.copy()
     idx[0, 1, 5] = w.n + 3          # out of range -> skipped, flagged
@@ -177,7 +177,7 @@ def test_device_flags(orc):
 
 def test_interleaved_kv_layout(orc):
     """K and V as views into one [B, Hkv, n, 2, d] buffer (strided rows)."""
-    w = synth.WORKLOADS["c2"].replace(B=2, n=2048, n_top=60, C=8)
+    w = synth.WORKLOADS["proxy_bf16_b1_n32k"].replace(B=2, n=2048, n_top=60, C=8)
     c = synth.make_case(w)
     d = case_to_dev(c)
     kv = torch.stack([d["K"], d["V"]], dim=3).contiguous()     # [B,Hkv,n,2,d]

@@ -52,7 +52,7 @@ def _check(orc, c, w, seed, b_cap, tol, idx=None, idx_len=None, K=None, V=None):
 
 
 def test_sampled_small_bf16(orc):
-    w = synth.WORKLOADS["c4"].replace(B=2, n=8192, n_top=82)
+    w = synth.WORKLOADS["sampled_bf16_b8_n64k"].replace(B=2, n=8192, n_top=82)
     c = synth.make_case(w)
     tail, flags, ref = _check(orc, c, w, w.sampler_seed, b_cap=8192, tol=2e-3)
     assert (flags.cpu().numpy() == 0).all()
@@ -61,20 +61,20 @@ def test_sampled_small_bf16(orc):
 
 @pytest.mark.parametrize("seed", [0, 7, 123456789])
 def test_sampled_seeds_and_ragged(orc, seed):
-    w = synth.WORKLOADS["c4"].replace(B=1, n=4096, n_top=40)
+    w = synth.WORKLOADS["sampled_bf16_b8_n64k"].replace(B=1, n=4096, n_top=40)
     c = synth.make_case(w)
     lens = np.array([[w.m, w.m // 2, 0, 1, w.m, 5, w.m - 1, 2]], np.int32)
     _check(orc, c, w, seed, b_cap=64, tol=2e-3, idx_len=lens)
 
 
 def test_sampled_fp32_single_head(orc):
-    w = synth.WORKLOADS["c4"].replace(B=2, Hq=2, Hkv=2, n=3000, n_top=30, dtype="f32")
+    w = synth.WORKLOADS["sampled_bf16_b8_n64k"].replace(B=2, Hq=2, Hkv=2, n=3000, n_top=30, dtype="f32")
     c = synth.make_case(w)
     _check(orc, c, w, 99, b_cap=4096, tol=1e-5)
 
 
 def test_sampled_no_tail_and_constant_tail(orc):
-    w = synth.WORKLOADS["c4"].replace(B=1, Hq=8, Hkv=2, n=300, n_top=20)
+    w = synth.WORKLOADS["sampled_bf16_b8_n64k"].replace(B=1, Hq=8, Hkv=2, n=300, n_top=20)
     c = synth.make_case(w)
     full = np.broadcast_to(np.arange(w.n, dtype=np.int32), (1, w.Hkv, w.n)).copy()
     tail, _, ref = _check(orc, c, w, 3, b_cap=4, tol=2e-3, idx=full)
@@ -91,10 +91,10 @@ def test_sampled_no_tail_and_constant_tail(orc):
     assert (tail.b.cpu().numpy() == 1).all()
 
 
-def test_sampled_full_size_c4(orc):
+def test_sampled_full_size_b8_n64k(orc):
     """The full sampling workload (batch 8, 64K context, 788 listed rows per
     KV head): every unit's budget, draws and output against the oracle."""
-    w = synth.WORKLOADS["c4"]
+    w = synth.WORKLOADS["sampled_bf16_b8_n64k"]
     c = synth.make_case(w)
     d = case_to_dev(c)
     tail = sda.SampledTail(eps=w.eps, delta=w.delta, b0=w.b0, seed=w.sampler_seed, b_cap=4096)

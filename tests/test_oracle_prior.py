@@ -142,7 +142,7 @@ def test_delta_form_equals_definition_on_every_subset(orc, lam):
 
 
 def test_delta_form_equals_definition_on_workload_unit(orc):
-    w = synth.WORKLOADS["c5"].replace(n=8192, n_top=3933 - 68 - 2000)
+    w = synth.WORKLOADS["prior_bf16_b16_n128k"].replace(n=8192, n_top=3933 - 68 - 2000)
     c = synth.unit_case(w, 0, 3)
     built = orc.prior_build(c.K, c.V, c.mu_Q)
     o1, l1 = orc.sparse_prior(c.q, c.K, c.V, c.idx, c.mu_Q, 1.0, *built)

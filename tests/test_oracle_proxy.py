@@ -108,7 +108,7 @@ def test_build_matches_numpy_segment_sums(orc):
             np.testing.assert_allclose(sV[s, g], rV, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("name", ["c1", "c2"])
+@pytest.mark.parametrize("name", ["proxy_f32_b1_n4k", "proxy_bf16_b1_n32k"])
 def test_method_form_equals_definition_on_workload_units(orc, name):
     """The O(|I|) subtraction form equals the O(n) definition (same math,
     different order) on generated units, including general cluster ids."""
@@ -142,7 +142,7 @@ def test_method_form_rejects_duplicates(orc):
 def test_proxy_moves_output_towards_dense(orc):
     """On the generated 4K workload the proxies recover most of the error that
     dropping the tail makes (the pages' motivation; a sanity check, not a bound)."""
-    c = synth.make_case(synth.WORKLOADS["c1"])
+    c = synth.make_case(synth.WORKLOADS["proxy_f32_b1_n4k"])
     o_d, _ = orc.dense(c.q, c.K, c.V)
     o_s, _ = orc.sparse(c.q, c.K, c.V, c.idx)
     o_p, _ = orc.sparse_proxy_def(c.q, c.K, c.V, c.idx, c.cid, c.w.C)

@@ -66,7 +66,7 @@ def test_budget_closed_forms(orc):
 
 
 def _small_workload(**kw):
-    base = synth.WORKLOADS["c4"].replace(B=1, Hkv=2, Hq=8, n=4096, n_sink=4, n_local=64, n_top=60)
+    base = synth.WORKLOADS["sampled_bf16_b8_n64k"].replace(B=1, Hkv=2, Hq=8, n=4096, n_sink=4, n_local=64, n_top=60)
     return base.replace(**kw)
 
 

@@ -16,15 +16,15 @@ def test_bf16_rounding_matches_torch():
 
 
 def test_index_counts_match_the_workloads():
-    assert synth.WORKLOADS["c1"].m == 196
-    assert synth.WORKLOADS["c2"].m == 328 and synth.WORKLOADS["c3"].m == 328
-    assert synth.WORKLOADS["c4"].m == 788
-    assert synth.WORKLOADS["c5"].m == 3933
-    assert abs(synth.WORKLOADS["c4"].z - 1.959963984540054) < 1e-12
+    assert synth.WORKLOADS["proxy_f32_b1_n4k"].m == 196
+    assert synth.WORKLOADS["proxy_bf16_b1_n32k"].m == 328 and synth.WORKLOADS["proxy_bf16_b32_n32k"].m == 328
+    assert synth.WORKLOADS["sampled_bf16_b8_n64k"].m == 788
+    assert synth.WORKLOADS["prior_bf16_b16_n128k"].m == 3933
+    assert abs(synth.WORKLOADS["sampled_bf16_b8_n64k"].z - 1.959963984540054) < 1e-12
 
 
-def test_unit_structure_c1():
-    w = synth.WORKLOADS["c1"]
+def test_unit_structure_f32_single_head():
+    w = synth.WORKLOADS["proxy_f32_b1_n4k"]
     u = synth.make_unit(w, 0, 0)
     idx = u.idx
     assert idx.dtype == np.int32 and idx.shape == (w.m,)
@@ -39,7 +39,7 @@ def test_unit_structure_c1():
 
 
 def test_random_segmentation_and_determinism():
-    w = synth.WORKLOADS["c2"]
+    w = synth.WORKLOADS["proxy_bf16_b1_n32k"]
     a = synth.make_unit(w, 0, 3)
     b = synth.make_unit(w, 0, 3)
     np.testing.assert_array_equal(a.K, b.K)
@@ -52,7 +52,7 @@ def test_random_segmentation_and_determinism():
 
 
 def test_case_assembly_matches_units():
-    w = synth.WORKLOADS["c2"].replace(n=2048, n_top=60)
+    w = synth.WORKLOADS["proxy_bf16_b1_n32k"].replace(n=2048, n_top=60)
     case = synth.make_case(w, threads=4)
     u = synth.make_unit(w, 0, 6)
     np.testing.assert_array_equal(case.K[0, 6], u.K)
@@ -63,7 +63,7 @@ def test_case_assembly_matches_units():
 
 
 def test_prior_workload_mean_query():
-    w = synth.WORKLOADS["c5"].replace(n=4096, n_top=100)
+    w = synth.WORKLOADS["prior_bf16_b16_n128k"].replace(n=4096, n_top=100)
     u = synth.make_unit(w, 1, 2)
     assert u.mu_Q.shape == (w.G, w.d) and u.mu_Q.dtype == np.float32
     # the prefill mean sits near a norm-3 vector
