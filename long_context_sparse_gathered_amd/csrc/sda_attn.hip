@@ -820,6 +820,7 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     put(12 + sub, sv1, true);
 #pragma unroll
     for (int j = 0; j < 4; ++j) split(acl, j, cws[j]);
+    wave_lds_sync();  // the tile's rows, written by other lanes
     tile_read(ct, bc);
   }
 #pragma unroll
@@ -1427,6 +1428,7 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
       const float v = max16(bmx[i]);
       if (r16 == 0 && 4 * sub + i < G) s_bm[w][4 * sub + i] = v;
     }
+    wave_lds_sync();  // logits and batch maxima, written by other lanes of the wave
     // ---- online rescale (same values in both layouts) --------------------------
     {
       const float mn = fmaxf(m_a, s_bm[w][hr]);
@@ -1451,6 +1453,7 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
 #pragma unroll
       for (int kq = 0; kq < 4; ++kq)
         *reinterpret_cast<uint4*>(vt + (4 * kq + sub) * kVRow + 8 * r16) = vc[4 * t + kq].raw;
+      wave_lds_sync();  // the tile's rows, staged by other lanes
       const float4 x4 = *reinterpret_cast<const float4*>(&s_x[w][r16 < RP ? r16 : 0][16 * t + 4 * sub]);
       float4 y4 = make_float4(0.f, 0.f, 0.f, 0.f);
       if constexpr (PRIOR) y4 = *reinterpret_cast<const float4*>(&s_x[w][r16 >= G && r16 < 2 * G ? r16 + G : 0][16 * t + 4 * sub]);

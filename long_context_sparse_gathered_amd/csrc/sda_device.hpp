@@ -83,6 +83,12 @@ __device__ __forceinline__ void load_q8(const void* q, int64_t off, float (&f)[8
 
 // ---- cross-lane --------------------------------------------------------------
 
+// Hand-off of LDS data between lanes of one wave: the wave's LDS operations
+// execute in order, and this wavefront-scope fence keeps the compiler from
+// moving LDS accesses across the hand-off or forwarding a lane's own store to
+// a load that another lane's store is meant to satisfy.
+__device__ __forceinline__ void wave_lds_sync() { __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront"); }
+
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));

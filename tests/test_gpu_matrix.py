@@ -1,0 +1,160 @@
+"""GPU parity across the kernel shapes: every query-group size G with each
+tail, the tile counts of the one-workgroup-per-unit kernel, the split-K
+matrix-core kernel with and without the rank-1 prior, the sampled kernels,
+and the full-size workloads in the launch configuration bench.py times
+(checked on sampled units against the oracle).
+
+Tolerances as in test_gpu_parity: max over rows of max|o - o*| / max|o*|
+<= 2e-3 for bf16 inputs; budgets and drawn positions bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+from long_context_sparse_gathered_amd import sda, synth
+from tests.gpu_util import case_to_dev, dev, lse_err, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+LSE_TOL = 1e-3
+
+
+def _sync():
+    torch.cuda.synchronize()
+
+
+def _grouped(w, G, Hkv):
+    return w.replace(Hq=G * Hkv, Hkv=Hkv)
+
+
+# list length -> tiles of 16 entries per wave in the unit kernel (8 waves)
+@pytest.mark.parametrize("G,n_top", [(1, 40), (2, 200), (4, 430), (8, 100), (8, 310)])
+def test_proxy_unit_kernel_group_sizes(orc, G, n_top):
+    """Proxy decode through the one-workgroup-per-unit kernel: G = 1..8 and
+    1..4 tiles per wave (m = 108 .. 498; at most 3 tiles for G = 8)."""
+    w = _grouped(synth.WORKLOADS["proxy_bf16_b1_n32k"], G, 2).replace(B=2, n=4096, n_top=n_top, C=37)
+    c = synth.make_case(w)
+    d = case_to_dev(c)
+    st = sda.build_tail_proxies(d["K"], d["V"], d["cid"], w.C)
+    out, lse = sda.sparse_decode_attn(d["q"], d["K"], d["V"], d["idx"], tail=st, idx_cluster=d["idx_cluster"])
+    _sync()
+    ref, ref_lse = orc.sparse_proxy_def(c.q, c.K, c.V, c.idx, c.cid, w.C)
+    assert rel_err(out, ref) <= TOL
+    assert lse_err(lse, ref_lse) <= LSE_TOL
+
+
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_none_unit_kernel_group_sizes(orc, G):
+    """No tail with 128 units (one workgroup per unit): random lists with
+    duplicates and log-weights."""
+    w = _grouped(synth.WORKLOADS["proxy_bf16_b1_n32k"], G, 2).replace(B=64, n=1024, n_top=40, C=0)
+    c = synth.make_case(w)
+    rng = np.random.default_rng(G)
+    idx = rng.integers(0, w.n, size=(w.B, w.Hkv, 200)).astype(np.int32)
+    logw = rng.normal(0, 1, size=idx.shape).astype(np.float32)
+    d = case_to_dev(c)
+    out, lse = sda.sparse_decode_attn(d["q"], d["K"], d["V"], to_dev(idx), logw=to_dev(logw))
+    _sync()
+    ref, ref_lse = orc.sparse(c.q, c.K, c.V, idx, logw=logw)
+    assert rel_err(out, ref) <= TOL
+    assert lse_err(lse, ref_lse) <= LSE_TOL
+
+
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_none_stream_kernel_group_sizes(orc, G):
+    """No tail with few units and a long list: split-K on the matrix cores
+    (several batches per workgroup, several workgroups per unit)."""
+    w = _grouped(synth.WORKLOADS["proxy_bf16_b1_n32k"], G, 2).replace(B=1, n=6000, n_top=40, C=0)
+    c = synth.make_case(w)
+    rng = np.random.default_rng(10 + G)
+    idx = np.sort(rng.integers(0, w.n, size=(w.B, w.Hkv, 2500)), axis=-1).astype(np.int32)
+    d = case_to_dev(c)
+    out, lse = sda.sparse_decode_attn(d["q"], d["K"], d["V"], to_dev(idx))
+    _sync()
+    ref, ref_lse = orc.sparse(c.q, c.K, c.V, idx)
+    assert rel_err(out, ref) <= TOL
+    assert lse_err(lse, ref_lse) <= LSE_TOL
+
+
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_prior_group_sizes(orc, G):
+    """Rank-1 prior: G = 1, 2 on the matrix-core stream (mean query split in
+    high part and remainder rows), G = 8 on the vector stream."""
+    w = _grouped(synth.WORKLOADS["prior_bf16_b16_n128k"], G, 2).replace(B=2, n=8192, n_top=1200)
+    c = synth.make_case(w)
+    d = case_to_dev(c)
+    ps = sda.build_prior(d["K"], d["V"], d["mu_Q"])
+    _sync()
+    muK, Oest, maxP, sumP = orc.prior_build(c.K, c.V, c.mu_Q)
+    for lam in (1.0, 0.5):
+        out, lse = sda.sparse_decode_attn(d["q"], d["K"], d["V"], d["idx"], tail=ps, lam=lam)
+        _sync()
+        ref, ref_lse = orc.sparse_prior(c.q, c.K, c.V, c.idx, c.mu_Q, lam, muK, Oest, maxP, sumP)
+        assert rel_err(out, ref) <= TOL, lam
+        assert lse_err(lse, ref_lse) <= LSE_TOL, lam
+
+
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_sampled_group_sizes(orc, G):
+    """Sampled tail for G = 1, 2, 8: budgets and draws bit-exact."""
+    w = _grouped(synth.WORKLOADS["sampled_bf16_b8_n64k"], G, 2).replace(B=2, n=4096, n_top=40)
+    c = synth.make_case(w)
+    d = case_to_dev(c)
+    tail = sda.SampledTail(eps=w.eps, delta=w.delta, b0=w.b0, seed=w.sampler_seed, b_cap=4096)
+    out, lse = sda.sparse_decode_attn(d["q"], d["K"], d["V"], d["idx"], tail=tail)
+    _sync()
+    ref = orc.sampled(c.q, c.K, c.V, c.idx, w.eps, w.z, w.b0, w.sampler_seed, 4096)
+    r = np.round(ref["bstar"])
+    assert not ((np.abs(ref["bstar"] - r) < 1e-9 * np.maximum(ref["bstar"], 1.0)) & (r >= 1)).any()
+    np.testing.assert_array_equal(tail.b.cpu().numpy(), ref["b"])
+    got = tail.samples.cpu().numpy()
+    for s in range(w.B):
+        for g in range(w.Hkv):
+            k = min(int(ref["b"][s, g]), 4096)
+            np.testing.assert_array_equal(got[s, g, :k], ref["samples"][s, g, :k])
+    assert rel_err(out, ref["out"]) <= TOL
+    assert lse_err(lse, ref["lse"]) <= LSE_TOL
+
+
+def _sample_units(w, k, seed):
+    rng = np.random.default_rng(seed)
+    return [divmod(int(u), w.Hkv) for u in rng.choice(w.B * w.Hkv, size=k, replace=False)]
+
+
+def test_proxy_full_size_b32_n32k(orc):
+    """The timed decode step (batch 32, 32K, 1% read, 32 proxies per KV head)
+    checked on 8 sampled units against the oracle's definition."""
+    w = synth.WORKLOADS["proxy_bf16_b32_n32k"]
+    c = synth.make_case(w)
+    d = case_to_dev(c)
+    st = sda.build_tail_proxies(d["K"], d["V"], d["cid"], w.C)
+    out, lse = sda.sparse_decode_attn(d["q"], d["K"], d["V"], d["idx"], tail=st, idx_cluster=d["idx_cluster"])
+    _sync()
+    got, got_lse = out.cpu().double().numpy(), lse.cpu().double().numpy()
+    for s, g in _sample_units(w, 8, 1):
+        uc = synth.unit_case(w, s, g)
+        ref, ref_lse = orc.sparse_proxy_def(uc.q, uc.K, uc.V, uc.idx, uc.cid, w.C)
+        rows = slice(g * w.G, (g + 1) * w.G)
+        assert rel_err(got[s, rows], ref[0]) <= TOL, (s, g)
+        assert np.abs(got_lse[s, rows] - ref_lse[0]).max() <= LSE_TOL, (s, g)
+
+
+def test_prior_full_size_b16_n128k(orc):
+    """The prior decode step (batch 16, 128K, 3% read) checked on 4 sampled
+    units against the oracle (its own prior build per unit)."""
+    w = synth.WORKLOADS["prior_bf16_b16_n128k"]
+    c = synth.make_case(w)
+    d = case_to_dev(c)
+    ps = sda.build_prior(d["K"], d["V"], d["mu_Q"])
+    out, lse = sda.sparse_decode_attn(d["q"], d["K"], d["V"], d["idx"], tail=ps)
+    _sync()
+    got, got_lse = out.cpu().double().numpy(), lse.cpu().double().numpy()
+    del d, ps
+    torch.cuda.empty_cache()
+    for s, g in _sample_units(w, 4, 2):
+        uc = synth.unit_case(w, s, g)
+        muK, Oest, maxP, sumP = orc.prior_build(uc.K, uc.V, uc.mu_Q)
+        ref, ref_lse = orc.sparse_prior(uc.q, uc.K, uc.V, uc.idx, uc.mu_Q, 1.0, muK, Oest, maxP, sumP)
+        rows = slice(g * w.G, (g + 1) * w.G)
+        assert rel_err(got[s, rows], ref[0]) <= TOL, (s, g)
+        assert np.abs(got_lse[s, rows] - ref_lse[0]).max() <= LSE_TOL, (s, g)
