@@ -1563,7 +1563,7 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
 // ---------------------------------------------------------------------------
 // Merge of split partials: one workgroup per unit, fixed split order.
 template <int G, int MODE>
-__global__ __launch_bounds__(256) void merge_kernel(const AttnParams p) {
+__global__ __launch_bounds__(512) void merge_kernel(const AttnParams p) {
   constexpr bool PRIOR = (MODE == kModePrior);
   constexpr bool BUILD = (MODE == kModeBuildPrior);
   const int u = blockIdx.x;
@@ -1571,29 +1571,36 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnParams p) {
   const int g = u - s * p.Hkv;
   const int tid = threadIdx.x;
 
-  for (int ei = tid; ei < G * kD; ei += 256) {
+  // one (head, dim) per thread; one pass over the splits with a running
+  // maximum, so that every split's loads are independent of the others
+  for (int ei = tid; ei < G * kD; ei += 512) {
     const int h = ei / kD, dim = ei - h * kD;
+    const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
+    float mP = 0.f, zP = 0.f, oe = 0.f;
+    if constexpr (PRIOR) {
+      mP = p.maxP[qh] * kLog2e;
+      zP = p.sumP[qh];
+      oe = p.O_est[qh * kD + dim];
+    }
     const float* base = p.part + ((int64_t)u * p.splits * G + h) * kPartStride;
     const int64_t stride = (int64_t)G * kPartStride;
-    float M = kNegInf;
-#pragma unroll 8
-    for (int sp = 0; sp < p.splits; ++sp) M = fmaxf(M, base[sp * stride]);
-    float a = 0.f, L = 0.f, SP = 0.f, SPV = 0.f;
-#pragma unroll 8
+    float M = kNegInf, a = 0.f, L = 0.f, SP = 0.f, SPV = 0.f;
+#pragma unroll 4
     for (int sp = 0; sp < p.splits; ++sp) {
       const float* rec = base + sp * stride;
-      const float f = rescale(rec[0], M);
-      a = fmaf(rec[4 + dim], f, a);
-      L = fmaf(rec[1], f, L);
+      const float ms = rec[0], ls = rec[1], as = rec[4 + dim];
+      const float mn = fmaxf(M, ms);
+      const float fo = rescale(M, mn), fs = rescale(ms, mn);
+      a = a * fo + as * fs;
+      L = L * fo + ls * fs;
+      M = mn;
       if constexpr (PRIOR) {
         SP += rec[2];
         SPV += rec[4 + kD + dim];
       }
     }
-    const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
     if constexpr (PRIOR) {
-      const float mP = p.maxP[qh] * kLog2e;
-      const Fin f = finalize_prior(M, L, a, base[3], mP, p.sumP[qh], p.O_est[qh * kD + dim], SP, SPV, p.lambda);
+      const Fin f = finalize_prior(M, L, a, base[3], mP, zP, oe, SP, SPV, p.lambda);
       p.out[qh * kD + dim] = f.out;
       if (dim == 0 && p.lse) p.lse[qh] = f.lse;
     } else if constexpr (BUILD) {
@@ -1611,7 +1618,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const AttnParams p) {
     }
   }
   if constexpr (BUILD) {
-    for (int dim = tid; dim < kD; dim += 256) {
+    for (int dim = tid; dim < kD; dim += 512) {
       float a = 0.f;
       for (int sp = 0; sp < p.splits; ++sp) a += p.ksum[((int64_t)u * p.splits + sp) * kD + dim];
       p.aux2[(int64_t)u * kD + dim] = a / (float)p.n;
@@ -1750,7 +1757,7 @@ hipError_t launch_stream(const AttnParams& p, int dtype, int G, int mode, hipStr
 
 template <int G>
 static hipError_t launch_merge_g(const AttnParams& p, int mode, hipStream_t st) {
-  const dim3 grid(p.B * p.Hkv), block(256);
+  const dim3 grid(p.B * p.Hkv), block(512);
   switch (mode) {
     case kModeSparse:
     case kModeDense: hipLaunchKernelGGL((merge_kernel<G, kModeSparse>), grid, block, 0, st, p); break;
