@@ -49,6 +49,9 @@
  *     Query head h attends with KV head h / (Hq / Hkv).
  *   - The logit of query head h and row j is scale * <q_h, k_j>.
  *   - Supported: d == 128; Hq / Hkv in {1, 2, 4, 8}; dtype bf16 or fp32.
+ *   - Rows are read as 16-byte vectors: q, K, V and the fp32 tail state
+ *     must be 16-byte aligned (else SDA_EINVAL) and the K/V strides in
+ *     bytes multiples of 16 (else SDA_ESHAPE).
  */
 #ifndef SDA_H
 #define SDA_H

@@ -172,10 +172,9 @@ size_t dense_ws(const Resolved& r, bool build) {
   return ws;
 }
 
-constexpr int kProxyRowsPerChunk = 4096;
-
 size_t proxy_ws(const Resolved& r, int C) {
-  const int chunks = ceil_div(r.n, kProxyRowsPerChunk);
+  int chunks, rows;
+  proxy_build_shape(r.B * r.Hkv, r.n, C, &chunks, &rows);
   const size_t units = (size_t)r.B * r.Hkv;
   return units * chunks * C * (2 * kD * sizeof(float) + sizeof(int32_t));
 }
@@ -239,6 +238,7 @@ SDA_EXPORT sda_status sda_build_tail_proxies(const sda_dims* dims, const void* K
   sda_status st = resolve(dims, &r);
   if (st != SDA_OK) return st;
   if (!K || !V || !cluster_id || !count || !sumK || !sumV) return SDA_EINVAL;
+  if (!aligned16(K) || !aligned16(V)) return SDA_EINVAL;
   if (C < 1 || C > kCmax) return SDA_EUNSUPPORTED;
   const size_t need = proxy_ws(r, C);
   if (!ws || ws_bytes < need) return SDA_EWORKSPACE;
@@ -253,9 +253,8 @@ SDA_EXPORT sda_status sda_build_tail_proxies(const sda_dims* dims, const void* K
   p.Hkv = r.Hkv;
   p.n = r.n;
   p.C = C;
-  p.rows_per_chunk = kProxyRowsPerChunk;
-  p.chunks = ceil_div(r.n, kProxyRowsPerChunk);
   const int units = r.B * r.Hkv;
+  proxy_build_shape(units, r.n, C, &p.chunks, &p.rows_per_chunk);
   p.part = reinterpret_cast<float*>(ws);
   p.pcount = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
                                         (size_t)units * p.chunks * C * 2 * kD * sizeof(float));

@@ -37,6 +37,12 @@ struct RowChunk<bf16_t> {
   __device__ __forceinline__ void load_cached(const bf16_t* p) {
     raw = *reinterpret_cast<const uint4*>(p);
   }
+  // read-once data (non-temporal: not kept in the caches)
+  __device__ __forceinline__ void load_stream(const bf16_t* p) {
+    typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+    const v4u v = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    raw = make_uint4(v.x, v.y, v.z, v.w);
+  }
   __device__ __forceinline__ void zero() { raw = make_uint4(0, 0, 0, 0); }
   __device__ __forceinline__ void unpack(float (&f)[8]) const {
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -54,6 +60,13 @@ struct RowChunk<float> {
   __device__ __forceinline__ void load_cached(const float* p) {
     a = reinterpret_cast<const float4*>(p)[0];
     b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void load_stream(const float* p) {
+    typedef float v4f __attribute__((ext_vector_type(4)));
+    const v4f x = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+    const v4f y = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p) + 1);
+    a = make_float4(x.x, x.y, x.z, x.w);
+    b = make_float4(y.x, y.y, y.z, y.w);
   }
   __device__ __forceinline__ void zero() {
     a = make_float4(0.f, 0.f, 0.f, 0.f);

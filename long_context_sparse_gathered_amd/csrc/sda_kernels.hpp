@@ -120,6 +120,22 @@ inline int sampled_exact_splits(int units) {
   return s < 1 ? 1 : (s > 8 ? 8 : s);
 }
 hipError_t launch_proxy_build(const ProxyBuildParams& p, int dtype, int units, hipStream_t st);
+// Row chunks of the proxy builder: 4096 rows each (a workgroup holds C*2*kD
+// fp32 column sums in LDS and writes them out once per chunk), shorter when
+// there are too few (unit, chunk) workgroups to fill the chip, but at least
+// 256 rows; always a multiple of 32 rows.
+inline void proxy_build_shape(int units, int n, int C, int* chunks, int* rows) {
+  (void)C;
+  int ch = (n + 4095) / 4096;
+  const int fill = (1280 + units - 1) / units;
+  const int max_ch = (n + 255) / 256;
+  const int want = fill < max_ch ? fill : max_ch;
+  if (ch < want) ch = want;
+  int r = (n + ch - 1) / ch;
+  r = (r + 31) / 32 * 32;
+  *rows = r;
+  *chunks = (n + r - 1) / r;
+}
 
 // Largest slot count the one-workgroup-per-unit kernel is built for.
 constexpr int kUnitWaves = 8;
