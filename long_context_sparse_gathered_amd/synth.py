@@ -13,7 +13,10 @@ unit can be regenerated alone):
 * key bias beta = 4 * (random unit vector); K = N(0,1) + beta; V = N(0,1).
 * query heads q_h ~ N(0,1) (prior workload: q_h = m_h + N(0,1) with
   m_h = 3 * random unit vector, and mu_Q_h = the fp32 mean of 2048 prefill
-  queries m_h + N(0,1)).
+  queries m_h + N(0,1)).  Selector workloads (r > 0) plant a query geometry:
+  U = the Q factor of a d x r Gaussian matrix (orthonormal columns, fp32) and
+  q_h = sqrt(d/r) * U z_h + 0.25 * N(0,1), z_h ~ N(0,1)^r, so that most of
+  every query lies in span(U), the subspace the selector scores in.
 * 8 heavy hitters at distinct positions in [n_sink, n - n_local): the row is
   replaced by t * sqrt(d) * qbar / <qbar, qbar> with t ~ U(11, 13) and qbar
   the group-mean query, so the scaled logit of qbar against it is t.
@@ -65,6 +68,7 @@ class Workload:
     n_prefill: int = 2048   # prior tail: prefill queries behind mu_Q
     muq_norm: float = 3.0
     lam: float = 1.0
+    r: int = 0              # selector workloads: rank of the query subspace
 
     @property
     def G(self) -> int:
@@ -104,6 +108,10 @@ WORKLOADS = {
     "sampled_bf16_b8_n64k": Workload("sampled_bf16_b8_n64k", 8, 32, 8, 65536, 128, "bf16", 4, 128, _pct(65536, 0.01), "sampled", seed=4),
     # rank-1 prior: batch 16, 128K, 3% read
     "prior_bf16_b16_n128k": Workload("prior_bf16_b16_n128k", 16, 32, 8, 131072, 128, "bf16", 4, 64, _pct(131072, 0.03) - 68, "prior", seed=5),
+    # selector in front of the proxy decode: the batch-32 32K shape, queries
+    # in a rank-32 subspace, 32 random contiguous clusters, 260 rows to pick
+    "qgs_bf16_b32_n32k": Workload("qgs_bf16_b32_n32k", 32, 32, 8, 32768, 128, "bf16", 4, 64, _pct(32768, 0.01) - 68, "proxy",
+                   seed=6, C=32, seg="random", r=32),
 }
 
 
@@ -148,6 +156,7 @@ class UnitData:
     cid: np.ndarray | None   # [n] int32
     mu_Q: np.ndarray | None  # [G, d] float32
     heavy: np.ndarray        # [n_heavy] positions
+    U: np.ndarray | None = None   # [d, r] float32 (selector workloads)
 
 
 def select_index_set(Kf: np.ndarray, qf: np.ndarray, n_sink: int, n_local: int, n_top: int,
@@ -190,6 +199,10 @@ def make_unit(w: Workload, s: int, g: int) -> UnitData:
         _, pre_f = _to_dtype(pre.astype(np.float32), w.dtype)
         mu_Q = pre_f.astype(np.float64).mean(axis=1).astype(np.float32)
         q_raw = (mean + rng.standard_normal((G, d))).astype(np.float32)
+    elif w.r > 0:
+        U = np.linalg.qr(rng.standard_normal((d, w.r)))[0].astype(np.float32)
+        z = rng.standard_normal((G, w.r))
+        q_raw = (np.sqrt(d / w.r) * z @ U.T.astype(np.float64) + 0.25 * rng.standard_normal((G, d))).astype(np.float32)
     else:
         q_raw = rng.standard_normal((G, d), dtype=np.float32)
     q, qf = _to_dtype(q_raw, w.dtype)
@@ -203,7 +216,7 @@ def make_unit(w: Workload, s: int, g: int) -> UnitData:
     V, _ = _to_dtype(Vf, w.dtype)
     idx = select_index_set(Kf, qf, w.n_sink, w.n_local, w.n_top, scale)
     cid = make_clusters(srng, n, w.C, w.seg) if w.C > 0 else None
-    return UnitData(K=K, V=V, q=q, idx=idx, cid=cid, mu_Q=mu_Q, heavy=heavy)
+    return UnitData(K=K, V=V, q=q, idx=idx, cid=cid, mu_Q=mu_Q, heavy=heavy, U=U if w.r > 0 else None)
 
 
 # ---------------------------------------------------------------------------
@@ -218,6 +231,7 @@ class Case:
     idx: np.ndarray          # [B, Hkv, m] int32
     cid: np.ndarray | None   # [B, Hkv, n] int32
     mu_Q: np.ndarray | None  # [B, Hq, d] float32
+    U: np.ndarray | None = None   # [B, Hkv, d, r] float32 (selector workloads)
 
     @property
     def idx_cluster(self) -> np.ndarray:
@@ -234,6 +248,7 @@ def make_case(w: Workload, threads: int | None = None) -> Case:
     idx = np.empty((B, Hkv, m), np.int32)
     cid = np.empty((B, Hkv, n), np.int32) if w.C > 0 else None
     mu_Q = np.empty((B, w.Hq, d), np.float32) if w.tail == "prior" else None
+    U = np.empty((B, Hkv, d, w.r), np.float32) if w.r > 0 else None
 
     def fill(u):
         s, g = divmod(u, Hkv)
@@ -245,6 +260,8 @@ def make_case(w: Workload, threads: int | None = None) -> Case:
             cid[s, g] = ud.cid
         if mu_Q is not None:
             mu_Q[s, g * G:(g + 1) * G] = ud.mu_Q
+        if U is not None:
+            U[s, g] = ud.U
 
     nthreads = threads or min(16, os.cpu_count() or 1)
     if nthreads > 1 and B * Hkv > 1:
@@ -253,7 +270,7 @@ def make_case(w: Workload, threads: int | None = None) -> Case:
     else:
         for u in range(B * Hkv):
             fill(u)
-    return Case(w=w, q=q, K=K, V=V, idx=idx, cid=cid, mu_Q=mu_Q)
+    return Case(w=w, q=q, K=K, V=V, idx=idx, cid=cid, mu_Q=mu_Q, U=U)
 
 
 def unit_case(w: Workload, s: int, g: int) -> Case:
@@ -262,4 +279,5 @@ def unit_case(w: Workload, s: int, g: int) -> Case:
     w1 = w.replace(B=1, Hq=w.G, Hkv=1)
     return Case(w=w1, q=ud.q[None], K=ud.K[None, None], V=ud.V[None, None], idx=ud.idx[None, None],
                 cid=None if ud.cid is None else ud.cid[None, None],
-                mu_Q=None if ud.mu_Q is None else ud.mu_Q[None])
+                mu_Q=None if ud.mu_Q is None else ud.mu_Q[None],
+                U=None if ud.U is None else ud.U[None, None])
