@@ -160,7 +160,9 @@ typedef enum {
   SDA_OP_SPARSE = 0,
   SDA_OP_DENSE = 1,
   SDA_OP_BUILD_PROXIES = 2,
-  SDA_OP_BUILD_PRIOR = 3
+  SDA_OP_BUILD_PRIOR = 3,
+  SDA_OP_BUILD_QGS = 4,
+  SDA_OP_SELECT_QGS = 5
 } sda_op;
 
 /* Workspace bytes an entry point needs for these sizes (m: entries per unit
@@ -170,14 +172,19 @@ size_t sda_workspace_bytes(const sda_dims* dims, int32_t op, int32_t tail_kind,
                            int32_t m, int32_t C);
 
 /* Count-aware mean proxy state (OpenAttention, method stage 01: the
- * per-cluster count and mean tokens cached once per request; here as sums).
+ * per-cluster count and mean tokens cached once per request; here as sums,
+ * and the diagonal-variance token as the sum of squared keys).
  * For each unit and cluster b: count[b] = #{j : cluster_id[j] == b},
- * sumK[b] = sum of those keys, sumV[b] = sum of those values (fp32).
+ * sumK[b] = sum of those keys, sumV[b] = sum of those values, and, when
+ * sumK2 is not NULL, sumK2[b] = sum of their elementwise squared keys (all
+ * fp32, [B,Hkv,C,d]).  Sums are deterministic (no atomics): repeated builds
+ * give the same bits.
  * cluster_id [B,Hkv,n] int32 in [-1, C); -1 = the row is in no cluster.
- * Ids outside [-1, C) are ignored and flagged in dev_flags. */
+ * Ids outside [-1, C) are ignored and flagged in dev_flags.  The workspace
+ * size (SDA_OP_BUILD_PROXIES) covers either form. */
 sda_status sda_build_tail_proxies(const sda_dims* dims, const void* K, const void* V,
                                   const int32_t* cluster_id, int32_t C,
-                                  int32_t* count, float* sumK, float* sumV,
+                                  int32_t* count, float* sumK, float* sumV, float* sumK2,
                                   int32_t* dev_flags, void* ws, size_t ws_bytes,
                                   void* stream);
 
@@ -215,6 +222,67 @@ const char* sda_status_str(int32_t status);
 
 /* Library version, "major.minor.patch". */
 const char* sda_version(void);
+
+/* ---- Selector in front of the proxy decode ------------------------------
+ * (OpenAttention, method stages 02-03 and the settings list: keys coded in
+ * int8 per KV head and coordinate and scored in an r = 32 query subspace;
+ * an exact-read budget per cluster from the estimated weight error of its
+ * mean proxy; each cluster reads its best-scoring rows.)  The page states
+ * the stages, not their formulas; the readings taken here are spelled out
+ * below. */
+#define SDA_QGS_RANK 32
+
+/* Key codes, once per request.  U [B,Hkv,d,32] fp32: the subspace basis of
+ * each unit (orthonormal columns; the leading eigenvectors of the queries'
+ * second moment).  For every row: y_j = U^T k_j, summed over d in order in
+ * fp64 (each product is exact); kmax [B,Hkv,32] fp64 = max_j |y_ji|;
+ * codes [B,Hkv,n,32] int8 = rint(127 y_ji / kmax_i), half to even, 0 where
+ * kmax_i = 0.  K and codes 16-byte aligned.  Workspace: SDA_OP_BUILD_QGS. */
+sda_status sda_build_qgs_codes(const sda_dims* dims, const void* K, const float* U,
+                               int8_t* codes, double* kmax, void* ws, size_t ws_bytes,
+                               void* stream);
+
+typedef struct {
+  int32_t n_sink;                /* rows [0, n_sink) are always listed       */
+  int32_t n_local;               /* rows [n - n_local, n) are always listed  */
+  int32_t E;                     /* rows to pick in between, over clusters   */
+  int32_t C;                     /* clusters, 1..64                          */
+  const int32_t* cluster_id;     /* [B,Hkv,n] in [-1, C)                     */
+  const int32_t* count;          /* [B,Hkv,C]    from sda_build_tail_proxies */
+  const float* sumK;             /* [B,Hkv,C,d]  from sda_build_tail_proxies */
+  const float* sumK2;            /* [B,Hkv,C,d]  from sda_build_tail_proxies */
+  const float* U;                /* [B,Hkv,d,32] the basis given to the codes */
+  const int8_t* codes;           /* [B,Hkv,n,32] from sda_build_qgs_codes    */
+  const double* kmax;            /* [B,Hkv,32]   from sda_build_qgs_codes    */
+} sda_selector;
+
+/* The index set of one decode step, per unit:
+ *   - query weights: qt_h = U^T q_h (fp64, in order), w_hi = qt_hi kmax_i,
+ *     wq_hi = rint(127 w_hi / max|w|) over the KV group (int8);
+ *   - score of row j: S_j = max over the group's heads of
+ *     sum_i wq_hi code_ji (exact integer);
+ *   - weight error of cluster b (Gaussian logit model, diagonal variance):
+ *     zbar = scale <q_h, mu_b>, s2 = scale^2 sum_d q_hd^2 nu_bd
+ *     (mu = sumK/N, nu = max(0, sumK2/N - mu^2)),
+ *     eps_b = sum_h N_b e^{zbar} (e^{s2/2} - 1) / sum_b' N_b' e^{zbar' + s2'/2};
+ *   - budgets: E split in proportion to eps_b by the largest remainder (ties
+ *     to the lower b), capped at A_b = members of b in [n_sink, n - n_local);
+ *     capped clusters are fixed and the rest split again; with no error left
+ *     the remaining capacity weighs; sum q_b = min(E, sum A_b);
+ *   - cluster b lists its q_b eligible rows with the largest S_j (ties to
+ *     the lower position); rows with cluster id -1 are never picked.
+ * Writes idx [B,Hkv,m] ascending (sink, local window and the picked rows),
+ * idx_len [B,Hkv], idx_cluster [B,Hkv,m] (cluster of each listed row, -1 if
+ * none; entries past idx_len are 0 and -1), and budget [B,Hkv,C] (or NULL).
+ * The output feeds sda_sparse_decode_attn with a PROXY tail directly.
+ * Requires n <= 2^20 (else SDA_EUNSUPPORTED) and
+ * m >= min(n, n_sink + n_local + E) (else SDA_EINVAL).  Cluster ids outside
+ * [-1, C) are treated as -1 and flagged.  Workspace: SDA_OP_SELECT_QGS
+ * (with this C). */
+sda_status sda_select_qgs(const sda_dims* dims, const void* q, const sda_selector* sel,
+                          int32_t m, int32_t* idx, int32_t* idx_len, int32_t* idx_cluster,
+                          int32_t* budget, int32_t* dev_flags, void* ws, size_t ws_bytes,
+                          void* stream);
 
 #ifdef __cplusplus
 }

@@ -5,10 +5,13 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include <hip/hip_runtime.h>
 
 #include "sda.h"
 #include "sda_kernels.hpp"
+#include "sda_select.hpp"
 
 #define SDA_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -176,7 +179,29 @@ size_t proxy_ws(const Resolved& r, int C) {
   int chunks, rows;
   proxy_build_shape(r.B * r.Hkv, r.n, C, &chunks, &rows);
   const size_t units = (size_t)r.B * r.Hkv;
-  return units * chunks * C * (2 * kD * sizeof(float) + sizeof(int32_t));
+  // column sums of K, V and K^2 per (unit, chunk, cluster), then the counts
+  return units * chunks * C * (3 * kD * sizeof(float) + sizeof(int32_t));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t qgs_build_ws(const Resolved& r) {
+  return (size_t)r.B * r.Hkv * qgs_chunks(r.n) * kQgsRank * sizeof(double);
+}
+
+struct QgsSelectWs {
+  size_t keys, wq, budget, avail, total;
+};
+
+QgsSelectWs qgs_select_ws(const Resolved& r, int C) {
+  const size_t units = (size_t)r.B * r.Hkv;
+  QgsSelectWs w;
+  w.keys = 0;
+  w.wq = w.keys + align256(units * r.n * sizeof(uint64_t));
+  w.budget = w.wq + align256(units * r.G * (kQgsRank / 4) * sizeof(uint32_t));
+  w.avail = w.budget + align256(units * C * sizeof(int32_t));
+  w.total = w.avail + align256(units * C * sizeof(int32_t));
+  return w;
 }
 
 void fill_common(const Resolved& r, AttnParams* p) {
@@ -226,14 +251,16 @@ SDA_EXPORT size_t sda_workspace_bytes(const sda_dims* dims, int32_t op, int32_t 
     case SDA_OP_DENSE: return dense_ws(r, false);
     case SDA_OP_BUILD_PRIOR: return dense_ws(r, true);
     case SDA_OP_BUILD_PROXIES: return (C >= 1 && C <= kCmax) ? proxy_ws(r, C) : 0;
+    case SDA_OP_BUILD_QGS: return qgs_build_ws(r);
+    case SDA_OP_SELECT_QGS: return (C >= 1 && C <= kCmax) ? qgs_select_ws(r, C).total : 0;
   }
   return 0;
 }
 
 SDA_EXPORT sda_status sda_build_tail_proxies(const sda_dims* dims, const void* K, const void* V,
                                              const int32_t* cluster_id, int32_t C, int32_t* count,
-                                             float* sumK, float* sumV, int32_t* dev_flags, void* ws,
-                                             size_t ws_bytes, void* stream) {
+                                             float* sumK, float* sumV, float* sumK2, int32_t* dev_flags,
+                                             void* ws, size_t ws_bytes, void* stream) {
   Resolved r;
   sda_status st = resolve(dims, &r);
   if (st != SDA_OK) return st;
@@ -257,9 +284,10 @@ SDA_EXPORT sda_status sda_build_tail_proxies(const sda_dims* dims, const void* K
   proxy_build_shape(units, r.n, C, &p.chunks, &p.rows_per_chunk);
   p.part = reinterpret_cast<float*>(ws);
   p.pcount = reinterpret_cast<int32_t*>(reinterpret_cast<char*>(ws) +
-                                        (size_t)units * p.chunks * C * 2 * kD * sizeof(float));
+                                        (size_t)units * p.chunks * C * 3 * kD * sizeof(float));
   p.count = count;
   p.sumK = sumK;
+  p.sumK2 = sumK2;
   p.sumV = sumV;
   p.flags = dev_flags;
   return hip_status(launch_proxy_build(p, r.dtype, units, reinterpret_cast<hipStream_t>(stream)));
@@ -414,4 +442,81 @@ SDA_EXPORT sda_status sda_sparse_decode_attn(const sda_dims* dims, const void* q
   hipError_t e = launch_stream_any(p, r, mode, hs);
   if (e == hipSuccess && p.splits > 1) e = launch_merge(p, r.G, mode, hs);
   return hip_status(e);
+}
+
+SDA_EXPORT sda_status sda_build_qgs_codes(const sda_dims* dims, const void* K, const float* U, int8_t* codes,
+                                          double* kmax, void* ws, size_t ws_bytes, void* stream) {
+  Resolved r;
+  sda_status st = resolve(dims, &r);
+  if (st != SDA_OK) return st;
+  if (!K || !U || !codes || !kmax) return SDA_EINVAL;
+  if (!aligned16(K) || !aligned16(codes)) return SDA_EINVAL;
+  const size_t need = qgs_build_ws(r);
+  if (!ws || ws_bytes < need) return SDA_EWORKSPACE;
+  QgsBuildParams p;
+  memset(&p, 0, sizeof(p));
+  p.K = K;
+  p.U = U;
+  p.sb = r.sb;
+  p.sh = r.sh;
+  p.sn = r.sn;
+  p.Hkv = r.Hkv;
+  p.n = r.n;
+  p.chunks = qgs_chunks(r.n);
+  p.part = reinterpret_cast<double*>(ws);
+  p.codes = codes;
+  p.kmax = kmax;
+  return hip_status(launch_qgs_build(p, r.dtype, r.B * r.Hkv, reinterpret_cast<hipStream_t>(stream)));
+}
+
+SDA_EXPORT sda_status sda_select_qgs(const sda_dims* dims, const void* q, const sda_selector* sel, int32_t m,
+                                     int32_t* idx, int32_t* idx_len, int32_t* idx_cluster, int32_t* budget,
+                                     int32_t* dev_flags, void* ws, size_t ws_bytes, void* stream) {
+  Resolved r;
+  sda_status st = resolve(dims, &r);
+  if (st != SDA_OK) return st;
+  if (!q || !sel || !idx || !idx_len || !idx_cluster) return SDA_EINVAL;
+  if (!sel->cluster_id || !sel->count || !sel->sumK || !sel->sumK2 || !sel->U || !sel->codes || !sel->kmax)
+    return SDA_EINVAL;
+  if (!aligned16(sel->codes) || !aligned16(sel->U) || !aligned16(sel->sumK) || !aligned16(sel->sumK2))
+    return SDA_EINVAL;
+  if (sel->C < 1 || sel->C > kCmax) return SDA_EUNSUPPORTED;
+  if (r.n > kQgsMaxN) return SDA_EUNSUPPORTED;
+  if (sel->n_sink < 0 || sel->n_local < 0 || sel->E < 0) return SDA_EINVAL;
+  const int64_t most = std::min<int64_t>((int64_t)r.n, (int64_t)sel->n_sink + sel->n_local + sel->E);
+  if (m < most) return SDA_EINVAL;
+  const QgsSelectWs w = qgs_select_ws(r, sel->C);
+  if (!ws || ws_bytes < w.total) return SDA_EWORKSPACE;
+  char* base = reinterpret_cast<char*>(ws);
+  QgsSelectParams p;
+  memset(&p, 0, sizeof(p));
+  p.q = q;
+  p.cid = sel->cluster_id;
+  p.count = sel->count;
+  p.sumK = sel->sumK;
+  p.sumK2 = sel->sumK2;
+  p.U = sel->U;
+  p.codes = sel->codes;
+  p.kmax = sel->kmax;
+  p.B = r.B;
+  p.Hq = r.Hq;
+  p.Hkv = r.Hkv;
+  p.n = r.n;
+  p.G = r.G;
+  p.C = sel->C;
+  p.n_sink = sel->n_sink;
+  p.n_local = sel->n_local;
+  p.E = sel->E;
+  p.m = m;
+  p.scale = r.scale;
+  p.keys = reinterpret_cast<uint64_t*>(base + w.keys);
+  p.wq = reinterpret_cast<uint32_t*>(base + w.wq);
+  p.wbudget = reinterpret_cast<int32_t*>(base + w.budget);
+  p.wavail = reinterpret_cast<int32_t*>(base + w.avail);
+  p.idx = idx;
+  p.idx_len = idx_len;
+  p.idx_cluster = idx_cluster;
+  p.budget = budget;
+  p.flags = dev_flags;
+  return hip_status(launch_qgs_select(p, r.dtype, reinterpret_cast<hipStream_t>(stream)));
 }

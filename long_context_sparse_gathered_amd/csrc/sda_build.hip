@@ -22,10 +22,12 @@ constexpr int kBuildLoads = kBuildRows / 4;   // row loads per lane per group
 // the current cluster; on a cluster change the four quarters' runs are added
 // in a fixed order and quarter 0 adds the result to this chunk's LDS column
 // sums.  Cluster ids are contiguous runs in practice: a group of 32 rows that
-// lies in one cluster is summed without per-row checks.
-template <typename T>
+// lies in one cluster is summed without per-row checks.  With SQ the K wave
+// also sums the squared keys (the diagonal-variance token of stage 01).
+template <typename T, bool SQ>
 __global__ __launch_bounds__(128) void proxy_partial_kernel(const ProxyBuildParams p) {
-  extern __shared__ float s_acc[];       // [C][2*kD] column sums of this chunk
+  constexpr int NCOL = SQ ? 3 * kD : 2 * kD;   // [K | V | K^2] columns per cluster
+  extern __shared__ float s_acc[];       // [C][NCOL] column sums of this chunk
 
   const int u = blockIdx.x / p.chunks;
   const int ch = blockIdx.x - u * p.chunks;
@@ -37,7 +39,7 @@ __global__ __launch_bounds__(128) void proxy_partial_kernel(const ProxyBuildPara
   const int r16 = lane & 15;
   const int rq = lane >> 4;              // row of the four a load covers
 
-  for (int i = tid; i < p.C * 2 * kD; i += 128) s_acc[i] = 0.f;
+  for (int i = tid; i < p.C * NCOL; i += 128) s_acc[i] = 0.f;
   __syncthreads();
 
   const int r0 = ch * p.rows_per_chunk;
@@ -49,9 +51,9 @@ __global__ __launch_bounds__(128) void proxy_partial_kernel(const ProxyBuildPara
   int cur = -1;
   int run_cnt = 0;
   int cnt_c = 0;   // K wave: lane c counts the rows of cluster c (C <= 64)
-  float run[kPerLane];
+  float run[kPerLane], run2[kPerLane];
 #pragma unroll
-  for (int e = 0; e < kPerLane; ++e) run[e] = 0.f;
+  for (int e = 0; e < kPerLane; ++e) run[e] = run2[e] = 0.f;
   bool bad = false;
 
   auto flush = [&]() {
@@ -59,12 +61,21 @@ __global__ __launch_bounds__(128) void proxy_partial_kernel(const ProxyBuildPara
 #pragma unroll
       for (int e = 0; e < kPerLane; ++e) {
         const float v = sum_rowgroups(run[e]);
-        if (rq == 0) s_acc[cur * 2 * kD + tensor * kD + r16 * kPerLane + e] += v;
+        if (rq == 0) s_acc[cur * NCOL + tensor * kD + r16 * kPerLane + e] += v;
+      }
+      if constexpr (SQ) {
+        if (tensor == 0) {
+#pragma unroll
+          for (int e = 0; e < kPerLane; ++e) {
+            const float v = sum_rowgroups(run2[e]);
+            if (rq == 0) s_acc[cur * NCOL + 2 * kD + r16 * kPerLane + e] += v;
+          }
+        }
       }
       if (tensor == 0 && lane == cur) cnt_c += run_cnt;
     }
 #pragma unroll
-    for (int e = 0; e < kPerLane; ++e) run[e] = 0.f;
+    for (int e = 0; e < kPerLane; ++e) run[e] = run2[e] = 0.f;
     run_cnt = 0;
   };
   auto add_row = [&](const RowChunk<T>& w) {
@@ -72,6 +83,12 @@ __global__ __launch_bounds__(128) void proxy_partial_kernel(const ProxyBuildPara
     w.unpack(f);
 #pragma unroll
     for (int e = 0; e < kPerLane; ++e) run[e] += f[e];
+    if constexpr (SQ) {
+      if (tensor == 0) {
+#pragma unroll
+        for (int e = 0; e < kPerLane; ++e) run2[e] = fmaf(f[e], f[e], run2[e]);
+      }
+    }
   };
 
   // Groups are double-buffered: the next group's rows are in flight while
@@ -136,42 +153,49 @@ __global__ __launch_bounds__(128) void proxy_partial_kernel(const ProxyBuildPara
   if (bad && tid == 0) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
   __syncthreads();
 
-  float* dst = p.part + ((int64_t)u * p.chunks + ch) * p.C * 2 * kD;
-  for (int i = tid; i < p.C * 2 * kD; i += 128) dst[i] = s_acc[i];
+  float* dst = p.part + ((int64_t)u * p.chunks + ch) * p.C * NCOL;
+  for (int i = tid; i < p.C * NCOL; i += 128) dst[i] = s_acc[i];
   if (tid < p.C) p.pcount[((int64_t)u * p.chunks + ch) * p.C + tid] = cnt_c;
 }
 
-__global__ __launch_bounds__(256) void proxy_reduce_kernel(const ProxyBuildParams p) {
+__global__ __launch_bounds__(384) void proxy_reduce_kernel(const ProxyBuildParams p) {
   const int u = blockIdx.x / p.C;
   const int b = blockIdx.x - u * p.C;
-  const int t = threadIdx.x;  // column of [K | V]
+  const int t = threadIdx.x;  // column of [K | V | K^2]
+  const int ncol = p.sumK2 ? 3 * kD : 2 * kD;
+  if (t >= ncol) return;
   float a = 0.f;
   int cnt = 0;
   for (int ch = 0; ch < p.chunks; ++ch) {
     const int64_t rec = (int64_t)u * p.chunks + ch;
-    a += p.part[(rec * p.C + b) * 2 * kD + t];
+    a += p.part[(rec * p.C + b) * ncol + t];
     if (t == 0) cnt += p.pcount[rec * p.C + b];
   }
   const int64_t o = ((int64_t)u * p.C + b) * kD;
   if (t < kD) {
     p.sumK[o + t] = a;
-  } else {
+  } else if (t < 2 * kD) {
     p.sumV[o + t - kD] = a;
+  } else {
+    p.sumK2[o + t - 2 * kD] = a;
   }
   if (t == 0) p.count[(int64_t)u * p.C + b] = cnt;
 }
 
 hipError_t launch_proxy_build(const ProxyBuildParams& p, int dtype, int units, hipStream_t st) {
-  const size_t lds = (size_t)p.C * 2 * kD * sizeof(float);
+  const bool sq = p.sumK2 != nullptr;
+  const size_t lds = (size_t)p.C * (sq ? 3 : 2) * kD * sizeof(float);
   const dim3 grid(units * p.chunks);
   if (dtype == SDA_BF16) {
-    hipLaunchKernelGGL(proxy_partial_kernel<bf16_t>, grid, dim3(128), lds, st, p);
+    if (sq) hipLaunchKernelGGL((proxy_partial_kernel<bf16_t, true>), grid, dim3(128), lds, st, p);
+    else hipLaunchKernelGGL((proxy_partial_kernel<bf16_t, false>), grid, dim3(128), lds, st, p);
   } else {
-    hipLaunchKernelGGL(proxy_partial_kernel<float>, grid, dim3(128), lds, st, p);
+    if (sq) hipLaunchKernelGGL((proxy_partial_kernel<float, true>), grid, dim3(128), lds, st, p);
+    else hipLaunchKernelGGL((proxy_partial_kernel<float, false>), grid, dim3(128), lds, st, p);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(proxy_reduce_kernel, dim3(units * p.C), dim3(2 * kD), 0, st, p);
+  hipLaunchKernelGGL(proxy_reduce_kernel, dim3(units * p.C), dim3((sq ? 3 : 2) * kD), 0, st, p);
   return hipGetLastError();
 }
 

@@ -84,11 +84,12 @@ struct ProxyBuildParams {
   int32_t Hkv, n, C;
   int32_t rows_per_chunk;
   int32_t chunks;
-  float* part;                 // [units, chunks, C, 2*d]
+  float* part;                 // [units, chunks, C, 2*d or 3*d]
   int32_t* pcount;             // [units, chunks, C]
   int32_t* count;              // outputs
   float* sumK;
   float* sumV;
+  float* sumK2;                // or null
   int32_t* flags;
 };
 

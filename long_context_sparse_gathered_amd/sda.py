@@ -22,11 +22,12 @@ LIB_PATH = os.path.join(_PKG, "libsda.so")
 SDA_OK, SDA_EINVAL, SDA_ESHAPE, SDA_EDTYPE, SDA_EWORKSPACE, SDA_EUNSUPPORTED, SDA_EHIP = 0, -1, -2, -3, -4, -5, -6
 SDA_BF16, SDA_F32 = 0, 1
 TAIL_NONE, TAIL_PROXY, TAIL_PRIOR, TAIL_SAMPLED = 0, 1, 2, 3
-OP_SPARSE, OP_DENSE, OP_BUILD_PROXIES, OP_BUILD_PRIOR = 0, 1, 2, 3
+OP_SPARSE, OP_DENSE, OP_BUILD_PROXIES, OP_BUILD_PRIOR, OP_BUILD_QGS, OP_SELECT_QGS = 0, 1, 2, 3, 4, 5
+QGS_RANK = 32
 FLAG_IDX_RANGE, FLAG_IDX_ORDER, FLAG_SAMPLE_CAP, FLAG_CLUSTER, FLAG_LEN = 1, 2, 4, 8, 16
 
 EXPORTED = ["sda_workspace_bytes", "sda_build_tail_proxies", "sda_build_prior", "sda_sparse_decode_attn",
-            "sda_dense_decode_attn", "sda_status_str", "sda_version"]
+            "sda_dense_decode_attn", "sda_build_qgs_codes", "sda_select_qgs", "sda_status_str", "sda_version"]
 
 
 class SdaError(RuntimeError):
@@ -56,6 +57,12 @@ class Tail(ctypes.Structure):
                 ("samples_out", _vp)]
 
 
+class Selector(ctypes.Structure):
+    _fields_ = [("n_sink", ctypes.c_int32), ("n_local", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("C", ctypes.c_int32), ("cluster_id", _vp), ("count", _vp), ("sumK", _vp), ("sumK2", _vp),
+                ("U", _vp), ("codes", _vp), ("kmax", _vp)]
+
+
 _lib = None
 
 
@@ -72,7 +79,11 @@ def lib() -> ctypes.CDLL:
     L.sda_workspace_bytes.restype = sz
     L.sda_workspace_bytes.argtypes = [D, i32, i32, i32, i32]
     L.sda_build_tail_proxies.restype = i32
-    L.sda_build_tail_proxies.argtypes = [D, _vp, _vp, _vp, i32, _vp, _vp, _vp, _vp, _vp, sz, _vp]
+    L.sda_build_tail_proxies.argtypes = [D, _vp, _vp, _vp, i32, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp]
+    L.sda_build_qgs_codes.restype = i32
+    L.sda_build_qgs_codes.argtypes = [D, _vp, _vp, _vp, _vp, _vp, sz, _vp]
+    L.sda_select_qgs.restype = i32
+    L.sda_select_qgs.argtypes = [D, _vp, ctypes.POINTER(Selector), i32, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp]
     L.sda_build_prior.restype = i32
     L.sda_build_prior.argtypes = [D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp]
     L.sda_sparse_decode_attn.restype = i32
@@ -168,6 +179,7 @@ class ProxyState:
     count: torch.Tensor     # [B,Hkv,C] int32
     sumK: torch.Tensor      # [B,Hkv,C,d] fp32
     sumV: torch.Tensor      # [B,Hkv,C,d] fp32
+    sumK2: Optional[torch.Tensor] = None   # [B,Hkv,C,d] fp32 sums of squared keys (selector)
 
 
 @dataclass
@@ -229,7 +241,7 @@ def _tail_struct(tail, idx_cluster, cluster_id, lam, keep) -> Tail:
 
 def build_tail_proxies(K: torch.Tensor, V: torch.Tensor, cluster_id: torch.Tensor, C: int,
                        flags: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                       stream=None) -> ProxyState:
+                       stream=None, with_sumK2: bool = False) -> ProxyState:
     dims = make_dims(K, 1)
     dims.Hq = dims.Hkv
     B, Hkv, n, d = K.shape
@@ -237,12 +249,13 @@ def build_tail_proxies(K: torch.Tensor, V: torch.Tensor, cluster_id: torch.Tenso
     count = torch.empty((B, Hkv, C), dtype=torch.int32, device=dev)
     sumK = torch.empty((B, Hkv, C, d), dtype=torch.float32, device=dev)
     sumV = torch.empty((B, Hkv, C, d), dtype=torch.float32, device=dev)
+    sumK2 = torch.empty((B, Hkv, C, d), dtype=torch.float32, device=dev) if with_sumK2 else None
     ws, wsb = _workspace(workspace_bytes(dims, OP_BUILD_PROXIES, C=C), dev, ws)
     rc = lib().sda_build_tail_proxies(ctypes.byref(dims), _ptr(K), _ptr(V), _ptr(_i32(cluster_id)), int(C),
-                                      _ptr(count), _ptr(sumK), _ptr(sumV), _ptr(flags), _ptr(ws), wsb,
-                                      _stream(stream))
+                                      _ptr(count), _ptr(sumK), _ptr(sumV), _ptr(sumK2), _ptr(flags), _ptr(ws),
+                                      wsb, _stream(stream))
     _check(rc, "sda_build_tail_proxies")
-    return ProxyState(C=C, count=count, sumK=sumK, sumV=sumV)
+    return ProxyState(C=C, count=count, sumK=sumK, sumV=sumV, sumK2=sumK2)
 
 
 def build_prior(K: torch.Tensor, V: torch.Tensor, mu_Q: torch.Tensor, scale: Optional[float] = None,
@@ -309,6 +322,61 @@ def sparse_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: O
                                       _ptr(out), _ptr(lse), _ptr(flags), _ptr(ws), wsb, _stream(stream))
     _check(rc, "sda_sparse_decode_attn")
     return out, lse
+
+
+@dataclass
+class QgsCodes:
+    """Selector key codes from build_qgs_codes."""
+    U: torch.Tensor         # [B,Hkv,d,32] fp32 basis the codes were built with
+    codes: torch.Tensor     # [B,Hkv,n,32] int8
+    kmax: torch.Tensor      # [B,Hkv,32] fp64
+
+
+def build_qgs_codes(K: torch.Tensor, U: torch.Tensor, ws: Optional[torch.Tensor] = None,
+                    stream=None) -> QgsCodes:
+    dims = make_dims(K, 1)
+    dims.Hq = dims.Hkv
+    B, Hkv, n, d = K.shape
+    dev = K.device
+    U = _f32c(U, "U")
+    if tuple(U.shape) != (B, Hkv, d, QGS_RANK):
+        raise ValueError(f"U must be [B, Hkv, d, {QGS_RANK}]")
+    codes = torch.empty((B, Hkv, n, QGS_RANK), dtype=torch.int8, device=dev)
+    kmax = torch.empty((B, Hkv, QGS_RANK), dtype=torch.float64, device=dev)
+    ws, wsb = _workspace(workspace_bytes(dims, OP_BUILD_QGS), dev, ws)
+    rc = lib().sda_build_qgs_codes(ctypes.byref(dims), _ptr(K), _ptr(U), _ptr(codes), _ptr(kmax), _ptr(ws), wsb,
+                                   _stream(stream))
+    _check(rc, "sda_build_qgs_codes")
+    return QgsCodes(U=U, codes=codes, kmax=kmax)
+
+
+def select_qgs(q: torch.Tensor, K: torch.Tensor, cluster_id: torch.Tensor, proxies: ProxyState, qc: QgsCodes,
+               n_sink: int, n_local: int, E: int, m: Optional[int] = None, scale: Optional[float] = None,
+               out: Optional[tuple] = None, budget: Optional[torch.Tensor] = None,
+               flags: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
+    """The selector: returns (idx [B,Hkv,m], idx_len [B,Hkv], idx_cluster [B,Hkv,m]); fills budget
+    [B,Hkv,C] when given.  K only supplies the cache's shape and strides."""
+    B, Hq, d = q.shape
+    dims = make_dims(K, Hq, scale)
+    n, Hkv = K.shape[2], K.shape[1]
+    dev = q.device
+    if proxies.sumK2 is None:
+        raise ValueError("the selector needs the proxies built with with_sumK2=True")
+    if m is None:
+        m = min(n, n_sink + n_local + E)
+    if out is None:
+        out = (torch.empty((B, Hkv, m), dtype=torch.int32, device=dev),
+               torch.empty((B, Hkv), dtype=torch.int32, device=dev),
+               torch.empty((B, Hkv, m), dtype=torch.int32, device=dev))
+    idx, idx_len, idx_cluster = out
+    sel = Selector(int(n_sink), int(n_local), int(E), int(proxies.C), _ptr(_i32(cluster_id)),
+                   _ptr(_i32(proxies.count)), _ptr(_f32c(proxies.sumK, "sumK")),
+                   _ptr(_f32c(proxies.sumK2, "sumK2")), _ptr(_f32c(qc.U, "U")), _ptr(qc.codes), _ptr(qc.kmax))
+    ws, wsb = _workspace(workspace_bytes(dims, OP_SELECT_QGS, C=proxies.C), dev, ws)
+    rc = lib().sda_select_qgs(ctypes.byref(dims), _ptr(q), ctypes.byref(sel), int(m), _ptr(idx), _ptr(idx_len),
+                              _ptr(idx_cluster), _ptr(budget), _ptr(flags), _ptr(ws), wsb, _stream(stream))
+    _check(rc, "sda_select_qgs")
+    return idx, idx_len, idx_cluster
 
 
 def default_scale(d: int) -> float:

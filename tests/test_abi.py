@@ -124,11 +124,11 @@ def test_prior_tail_validation(L):
 
 def test_builder_and_dense_validation(L):
     dims = _dims()
-    assert L.sda_build_tail_proxies(ctypes.byref(dims), FAKE, FAKE, FAKE, 100, FAKE, FAKE, FAKE, None, FAKE, 1 << 30,
-                                    None) == sda.SDA_EUNSUPPORTED
-    assert L.sda_build_tail_proxies(ctypes.byref(dims), FAKE, FAKE, None, 8, FAKE, FAKE, FAKE, None, FAKE, 1 << 30,
-                                    None) == sda.SDA_EINVAL
-    assert L.sda_build_tail_proxies(ctypes.byref(dims), FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, None, FAKE, 16,
+    assert L.sda_build_tail_proxies(ctypes.byref(dims), FAKE, FAKE, FAKE, 100, FAKE, FAKE, FAKE, None, None, FAKE,
+                                    1 << 30, None) == sda.SDA_EUNSUPPORTED
+    assert L.sda_build_tail_proxies(ctypes.byref(dims), FAKE, FAKE, None, 8, FAKE, FAKE, FAKE, None, None, FAKE,
+                                    1 << 30, None) == sda.SDA_EINVAL
+    assert L.sda_build_tail_proxies(ctypes.byref(dims), FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, FAKE, None, FAKE, 16,
                                     None) == sda.SDA_EWORKSPACE
     assert L.sda_build_prior(ctypes.byref(dims), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None, 0,
                              None) == sda.SDA_EINVAL
@@ -146,3 +146,38 @@ def test_workspace_sizes(L):
     assert L.sda_workspace_bytes(ctypes.byref(b32), sda.OP_BUILD_PROXIES, 0, 0, 32) > 0
     assert L.sda_workspace_bytes(ctypes.byref(b32), sda.OP_BUILD_PROXIES, 0, 0, 99) == 0
     assert L.sda_workspace_bytes(None, sda.OP_DENSE, 0, 0, 0) == 0
+
+
+def test_selector_validation(L):
+    """Host-side checks of the selector entry points (nothing launches)."""
+    dims = _dims()
+    assert L.sda_build_qgs_codes(ctypes.byref(dims), FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == sda.SDA_EINVAL
+    assert L.sda_build_qgs_codes(ctypes.byref(dims), MISALIGNED, FAKE, FAKE, FAKE, FAKE, 1 << 30,
+                                 None) == sda.SDA_EINVAL
+    need = L.sda_workspace_bytes(ctypes.byref(dims), sda.OP_BUILD_QGS, 0, 0, 0)
+    assert need == 2 * 2 * (1024 // 256) * 32 * 8          # fp64 chunk maxima per (unit, chunk, coordinate)
+    assert L.sda_build_qgs_codes(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+                                 None) == sda.SDA_EWORKSPACE
+
+    def sel(**kw):
+        f = dict(n_sink=4, n_local=16, E=40, C=8, cluster_id=FAKE, count=FAKE, sumK=FAKE, sumK2=FAKE, U=FAKE,
+                 codes=FAKE, kmax=FAKE)
+        f.update(kw)
+        return sda.Selector(**f)
+
+    def call(s, m=60, ws_bytes=1 << 30, d=dims):
+        return L.sda_select_qgs(ctypes.byref(d), FAKE, ctypes.byref(s), m, FAKE, FAKE, FAKE, None, None, FAKE,
+                                ws_bytes, None)
+
+    assert call(sel(C=0)) == sda.SDA_EUNSUPPORTED
+    assert call(sel(C=65)) == sda.SDA_EUNSUPPORTED
+    assert call(sel(sumK2=None)) == sda.SDA_EINVAL
+    assert call(sel(E=-1)) == sda.SDA_EINVAL
+    assert call(sel(), m=59) == sda.SDA_EINVAL                  # capacity below 4 + 16 + 40
+    assert call(sel(codes=MISALIGNED)) == sda.SDA_EINVAL
+    big = _dims(n=(1 << 20) + 1, B=1, Hq=4, Hkv=1)
+    assert call(sel(), d=big) == sda.SDA_EUNSUPPORTED
+    wsel = L.sda_workspace_bytes(ctypes.byref(dims), sda.OP_SELECT_QGS, 0, 0, 8)
+    assert wsel >= 4 * 1024 * 8                                 # one 8-byte key per row
+    assert call(sel(), ws_bytes=wsel - 1) == sda.SDA_EWORKSPACE
+    assert L.sda_workspace_bytes(ctypes.byref(dims), sda.OP_SELECT_QGS, 0, 0, 0) == 0
