@@ -20,9 +20,9 @@ read different copies of the KV cache and proxy state (standing in for the
 other layers of a decode step); a copy comes back only after the other
 copies have streamed several times the cache size.
 
-`--rows` adds measurements of the other hot-path rows (sampled tail at
-batch 8 / 64K, rank-1 prior at batch 16 / 128K, the builders) under
-`secondary`.  `--copy-calibration` runs only a plain 1 GiB device copy (the
+The other hot-path rows (sampled tail at batch 8 / 64K, rank-1 prior at
+batch 16 / 128K, the selector at batch 32 / 32K, the builders) are measured
+too and reported under `secondary` (`--no-rows` skips them).  `--copy-calibration` runs only a plain 1 GiB device copy (the
 reference kernel for scaling the HBM byte counters).
 """
 from __future__ import annotations
@@ -64,7 +64,9 @@ def _args():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--check-units", type=int, default=4, help="units checked against the oracle")
-    ap.add_argument("--rows", action="store_true", help="also measure the sampled and prior rows and the builders")
+    ap.add_argument("--rows", action="store_true", default=True,
+                    help="also measure the sampled, prior and selector rows and the builders (default)")
+    ap.add_argument("--no-rows", dest="rows", action="store_false", help="the headline step only")
     ap.add_argument("--copy-calibration", action="store_true")
     return ap.parse_args()
 
@@ -278,7 +280,8 @@ def cpu_baseline(w, c, seconds):
 
 def measure_rows(a, dev):
     """Sampled tail (batch 8, 64K) and rank-1 prior (batch 16, 128K) decode
-    steps, and the prior build, each on its own synthetic workload."""
+    steps, the prior build, and the selector (QGS + ErrorGate, batch 32, 32K)
+    with its builders, each on its own synthetic workload."""
     import torch
 
     from long_context_sparse_gathered_amd import sda, synth
@@ -334,6 +337,41 @@ def measure_rows(a, dev):
                               "frac_hbm_peak": round(by / (ms_p * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                               "build_prior_us": round(build_ms * 1e3, 1),
                               "build_prior_gbs": round(dense_by / (build_ms * 1e-3) / 1e9, 1)}
+    del copies, K, V, c, ps
+    torch.cuda.empty_cache()
+
+    # the selector in front of the proxy decode (QGS codes + ErrorGate + per-cluster top-q)
+    w = synth.WORKLOADS["qgs_bf16_b32_n32k"]
+    c = synth.make_case(w)
+    q, K, V, U, cid = (to_dev(x, dev) for x in (c.q, c.K, c.V, c.U, c.cid))
+    ws_b = torch.empty(sda.workspace_bytes(sda.make_dims(K, w.Hq), sda.OP_BUILD_PROXIES, C=w.C), dtype=torch.uint8,
+                       device=dev)
+    pbuild_ms = time_steps(lambda i: sda.build_tail_proxies(K, V, cid, w.C, ws=ws_b, with_sumK2=True), 3, 1,
+                           graph=False)
+    st = sda.build_tail_proxies(K, V, cid, w.C, ws=ws_b, with_sumK2=True)
+    ws_c = torch.empty(sda.workspace_bytes(sda.make_dims(K, w.Hq), sda.OP_BUILD_QGS), dtype=torch.uint8, device=dev)
+    cbuild_ms = time_steps(lambda i: sda.build_qgs_codes(K, U, ws=ws_c), 3, 1, graph=False)
+    qc = sda.build_qgs_codes(K, U, ws=ws_c)
+    del V
+    ncopy = 2
+    copies = [(qc, cid)] + [(sda.QgsCodes(U=U, codes=qc.codes.clone(), kmax=qc.kmax), cid.clone())
+                            for _ in range(ncopy - 1)]
+    units = w.B * w.Hkv
+    outs = (torch.empty((w.B, w.Hkv, w.m), dtype=torch.int32, device=dev),
+            torch.empty((w.B, w.Hkv), dtype=torch.int32, device=dev),
+            torch.empty((w.B, w.Hkv, w.m), dtype=torch.int32, device=dev))
+    ws = torch.empty(sda.workspace_bytes(sda.make_dims(K, w.Hq), sda.OP_SELECT_QGS, C=w.C), dtype=torch.uint8,
+                     device=dev)
+    ms_s = time_steps(lambda i: sda.select_qgs(q, K, copies[i % ncopy][1], st, copies[i % ncopy][0], w.n_sink,
+                                               w.n_local, w.n_top, out=outs, ws=ws), 50, 5, graph=not a.no_graph)
+    per_unit = (w.n * (w.r + 4) + w.C * (4 + 2 * w.d * 4) + w.d * w.r * 4 + w.r * 8 + w.m * 8 + 4)
+    by = units * per_unit + w.B * w.Hq * w.d * w.elem_bytes
+    out["qgs_select_b32_n32k"] = {"us_per_step": round(ms_s * 1e3, 2), "bytes_per_step": by,
+                                  "gbs": round(by / (ms_s * 1e-3) / 1e9, 1),
+                                  "frac_hbm_peak": round(by / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                  "rows_scored": units * w.n, "rows_picked": units * w.n_top,
+                                  "build_codes_us": round(cbuild_ms * 1e3, 1),
+                                  "build_proxies_with_sq_us": round(pbuild_ms * 1e3, 1)}
     return out
 
 
