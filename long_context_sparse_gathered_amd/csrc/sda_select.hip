@@ -53,8 +53,10 @@ __device__ __forceinline__ double wave_max_f64(double v) {
 // Build: projections y_j = U^T k_j and their int8 codes.  Pass 1 (QUANT =
 // false) writes each (unit, chunk)'s maxima of |y_i|; pass 2 recomputes the
 // projections, takes kmax_i as the maximum over the unit's chunks and writes
-// code_ji = rint(127 y_ji / kmax_i).  One thread per row; the basis sits in
-// LDS in fp64 and every lane reads the same entry (broadcast).
+// code_ji = rint(127 y_ji / kmax_i).  The basis sits in LDS in fp64.  A lane
+// owns 4 rows x 8 coordinates (lane & 3 picks the coordinates), so every
+// basis entry read from LDS serves four rows; each (row, coordinate) sum runs
+// over d in order.
 template <typename T, bool QUANT>
 __global__ __launch_bounds__(256) void qgs_code_kernel(const QgsBuildParams p) {
   __shared__ double s_u[kD * kQgsRank];
@@ -64,6 +66,7 @@ __global__ __launch_bounds__(256) void qgs_code_kernel(const QgsBuildParams p) {
   const int ch = blockIdx.x - u * p.chunks;
   const int s = u / p.Hkv, g = u - s * p.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int cg = tid & 3, rg = tid >> 2;    // coordinates 8cg..8cg+7, rows 4rg..4rg+3 of the chunk
 
   const float* Uu = p.U + (int64_t)u * kD * kQgsRank;
   for (int i = tid; i < kD * kQgsRank; i += 256) s_u[i] = (double)Uu[i];
@@ -75,32 +78,48 @@ __global__ __launch_bounds__(256) void qgs_code_kernel(const QgsBuildParams p) {
   }
   __syncthreads();
 
-  const int j = ch * kQgsRows + tid;
-  const bool live = j < p.n;
-  const T* krow = reinterpret_cast<const T*>(p.K) + (int64_t)s * p.sb + (int64_t)g * p.sh +
-                  (int64_t)(live ? j : 0) * p.sn;
-  double acc[kQgsRank];
+  const int j0 = ch * kQgsRows + 4 * rg;
+  const T* kbase = reinterpret_cast<const T*>(p.K) + (int64_t)s * p.sb + (int64_t)g * p.sh;
+  const T* krow[4];
 #pragma unroll
-  for (int i = 0; i < kQgsRank; ++i) acc[i] = 0.0;
+  for (int r = 0; r < 4; ++r) krow[r] = kbase + (int64_t)min(j0 + r, p.n - 1) * p.sn;
+  double acc[4][8];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[r][i] = 0.0;
   for (int d0 = 0; d0 < kD; d0 += 8) {
-    RowChunk<T> c;
-    c.load_cached(krow + d0);
-    float kf[8];
-    c.unpack(kf);
+    float kf[4][8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      RowChunk<T> c;
+      c.load_cached(krow[r] + d0);
+      c.unpack(kf[r]);
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const double kd = (double)kf[e];
-      const double* ur = &s_u[(d0 + e) * kQgsRank];
+      const double* ur = &s_u[(d0 + e) * kQgsRank + 8 * cg];
+      double uv[8];
 #pragma unroll
-      for (int i = 0; i < kQgsRank; ++i) acc[i] = fma(kd, ur[i], acc[i]);  // exact product: one rounding
+      for (int i = 0; i < 8; ++i) uv[i] = ur[i];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const double kd = (double)kf[r][e];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[r][i] = fma(kd, uv[i], acc[r][i]);  // exact product: one rounding
+      }
     }
   }
 
   if constexpr (!QUANT) {
 #pragma unroll
-    for (int i = 0; i < kQgsRank; ++i) {
-      const double v = wave_max_f64(live ? fabs(acc[i]) : 0.0);
-      if (lane == 0) s_max[w][i] = v;
+    for (int i = 0; i < 8; ++i) {
+      double v = 0.0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v = fmax(v, j0 + r < p.n ? fabs(acc[r][i]) : 0.0);
+#pragma unroll
+      for (int off = 4; off < 64; off <<= 1) v = fmax(v, __shfl_xor(v, off, 64));
+      if (lane < 4) s_max[w][8 * lane + i] = v;
     }
     __syncthreads();
     if (tid < kQgsRank) {
@@ -108,23 +127,18 @@ __global__ __launch_bounds__(256) void qgs_code_kernel(const QgsBuildParams p) {
       p.part[((int64_t)u * p.chunks + ch) * kQgsRank + tid] = m;
     }
   } else {
-    if (live) {
-      uint32_t packed[kQgsRank / 4];
 #pragma unroll
-      for (int k = 0; k < kQgsRank / 4; ++k) {
-        uint32_t word = 0;
+    for (int r = 0; r < 4; ++r) {
+      if (j0 + r >= p.n) break;
+      uint32_t word[2] = {0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = 4 * k + e;
-          const double km = s_kmax[i];
-          const int code = km > 0.0 ? (int)rint((acc[i] * 127.0) / km) : 0;
-          word |= ((uint32_t)code & 0xffu) << (8 * e);
-        }
-        packed[k] = word;
+      for (int i = 0; i < 8; ++i) {
+        const double km = s_kmax[8 * cg + i];
+        const int code = km > 0.0 ? (int)rint((acc[r][i] * 127.0) / km) : 0;
+        word[i >> 2] |= ((uint32_t)code & 0xffu) << (8 * (i & 3));
       }
-      uint4* dst = reinterpret_cast<uint4*>(p.codes + ((int64_t)u * p.n + j) * kQgsRank);
-      dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+      *reinterpret_cast<uint2*>(p.codes + ((int64_t)u * p.n + j0 + r) * kQgsRank + 8 * cg) =
+          make_uint2(word[0], word[1]);
     }
   }
 }
@@ -215,13 +229,34 @@ __device__ void prep_unit(const QgsSelectParams& p, int u, PrepLds& L, float* su
     }
   }
   for (int c = tid; c < C; c += nt) L.loc[c] = 0;
+  // cluster ids of the always-read sink and local window (counted below)
+  const int32_t* cidu = p.cid + (int64_t)u * p.n;
+  const int sink_end = min(p.n_sink, p.n);
+  const int loc_begin = max(sink_end, p.n - p.n_local);
+  const int nfix = sink_end + (p.n - loc_begin);
+  int fixc[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int t = tid + k * nt;
+    const int j = t < sink_end ? t : loc_begin + (t - sink_end);
+    fixc[k] = t < nfix ? cidu[j] : -1;
+  }
   __syncthreads();
 
   // query weights (unscaled) and the clusters' logit moments
   for (int t = tid; t < G * kQgsRank; t += nt) {
     const int h = t / kQgsRank, i = t - h * kQgsRank;
     double acc = 0.0;
-    for (int d = 0; d < kD; ++d) acc = fma((double)L.qf[h][d], (double)L.u[d * kQgsRank + i], acc);
+    for (int d0 = 0; d0 < kD; d0 += 16) {
+      float qv[16], uv[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        qv[e] = L.qf[h][d0 + e];
+        uv[e] = L.u[(d0 + e) * kQgsRank + i];
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc = fma((double)qv[e], (double)uv[e], acc);  // in dimension order
+    }
     L.w[h][i] = acc * km[i];
   }
   // Logit moments: four lanes per (cluster, head), 32 dimensions each, the
@@ -237,6 +272,7 @@ __device__ void prep_unit(const QgsSelectParams& p, int u, PrepLds& L, float* su
     const double inv = N > 0 ? 1.0 / (double)N : 0.0;
     double zb = 0.0, v2 = 0.0;
     if (N > 0) {
+#pragma unroll 8
       for (int d = 32 * part; d < 32 * part + 32; ++d) {
         const double qd = (double)L.qf[h][d];
         const double mu = (double)sk[b * kD + d] * inv;
@@ -265,16 +301,13 @@ __device__ void prep_unit(const QgsSelectParams& p, int u, PrepLds& L, float* su
     }
   }
   // members of each cluster inside the always-read sink and local window
-  {
-    const int32_t* cid = p.cid + (int64_t)u * p.n;
-    const int sink_end = min(p.n_sink, p.n);
-    const int loc_begin = max(sink_end, p.n - p.n_local);
-    const int nfix = sink_end + (p.n - loc_begin);
-    for (int t = tid; t < nfix; t += nt) {
-      const int j = t < sink_end ? t : loc_begin + (t - sink_end);
-      const int c = cid[j];
-      if (c >= 0 && c < C) atomicAdd(&L.loc[c], 1);
-    }
+#pragma unroll
+  for (int k = 0; k < 2; ++k)
+    if (fixc[k] >= 0 && fixc[k] < C) atomicAdd(&L.loc[fixc[k]], 1);
+  for (int t = tid + 2 * nt; t < nfix; t += nt) {
+    const int j = t < sink_end ? t : loc_begin + (t - sink_end);
+    const int c = cidu[j];
+    if (c >= 0 && c < C) atomicAdd(&L.loc[c], 1);
   }
   __syncthreads();
   // wave h < G: the head's largest cluster weight exponent M_h (lane b holds
@@ -667,15 +700,20 @@ __global__ __launch_bounds__(kSelThreads) void qgs_select_kernel(const QgsSelect
 constexpr int kFusedMaxN = 32768;
 constexpr int kFusedMaxC = 32;
 
-constexpr int kFusedSel = 2048;   // picked rows collected in LDS before they are ordered
+constexpr int kFusedSel = 1024;    // picked rows collected in LDS before they are ordered
+constexpr int kFusedCand = 1024;   // rows on a pending cluster's boundary after two digits
 
 struct FusedState {
   SelState sel;
   uint32_t wq[kQgsMaxG][kQgsRank / 4];
   int budget[kCmax];
   int avail[kCmax];
-  int nsel;
+  int match[kCmax];
+  int thrA[kCmax];
+  int thrB[kCmax];
+  int nsel, ncand;
   int picked[kFusedSel];
+  int cand[kFusedCand];
 };
 
 // LDS layout: [0, big) records or (first part) PrepLds + sums; then the
@@ -754,10 +792,101 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
   if (bad) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
   __syncthreads();
 
-  for (int pass = 0; pass < 6; ++pass) {
-    int top, shift, width;
-    pass_digits(pass, top, shift, width);
-    if (pass > 0) {
+  // pass 0: its histograms came with the scores (key bits [33, 40) = S20 >> 13)
+  sel_resolve(S, hist, C, 33);
+  __syncthreads();
+
+  // pass 1: key bits [26, 33) = (S20 >> 6) & 127 of the rows in each pending
+  // cluster's boundary digit; 32-bit arithmetic on the records
+  if (tid < C) F.match[tid] = S.done[tid] ? -1 : (int)(S.pref[tid] >> 33);
+  for (int i = tid; i < C * 128; i += kSelThreads) hist[i] = 0;
+  __syncthreads();
+  for (int j0 = tid; j0 < n; j0 += 8 * kSelThreads) {
+    uint32_t rr[8];
+    int mt[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) rr[k] = rec[min(j0 + k * kSelThreads, n - 1)];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int c = (int)((rr[k] >> 20) & 127);
+      mt[k] = F.match[c < C ? c : 0];
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t r = rr[k], s20 = r & 0xfffffu;
+      const bool hit = (j0 + k * kSelThreads < n) & ((r >> 27) & 1) & ((int)(s20 >> 13) == mt[k]);
+      if (hit) atomicAdd(&hist[(int)((r >> 20) & 127) * 128 + (int)((s20 >> 6) & 127)], 1);
+    }
+  }
+  __syncthreads();
+  sel_resolve(S, hist, C, 26);
+  __syncthreads();
+
+  // Classify the rows between sink and local window once: a row of a done
+  // cluster is picked when S20 >= A_c (its threshold's score part; those
+  // thresholds have zero position bits); for a pending cluster, a row above
+  // its boundary (S20 >> 6 > P_c) is picked and a row on it (== P_c) is a
+  // candidate for the remaining digits.
+  const int lane = tid & 63, w = tid >> 6;
+  if (tid < C) {
+    if (S.done[tid]) {
+      F.thrA[tid] = (int)(S.T[tid] >> 20);
+      F.thrB[tid] = -1;
+    } else {
+      const int P = (int)(S.pref[tid] >> 26);
+      F.thrA[tid] = (P + 1) << 6;
+      F.thrB[tid] = P;
+    }
+  }
+  if (tid == 0) {
+    F.nsel = 0;
+    F.ncand = 0;
+  }
+  __syncthreads();
+  auto push = [&](bool on, int* cnt, int* list, int cap, int j) {
+    const uint64_t bal = __ballot(on);
+    if (bal) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(cnt, __popcll(bal));
+      base = __shfl(base, 0, 64);
+      const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      if (on && pos < cap) list[pos] = j;
+    }
+  };
+  {
+    const int mid = max(0, hi - lo);
+    const int span = ((mid + 7) / 8 + 63) / 64 * 64;
+    const int r0 = lo + w * span, r1 = min(hi, r0 + span);
+    for (int j0 = r0; j0 < r1; j0 += 512) {
+      uint32_t rr[8];
+      int ta[8], tb[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) rr[k] = rec[min(j0 + 64 * k + lane, r1 - 1)];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int c = (int)((rr[k] >> 20) & 127);
+        ta[k] = F.thrA[c < C ? c : 0];
+        tb[k] = F.thrB[c < C ? c : 0];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = j0 + 64 * k + lane;
+        const int s20 = (int)(rr[k] & 0xfffffu);
+        const bool el = (j < r1) & ((rr[k] >> 27) & 1);
+        push(el & (s20 >= ta[k]), &F.nsel, F.picked, kFusedSel, j);
+        push(el & ((s20 >> 6) == tb[k]), &F.ncand, F.cand, kFusedCand, j);
+      }
+    }
+  }
+  __syncthreads();
+
+  if (F.ncand > kFusedCand || F.nsel > kFusedSel) {
+    // too many rows for the LDS lists: the remaining digits over all rows,
+    // then the ordered emission by scans
+    for (int pass = 2; pass < 6; ++pass) {
+      int top, shift, width;
+      pass_digits(pass, top, shift, width);
       if (tid < 64) {
         const int left = __popcll(__ballot(tid < C && !S.done[tid]));
         if (tid == 0) S.left = left;
@@ -765,77 +894,17 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
       for (int i = tid; i < C * 128; i += kSelThreads) hist[i] = 0;
       __syncthreads();
       if (S.left == 0) break;
-      for (int j0 = tid; j0 < n; j0 += 8 * kSelThreads) {
-        uint32_t rr[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int j = j0 + k * kSelThreads;
-          rr[k] = j < n ? rec[j] : 0u;
-        }
-        int dn[8];
-        uint64_t pf[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int c = (int)((rr[k] >> 20) & 127);
-          const int cs = c < C ? c : 0;
-          dn[k] = S.done[cs];
-          pf[k] = S.pref[cs];
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const uint32_t r = rr[k];
-          const int c = (int)((r >> 20) & 127);
-          const uint64_t k40 = rec_key(r, j0 + k * kSelThreads);
-          const bool hit = ((r >> 27) & 1) & (dn[k] == 0) & ((k40 >> top) == (pf[k] >> top));
-          if (hit) atomicAdd(&hist[c * 128 + (int)((k40 >> shift) & ((1u << width) - 1))], 1);
-        }
+      for (int j = tid; j < n; j += kSelThreads) {
+        const uint32_t r = rec[j];
+        const int c = (int)((r >> 20) & 127);
+        const uint64_t k40 = rec_key(r, j);
+        const bool hit = ((r >> 27) & 1) && !S.done[c] && (k40 >> top) == (S.pref[c] >> top);
+        if (hit) atomicAdd(&hist[c * 128 + (int)((k40 >> shift) & ((1u << width) - 1))], 1);
       }
       __syncthreads();
+      sel_resolve(S, hist, C, shift);
+      __syncthreads();
     }
-    sel_resolve(S, hist, C, shift);
-    __syncthreads();
-  }
-
-  // The listed rows are the sink, the picked rows (all inside
-  // [n_sink, n - n_local)) and the local window, in that position order:
-  // collect the picked rows in any order, then place each by its rank.
-  const int lane = tid & 63, w = tid >> 6;
-  if (tid == 0) F.nsel = 0;
-  __syncthreads();
-  {
-    const int mid = max(0, hi - lo);
-    const int span = ((mid + 7) / 8 + 63) / 64 * 64;
-    const int r0 = lo + w * span, r1 = min(hi, r0 + span);
-    for (int j0 = r0; j0 < r1; j0 += 512) {
-      uint32_t rr[8];
-      uint64_t th[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) rr[k] = rec[min(j0 + 64 * k + lane, r1 - 1)];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int c = (int)((rr[k] >> 20) & 127);
-        th[k] = S.T[c < C ? c : 0];
-      }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int j = j0 + 64 * k + lane;
-        const bool on = (j < r1) & ((rr[k] >> 27) & 1) & (rec_key(rr[k], j) >= th[k]);
-        const uint64_t bal = __ballot(on);
-        if (bal) {
-          int base = 0;
-          if (lane == 0) base = atomicAdd(&F.nsel, __popcll(bal));
-          base = __shfl(base, 0, 64);
-          const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                               __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
-          if (on && pos < kFusedSel) F.picked[pos] = j;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  const int nsel = F.nsel;
-  if (nsel > kFusedSel) {
-    // more picked rows than the collection holds: ordered emission by scans
     emit_listed(p, u, S, [&](int j, bool& el, int& c, uint64_t& k40) {
       const uint32_t r = rec[j];
       el = (r >> 27) & 1;
@@ -844,6 +913,58 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
     });
     return;
   }
+
+  // the remaining digits over the candidates only
+  const int ncand = F.ncand;
+  for (int pass = 2; pass < 6; ++pass) {
+    int top, shift, width;
+    pass_digits(pass, top, shift, width);
+    if (tid < 64) {
+      const int left = __popcll(__ballot(tid < C && !S.done[tid]));
+      if (tid == 0) S.left = left;
+    }
+    for (int i = tid; i < C * 128; i += kSelThreads) hist[i] = 0;
+    __syncthreads();
+    if (S.left == 0) break;
+    for (int t = tid; t < ncand; t += kSelThreads) {
+      const int j = F.cand[t];
+      const uint32_t r = rec[j];
+      const int c = (int)((r >> 20) & 127);
+      const uint64_t k40 = rec_key(r, j);
+      if (!S.done[c] && (k40 >> top) == (S.pref[c] >> top))
+        atomicAdd(&hist[c * 128 + (int)((k40 >> shift) & ((1u << width) - 1))], 1);
+    }
+    __syncthreads();
+    sel_resolve(S, hist, C, shift);
+    __syncthreads();
+  }
+  for (int t0 = 0; t0 < ncand; t0 += kSelThreads) {
+    const int t = t0 + tid;
+    int j = 0;
+    bool on = false;
+    if (t < ncand) {
+      j = F.cand[t];
+      const uint32_t r = rec[j];
+      const int c = (int)((r >> 20) & 127);
+      on = rec_key(r, j) >= S.T[c];
+    }
+    push(on, &F.nsel, F.picked, kFusedSel, j);
+  }
+  __syncthreads();
+  const int nsel = F.nsel;
+  if (nsel > kFusedSel) {
+    emit_listed(p, u, S, [&](int j, bool& el, int& c, uint64_t& k40) {
+      const uint32_t r = rec[j];
+      el = (r >> 27) & 1;
+      c = (int)((r >> 20) & 127);
+      k40 = rec_key(r, j);
+    });
+    return;
+  }
+
+  // The listed rows are the sink, the picked rows (all inside
+  // [n_sink, n - n_local)) and the local window, in that position order:
+  // each picked row goes to its rank among the picked.
   const int sink_end = min(lo, n);
   const int loc_begin = max(sink_end, hi);
   const int total = sink_end + nsel + (n - loc_begin);
