@@ -50,16 +50,20 @@ __device__ __forceinline__ double wave_max_f64(double v) {
 }
 
 // ---------------------------------------------------------------------------
-// Build: projections y_j = U^T k_j and their int8 codes.  Pass 1 (QUANT =
-// false) writes each (unit, chunk)'s maxima of |y_i|; pass 2 recomputes the
-// projections, takes kmax_i as the maximum over the unit's chunks and writes
-// code_ji = rint(127 y_ji / kmax_i).  The basis sits in LDS in fp64.  A lane
-// owns 4 rows x 8 coordinates (lane & 3 picks the coordinates), so every
-// basis entry read from LDS serves four rows; each (row, coordinate) sum runs
-// over d in order.
+// Build: projections y_j = U^T k_j and their int8 codes, in three launches:
+// pass 1 (QUANT = false) writes each (unit, chunk)'s maxima of |y_i|; a small
+// kernel reduces them to kmax_i per unit; pass 2 recomputes the projections
+// and writes code_ji = rint(127 y_ji / kmax_i).  The basis sits in LDS in
+// fp64; the chunk's keys pass through LDS 32 dimensions at a time (read from
+// HBM once, coalesced).  A lane owns 4 rows x 8 coordinates (lane & 3 picks
+// the coordinates), so every LDS read serves several products; each
+// (row, coordinate) sum runs over d in order.
+constexpr int kCodeDims = 32;   // key dimensions staged per step
+
 template <typename T, bool QUANT>
 __global__ __launch_bounds__(256) void qgs_code_kernel(const QgsBuildParams p) {
   __shared__ double s_u[kD * kQgsRank];
+  __shared__ float s_k[kQgsRows][kCodeDims + 1];   // +1: the four rows of a lane group hit different banks
   __shared__ double s_max[4][kQgsRank];
   __shared__ double s_kmax[kQgsRank];
   const int u = blockIdx.x / p.chunks;
@@ -70,47 +74,47 @@ __global__ __launch_bounds__(256) void qgs_code_kernel(const QgsBuildParams p) {
 
   const float* Uu = p.U + (int64_t)u * kD * kQgsRank;
   for (int i = tid; i < kD * kQgsRank; i += 256) s_u[i] = (double)Uu[i];
-  if (QUANT && tid < kQgsRank) {
-    double m = 0.0;
-    for (int c = 0; c < p.chunks; ++c) m = fmax(m, p.part[((int64_t)u * p.chunks + c) * kQgsRank + tid]);
-    s_kmax[tid] = m;
-    if (ch == 0) p.kmax[(int64_t)u * kQgsRank + tid] = m;
-  }
-  __syncthreads();
+  if (QUANT && tid < kQgsRank) s_kmax[tid] = p.kmax[(int64_t)u * kQgsRank + tid];
 
-  const int j0 = ch * kQgsRows + 4 * rg;
+  const int row0 = ch * kQgsRows;
   const T* kbase = reinterpret_cast<const T*>(p.K) + (int64_t)s * p.sb + (int64_t)g * p.sh;
-  const T* krow[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) krow[r] = kbase + (int64_t)min(j0 + r, p.n - 1) * p.sn;
   double acc[4][8];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[r][i] = 0.0;
-  for (int d0 = 0; d0 < kD; d0 += 8) {
-    float kf[4][8];
+  for (int d0 = 0; d0 < kD; d0 += kCodeDims) {
+    __syncthreads();   // the previous step's keys are consumed (and the basis is in place)
+    // 256 rows x 32 dims: four lanes per row, 8 elements each, in 4 sweeps of 64 rows
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int sw = 0; sw < 4; ++sw) {
+      const int rr = sw * 64 + (tid >> 2);
+      const int part = tid & 3;
+      const int j = min(row0 + rr, p.n - 1);
       RowChunk<T> c;
-      c.load_cached(krow[r] + d0);
-      c.unpack(kf[r]);
-    }
+      c.load_cached(kbase + (int64_t)j * p.sn + d0 + 8 * part);
+      float f[8];
+      c.unpack(f);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 8; ++e) s_k[rr][8 * part + e] = f[e];
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int e = 0; e < kCodeDims; ++e) {
       const double* ur = &s_u[(d0 + e) * kQgsRank + 8 * cg];
       double uv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) uv[i] = ur[i];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const double kd = (double)kf[r][e];
+        const double kd = (double)s_k[4 * rg + r][e];
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[r][i] = fma(kd, uv[i], acc[r][i]);  // exact product: one rounding
       }
     }
   }
 
+  const int j0 = row0 + 4 * rg;
   if constexpr (!QUANT) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -143,17 +147,30 @@ __global__ __launch_bounds__(256) void qgs_code_kernel(const QgsBuildParams p) {
   }
 }
 
+// kmax_i of each unit: the maximum over its chunks.
+__global__ __launch_bounds__(64) void qgs_kmax_kernel(const QgsBuildParams p) {
+  const int u = blockIdx.x, i = threadIdx.x;
+  if (i >= kQgsRank) return;
+  double m = 0.0;
+  for (int c = 0; c < p.chunks; ++c) m = fmax(m, p.part[((int64_t)u * p.chunks + c) * kQgsRank + i]);
+  p.kmax[(int64_t)u * kQgsRank + i] = m;
+}
+
 hipError_t launch_qgs_build(const QgsBuildParams& p, int dtype, int units, hipStream_t st) {
   const dim3 grid(units * p.chunks), block(256);
   if (dtype == SDA_BF16) {
     hipLaunchKernelGGL((qgs_code_kernel<bf16_t, false>), grid, block, 0, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((qgs_code_kernel<bf16_t, true>), grid, block, 0, st, p);
   } else {
     hipLaunchKernelGGL((qgs_code_kernel<float, false>), grid, block, 0, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(qgs_kmax_kernel, dim3(units), dim3(64), 0, st, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (dtype == SDA_BF16) {
+    hipLaunchKernelGGL((qgs_code_kernel<bf16_t, true>), grid, block, 0, st, p);
+  } else {
     hipLaunchKernelGGL((qgs_code_kernel<float, true>), grid, block, 0, st, p);
   }
   return hipGetLastError();
