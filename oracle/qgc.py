@@ -20,14 +20,19 @@ notes):
       product of a bf16/fp32 element and an fp32 basis entry is exact), then
       held in fixed point: zq_j = rint(z_j * 2^16) as an integer (round half
       to even).  Integer coordinates make every centroid sum exact.
-  G3  k-means (Lloyd's iteration) on zq with C centroids.  Start: centroid k
-      is the point of row floor((2k + 1) n / (2C)).  One iteration: each row
-      goes to the centroid at the smallest squared distance
-      sum_i (zq_i - c_ki)^2 (fp64, coordinates in order, no fused
-      multiply-add; ties to the lower k); each centroid becomes the mean of
-      its rows (exact integer sum, one fp64 division per coordinate); a
+  G3  k-means (Lloyd's iteration) on zq with C centroids held in the same
+      fixed point as the points.  Start: centroid k is the point of row
+      floor((2k + 1) n / (2C)).  One iteration: each row goes to the centroid
+      at the smallest squared distance sum_i (zq_i - c_ki)^2 (ties to the
+      lower k); each centroid becomes its rows' mean rounded to the grid,
+      rint(S / N) with S the exact integer sum (round half to even); a
       centroid with no rows stays where it is.  T iterations (default 10),
       stopping early once no row changes its centroid (a fixed point).
+      Points and centroids are integers below 2^21, so every distance is an
+      integer below 2^48 and exact in fp64 in any order; and fp64(S)/fp64(N)
+      rounds to the same integer as the exact S/N (an exact quotient that is
+      not a half-integer lies at least 1/(2N) from one, far above the
+      division's rounding error).
   G4  The cluster id of a row is its final centroid.  The per-cluster state
       (count, key sum, value sum, squared-key sum) is then the proxy
       builder's, over these ids.
@@ -64,8 +69,7 @@ def init_centroids(zq, C) -> np.ndarray:
 
 
 def sq_distances(zq, cent) -> np.ndarray:
-    """[n, C] squared distances, summed over the coordinates in order (fp64,
-    one rounding per subtraction, product and addition)."""
+    """[n, C] squared distances (integers below 2^48: exact in fp64)."""
     zf = zq.astype(np.float64)
     D = np.zeros((zq.shape[0], cent.shape[0]))
     for i in range(zq.shape[1]):
@@ -79,8 +83,8 @@ def assign(zq, cent) -> np.ndarray:
 
 
 def update(zq, a, cent) -> np.ndarray:
-    """Each centroid = exact integer sum of its rows / count (fp64 division);
-    empty centroids stay."""
+    """Each centroid = rint(exact integer sum of its rows / count); empty
+    centroids stay."""
     C, r = cent.shape
     new = cent.copy()
     for k in range(C):
@@ -88,7 +92,7 @@ def update(zq, a, cent) -> np.ndarray:
         cnt = int(m.sum())
         if cnt:
             s = zq[m].sum(axis=0)          # int64, exact
-            new[k] = s.astype(np.float64) / float(cnt)
+            new[k] = np.rint(s.astype(np.float64) / float(cnt))
     return new
 
 

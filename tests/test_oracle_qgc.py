@@ -50,13 +50,13 @@ def test_separated_blobs_recovered():
     np.testing.assert_array_equal(a, np.repeat(np.arange(C), per))
     assert it <= 2
     for k in range(C):
-        np.testing.assert_allclose(cent[k], zq[k * per:(k + 1) * per].mean(axis=0), rtol=0, atol=1e-9)
+        np.testing.assert_allclose(cent[k], zq[k * per:(k + 1) * per].mean(axis=0), rtol=0, atol=0.5)
 
 
 def test_fixed_point_properties_exact():
-    """G3 at convergence: every centroid is the correctly rounded mean of its
-    rows (exact rational sum, one rounding), and every sampled row sits at a
-    centroid of least exact squared distance."""
+    """G3 at convergence: every centroid is its rows' exact mean rounded half
+    to even to the integer grid (rational arithmetic), and every sampled row
+    sits at a centroid of least exact squared distance."""
     rng = np.random.default_rng(2)
     zq = rng.integers(-200000, 200000, size=(600, 16)).astype(np.int64)
     zq[:300] += 300000
@@ -66,7 +66,7 @@ def test_fixed_point_properties_exact():
         rows = zq[a == k]
         if len(rows):
             for i in range(16):
-                assert cent[k, i] == float(Fraction(int(rows[:, i].sum()), len(rows)))
+                assert cent[k, i] == float(round(Fraction(int(rows[:, i].sum()), len(rows))))
     cf = [[Fraction(float(x)) for x in c] for c in cent]
     for j in rng.choice(600, size=40, replace=False):
         d = [sum((Fraction(int(zq[j, i])) - cf[k][i]) ** 2 for i in range(16)) for k in range(6)]
@@ -74,6 +74,9 @@ def test_fixed_point_properties_exact():
 
 
 def test_objective_never_increases():
+    """Lloyd's objective does not increase from one iteration to the next,
+    up to the grid rounding of the centroids (each coordinate of a centroid
+    moves at most 1/2 from the exact mean: at most 16 * 1/4 per row)."""
     rng = np.random.default_rng(3)
     zq = np.rint(rng.standard_normal((400, 16)) * 5e4).astype(np.int64)
     prev = None
@@ -81,7 +84,7 @@ def test_objective_never_increases():
         a, cent, _ = qgc.kmeans(zq, 5, T=T)
         obj = qgc.objective(zq, a, cent)
         if prev is not None:
-            assert obj <= prev * (1 + 1e-12)
+            assert obj <= prev + 4 * len(zq)
         prev = obj
 
 
