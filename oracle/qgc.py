@@ -18,8 +18,10 @@ notes):
       16 columns of the query subspace basis the selector uses.
   G2  Projection z_j = V^T k_j, summed over d in index order in fp64 (every
       product of a bf16/fp32 element and an fp32 basis entry is exact), then
-      held in fixed point: zq_j = rint(z_j * 2^16) as an integer (round half
-      to even).  Integer coordinates make every centroid sum exact.
+      held in fixed point: zq_j = rint(z_j * 2^12) as an integer (round half
+      to even), clamped to |zq| <= 2^23 - 1 (|z| < 2048; larger projections
+      are flagged on the GPU).  Integer coordinates make every centroid sum
+      exact.
   G3  k-means (Lloyd's iteration) on zq with C centroids held in the same
       fixed point as the points.  Start: centroid k is the point of row
       floor((2k + 1) n / (2C)).  One iteration: each row goes to the centroid
@@ -28,8 +30,8 @@ notes):
       rint(S / N) with S the exact integer sum (round half to even); a
       centroid with no rows stays where it is.  T iterations (default 10),
       stopping early once no row changes its centroid (a fixed point).
-      Points and centroids are integers below 2^21, so every distance is an
-      integer below 2^48 and exact in fp64 in any order; and fp64(S)/fp64(N)
+      Points and centroids are integers below 2^23, so every distance is an
+      integer below 2^52 and exact in fp64 in any order; and fp64(S)/fp64(N)
       rounds to the same integer as the exact S/N (an exact quotient that is
       not a half-integer lies at least 1/(2N) from one, far above the
       division's rounding error).
@@ -42,7 +44,8 @@ from __future__ import annotations
 import numpy as np
 
 R_QGC = 16          # projection rank (settings list)
-FIX_SCALE = 65536.0 # fixed-point scale of the projected coordinates
+FIX_SCALE = 4096.0  # fixed-point scale of the projected coordinates
+FIX_MAX = (1 << 23) - 1
 T_DEFAULT = 10
 
 
@@ -59,7 +62,7 @@ def project_fixed(K, V) -> np.ndarray:
     z = np.zeros((X.shape[0], Vv.shape[1]))
     for dd in range(X.shape[1]):
         z += X[:, dd:dd + 1] * Vv[dd][None, :]
-    return np.rint(z * FIX_SCALE).astype(np.int64)
+    return np.clip(np.rint(z * FIX_SCALE), -FIX_MAX, FIX_MAX).astype(np.int64)
 
 
 def init_centroids(zq, C) -> np.ndarray:
@@ -69,7 +72,7 @@ def init_centroids(zq, C) -> np.ndarray:
 
 
 def sq_distances(zq, cent) -> np.ndarray:
-    """[n, C] squared distances (integers below 2^48: exact in fp64)."""
+    """[n, C] squared distances (integers below 2^52: exact in fp64)."""
     zf = zq.astype(np.float64)
     D = np.zeros((zq.shape[0], cent.shape[0]))
     for i in range(zq.shape[1]):

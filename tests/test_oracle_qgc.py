@@ -17,13 +17,14 @@ def _eye(d, r):
 
 
 def test_fixed_point_hand_example():
-    """G2: identity basis; 1.5 -> 98304; 2^-17 * 65536 = 0.5 -> 0 and
-    3 * 2^-17 * 65536 = 1.5 -> 2 (half to even); -2.25 -> -147456."""
-    K = np.zeros((4, 32), np.float32)
-    K[:, 0] = [1.5, 2.0 ** -17, 3 * 2.0 ** -17, -2.25]
+    """G2: identity basis; 1.5 -> 6144; 2^-13 * 4096 = 0.5 -> 0 and
+    3 * 2^-13 * 4096 = 1.5 -> 2 (half to even); -2.25 -> -9216; 3000 is
+    clamped to 2^23 - 1."""
+    K = np.zeros((5, 32), np.float32)
+    K[:, 0] = [1.5, 2.0 ** -13, 3 * 2.0 ** -13, -2.25, 3000.0]
     K[:, 20] = 7.0                              # outside the 16 coordinates
     zq = qgc.project_fixed(K, _eye(32, 16))
-    np.testing.assert_array_equal(zq[:, 0], [98304, 0, 2, -147456])
+    np.testing.assert_array_equal(zq[:, 0], [6144, 0, 2, -9216, (1 << 23) - 1])
     assert (zq[:, 1:] == 0).all() and zq.dtype == np.int64
 
 
@@ -35,7 +36,7 @@ def test_projection_against_exact_sum():
     for j in range(10):
         for i in range(16):
             exact = math.fsum(float(K[j, t]) * float(V[t, i]) for t in range(128))
-            assert abs(zq[j, i] - exact * 65536.0) <= 0.5 + 1e-6
+            assert abs(zq[j, i] - exact * 4096.0) <= 0.5 + 1e-9
 
 
 def test_separated_blobs_recovered():
