@@ -162,7 +162,8 @@ typedef enum {
   SDA_OP_BUILD_PROXIES = 2,
   SDA_OP_BUILD_PRIOR = 3,
   SDA_OP_BUILD_QGS = 4,
-  SDA_OP_SELECT_QGS = 5
+  SDA_OP_SELECT_QGS = 5,
+  SDA_OP_BUILD_QGC = 6
 } sda_op;
 
 /* Workspace bytes an entry point needs for these sizes (m: entries per unit
@@ -222,6 +223,29 @@ const char* sda_status_str(int32_t status);
 
 /* Library version, "major.minor.patch". */
 const char* sda_version(void);
+
+/* ---- Query-geometry clustering of the keys ------------------------------
+ * (OpenAttention, method stage 01 and the settings list: the keys, projected
+ * on the top 16 query eigenvectors, are clustered with k-means; C = 64.)
+ * Once per request; the ids then feed sda_build_tail_proxies and
+ * sda_select_qgs.  Per unit:
+ *   - V [B,Hkv,d,16] fp32: the projection basis (orthonormal columns; the
+ *     leading 16 columns of the selector's basis);
+ *   - fixed-point coordinates zq_j = rint(4096 * V^T k_j), the projection
+ *     summed over d in order in fp64 (exact products), clamped to
+ *     |zq| <= 2^23 - 1 (a clamp sets SDA_FLAG_CLUSTER);
+ *   - k-means with C centroids on the same integer grid: start at the points
+ *     of rows floor((2k + 1) n / (2C)); T passes of "each row to its nearest
+ *     centroid (squared distance, ties to the lower k), each centroid to its
+ *     rows' mean rounded half to even (an empty one stays)";
+ *   - cluster_id [B,Hkv,n] int32 = the centroid of each row after pass T.
+ * Distances and sums are exact integers, so the result does not depend on
+ * the order of the arithmetic.  C in [1, 64] (else SDA_EUNSUPPORTED),
+ * T in [1, 1000] (else SDA_EINVAL); K and V 16-byte aligned.  Workspace:
+ * SDA_OP_BUILD_QGC with this C (64 B per row of fixed-point coordinates). */
+sda_status sda_build_qgc_clusters(const sda_dims* dims, const void* K, const float* V, int32_t C,
+                                  int32_t T, int32_t* cluster_id, int32_t* dev_flags, void* ws,
+                                  size_t ws_bytes, void* stream);
 
 /* ---- Selector in front of the proxy decode ------------------------------
  * (OpenAttention, method stages 02-03 and the settings list: keys coded in

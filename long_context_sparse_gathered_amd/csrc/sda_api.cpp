@@ -12,6 +12,7 @@
 #include "sda.h"
 #include "sda_kernels.hpp"
 #include "sda_select.hpp"
+#include "sda_cluster.hpp"
 
 #define SDA_EXPORT extern "C" __attribute__((visibility("default")))
 
@@ -204,6 +205,21 @@ QgsSelectWs qgs_select_ws(const Resolved& r, int C) {
   return w;
 }
 
+struct QgcWs {
+  size_t zq, cent, sums, cnt, total;
+};
+
+QgcWs qgc_ws(const Resolved& r, int C) {
+  const size_t units = (size_t)r.B * r.Hkv;
+  QgcWs w;
+  w.zq = 0;
+  w.cent = align256(units * r.n * kQgcRank * sizeof(int32_t));
+  w.sums = w.cent + align256(units * C * kQgcRank * sizeof(double));
+  w.cnt = w.sums + align256(units * C * kQgcRank * sizeof(uint64_t));
+  w.total = w.cnt + align256(units * C * sizeof(int32_t));
+  return w;
+}
+
 void fill_common(const Resolved& r, AttnParams* p) {
   memset(p, 0, sizeof(*p));
   p->sb = r.sb;
@@ -253,6 +269,7 @@ SDA_EXPORT size_t sda_workspace_bytes(const sda_dims* dims, int32_t op, int32_t 
     case SDA_OP_BUILD_PROXIES: return (C >= 1 && C <= kCmax) ? proxy_ws(r, C) : 0;
     case SDA_OP_BUILD_QGS: return qgs_build_ws(r);
     case SDA_OP_SELECT_QGS: return (C >= 1 && C <= kCmax) ? qgs_select_ws(r, C).total : 0;
+    case SDA_OP_BUILD_QGC: return (C >= 1 && C <= kCmax) ? qgc_ws(r, C).total : 0;
   }
   return 0;
 }
@@ -519,4 +536,36 @@ SDA_EXPORT sda_status sda_select_qgs(const sda_dims* dims, const void* q, const 
   p.budget = budget;
   p.flags = dev_flags;
   return hip_status(launch_qgs_select(p, r.dtype, reinterpret_cast<hipStream_t>(stream)));
+}
+
+SDA_EXPORT sda_status sda_build_qgc_clusters(const sda_dims* dims, const void* K, const float* V, int32_t C,
+                                             int32_t T, int32_t* cluster_id, int32_t* dev_flags, void* ws,
+                                             size_t ws_bytes, void* stream) {
+  Resolved r;
+  sda_status st = resolve(dims, &r);
+  if (st != SDA_OK) return st;
+  if (!K || !V || !cluster_id) return SDA_EINVAL;
+  if (!aligned16(K) || !aligned16(V)) return SDA_EINVAL;
+  if (C < 1 || C > kCmax) return SDA_EUNSUPPORTED;
+  if (T < 1 || T > 1000) return SDA_EINVAL;
+  const QgcWs w = qgc_ws(r, C);
+  if (!ws || ws_bytes < w.total) return SDA_EWORKSPACE;
+  char* base = reinterpret_cast<char*>(ws);
+  QgcParams p;
+  memset(&p, 0, sizeof(p));
+  p.K = K;
+  p.V = V;
+  p.sb = r.sb;
+  p.sh = r.sh;
+  p.sn = r.sn;
+  p.Hkv = r.Hkv;
+  p.n = r.n;
+  p.C = C;
+  p.zq = reinterpret_cast<int32_t*>(base + w.zq);
+  p.cent = reinterpret_cast<double*>(base + w.cent);
+  p.sums = reinterpret_cast<unsigned long long*>(base + w.sums);
+  p.cnt = reinterpret_cast<int32_t*>(base + w.cnt);
+  p.cluster_id = cluster_id;
+  p.flags = dev_flags;
+  return hip_status(launch_qgc(p, r.dtype, r.B * r.Hkv, T, reinterpret_cast<hipStream_t>(stream)));
 }

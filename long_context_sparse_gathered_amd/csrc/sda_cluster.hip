@@ -1,0 +1,222 @@
+// sda_cluster.hip -- clustering of the keys in the query geometry
+// ("OpenAttention: One Percent Is Enough with Tail Proxies", stage 01 of the
+// method list and the settings list: keys projected on the top 16 query
+// eigenvectors are clustered with k-means, C = 64).
+//
+// Coordinates are fixed point: zq = rint(4096 * V^T k), the projection summed
+// over d in order in fp64 (exact products), clamped to |zq| < 2^23.  Centroids
+// live on the same integer grid (each is its rows' mean rounded half to
+// even), so every squared distance is an integer below 2^52 -- exact in fp64
+// whatever the order of the terms -- and the centroid sums are exact 64-bit
+// integer sums (atomics in any order give the same bits).  The k-means
+// trajectory is therefore reproducible bit for bit.
+#include <math.h>
+
+#include "sda_device.hpp"
+#include "sda_kernels.hpp"
+#include "sda_cluster.hpp"
+
+namespace sda {
+
+// Projection: a lane owns 4 rows x 4 coordinates (lane & 3 picks the
+// coordinates); keys pass through LDS 32 dimensions at a time.
+template <typename T>
+__global__ __launch_bounds__(256) void qgc_project_kernel(const QgcParams p) {
+  __shared__ double s_v[kD * kQgcRank];
+  __shared__ float s_k[kQgcRows][33];
+  const int u = blockIdx.x / qgc_chunks(p.n);
+  const int ch = blockIdx.x - u * qgc_chunks(p.n);
+  const int s = u / p.Hkv, g = u - s * p.Hkv;
+  const int tid = threadIdx.x;
+  const int cg = tid & 3, rg = tid >> 2;
+
+  const float* Vu = p.V + (int64_t)u * kD * kQgcRank;
+  for (int i = tid; i < kD * kQgcRank; i += 256) s_v[i] = (double)Vu[i];
+  const int row0 = ch * kQgcRows;
+  const T* kbase = reinterpret_cast<const T*>(p.K) + (int64_t)s * p.sb + (int64_t)g * p.sh;
+  double acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[r][i] = 0.0;
+  for (int d0 = 0; d0 < kD; d0 += 32) {
+    __syncthreads();
+#pragma unroll
+    for (int sw = 0; sw < 4; ++sw) {
+      const int rr = sw * 64 + (tid >> 2);
+      const int part = tid & 3;
+      const int j = min(row0 + rr, p.n - 1);
+      RowChunk<T> c;
+      c.load_cached(kbase + (int64_t)j * p.sn + d0 + 8 * part);
+      float f[8];
+      c.unpack(f);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_k[rr][8 * part + e] = f[e];
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int e = 0; e < 32; ++e) {
+      double uv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) uv[i] = s_v[(d0 + e) * kQgcRank + 4 * cg + i];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const double kd = (double)s_k[4 * rg + r][e];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[r][i] = fma(kd, uv[i], acc[r][i]);  // exact product: one rounding
+      }
+    }
+  }
+  bool bad = false;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int j = row0 + 4 * rg + r;
+    if (j >= p.n) break;
+    int zi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      double x = rint(acc[r][i] * kQgcScale);
+      if (fabs(x) > (double)kQgcMax) {
+        x = x > 0.0 ? (double)kQgcMax : -(double)kQgcMax;
+        bad = true;
+      }
+      zi[i] = (int)x;
+    }
+    *reinterpret_cast<int4*>(p.zq + ((int64_t)u * p.n + j) * kQgcRank + 4 * cg) = make_int4(zi[0], zi[1], zi[2], zi[3]);
+  }
+  if (bad) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
+}
+
+// Start: centroid k is the point of row floor((2k + 1) n / (2C)); sums and
+// counts cleared.
+__global__ __launch_bounds__(256) void qgc_init_kernel(const QgcParams p) {
+  const int u = blockIdx.x, C = p.C;
+  for (int t = threadIdx.x; t < C * kQgcRank; t += 256) {
+    const int k = t / kQgcRank, i = t - k * kQgcRank;
+    const int row = (int)(((int64_t)(2 * k + 1) * p.n) / (2 * C));
+    p.cent[(int64_t)u * C * kQgcRank + t] = (double)p.zq[((int64_t)u * p.n + row) * kQgcRank + i];
+    p.sums[(int64_t)u * C * kQgcRank + t] = 0ull;
+  }
+  for (int k = threadIdx.x; k < C; k += 256) p.cnt[(int64_t)u * C + k] = 0;
+}
+
+// One assignment pass: each row to its nearest centroid (ties to the lower
+// k), its coordinates added to that centroid's sums.  Two rows per thread
+// share each centroid read.
+__global__ __launch_bounds__(256) void qgc_assign_kernel(const QgcParams p) {
+  __shared__ double s_c[kCmax * kQgcRank];
+  __shared__ unsigned long long s_sum[kCmax * kQgcRank];
+  __shared__ int s_cnt[kCmax];
+  const int chunks = qgc_assign_chunks(p.n);
+  const int u = blockIdx.x / chunks;
+  const int ch = blockIdx.x - u * chunks;
+  const int C = p.C, tid = threadIdx.x;
+  for (int t = tid; t < C * kQgcRank; t += 256) {
+    s_c[t] = p.cent[(int64_t)u * C * kQgcRank + t];
+    s_sum[t] = 0ull;
+  }
+  for (int k = tid; k < C; k += 256) s_cnt[k] = 0;
+  __syncthreads();
+
+  constexpr int RW = 2;
+  int jr[RW];
+  int zi[RW][kQgcRank];
+  double z[RW][kQgcRank];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    jr[r] = ch * kQgcAssignRows + r * 256 + tid;
+    const int j = min(jr[r], p.n - 1);
+    const int4* src = reinterpret_cast<const int4*>(p.zq + ((int64_t)u * p.n + j) * kQgcRank);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int4 v = src[q4];
+      zi[r][4 * q4] = v.x;
+      zi[r][4 * q4 + 1] = v.y;
+      zi[r][4 * q4 + 2] = v.z;
+      zi[r][4 * q4 + 3] = v.w;
+    }
+#pragma unroll
+    for (int i = 0; i < kQgcRank; ++i) z[r][i] = (double)zi[r][i];
+  }
+  double best[RW];
+  int bk[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    best[r] = INFINITY;
+    bk[r] = 0;
+  }
+  for (int k = 0; k < C; ++k) {
+    double c[kQgcRank];
+#pragma unroll
+    for (int i = 0; i < kQgcRank; ++i) c[i] = s_c[k * kQgcRank + i];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+      double d = 0.0;
+#pragma unroll
+      for (int i = 0; i < kQgcRank; ++i) {
+        const double diff = z[r][i] - c[i];
+        d = fma(diff, diff, d);   // integers below 2^52: exact
+      }
+      if (d < best[r]) {
+        best[r] = d;
+        bk[r] = k;
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    if (jr[r] >= p.n) continue;
+    p.cluster_id[(int64_t)u * p.n + jr[r]] = bk[r];
+    atomicAdd(&s_cnt[bk[r]], 1);
+#pragma unroll
+    for (int i = 0; i < kQgcRank; ++i)
+      atomicAdd(&s_sum[bk[r] * kQgcRank + i], (unsigned long long)(long long)zi[r][i]);
+  }
+  __syncthreads();
+  for (int t = tid; t < C * kQgcRank; t += 256)
+    if (s_sum[t]) atomicAdd(&p.sums[(int64_t)u * C * kQgcRank + t], s_sum[t]);
+  for (int k = tid; k < C; k += 256)
+    if (s_cnt[k]) atomicAdd(&p.cnt[(int64_t)u * C + k], s_cnt[k]);
+}
+
+// Centroids = rint(sum / count) (fp64 quotient of two exact integers rounds
+// to the same integer as the exact quotient); empty centroids stay; sums and
+// counts cleared for the next pass.
+__global__ __launch_bounds__(256) void qgc_update_kernel(const QgcParams p) {
+  const int u = blockIdx.x, C = p.C;
+  for (int t = threadIdx.x; t < C * kQgcRank; t += 256) {
+    const int k = t / kQgcRank;
+    const int N = p.cnt[(int64_t)u * C + k];
+    const int64_t idx = (int64_t)u * C * kQgcRank + t;
+    if (N > 0) p.cent[idx] = rint((double)(long long)p.sums[idx] / (double)N);
+    p.sums[idx] = 0ull;
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < C; k += 256) p.cnt[(int64_t)u * C + k] = 0;
+}
+
+hipError_t launch_qgc(const QgcParams& p, int dtype, int units, int T, hipStream_t st) {
+  if (dtype == SDA_BF16) {
+    hipLaunchKernelGGL(qgc_project_kernel<bf16_t>, dim3(units * qgc_chunks(p.n)), dim3(256), 0, st, p);
+  } else {
+    hipLaunchKernelGGL(qgc_project_kernel<float>, dim3(units * qgc_chunks(p.n)), dim3(256), 0, st, p);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(qgc_init_kernel, dim3(units), dim3(256), 0, st, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  for (int t = 1; t <= T; ++t) {
+    hipLaunchKernelGGL(qgc_assign_kernel, dim3(units * qgc_assign_chunks(p.n)), dim3(256), 0, st, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (t < T) {
+      hipLaunchKernelGGL(qgc_update_kernel, dim3(units), dim3(256), 0, st, p);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace sda

@@ -1,0 +1,37 @@
+// sda_cluster.hpp -- parameter block and launcher of the clustering kernels
+// (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sda.h"
+
+namespace sda {
+
+constexpr int kQgcRank = 16;          // projection rank
+constexpr int kQgcRows = 256;         // rows per workgroup of the projection
+constexpr int kQgcAssignRows = 512;   // rows per workgroup of an assignment pass
+constexpr double kQgcScale = 4096.0;  // fixed-point scale of the coordinates
+constexpr int kQgcMax = (1 << 23) - 1;
+
+struct QgcParams {
+  const void* K;
+  const float* V;              // [units, d, 16]
+  int64_t sb, sh, sn;
+  int32_t Hkv, n, C;
+  int32_t* zq;                 // workspace [units, n, 16] fixed-point coordinates
+  double* cent;                // workspace [units, C, 16] centroids (integers)
+  unsigned long long* sums;    // workspace [units, C, 16] two's-complement integer sums
+  int32_t* cnt;                // workspace [units, C]
+  int32_t* cluster_id;         // [units, n] output
+  int32_t* flags;              // [units] or null
+};
+
+__host__ __device__ inline int qgc_chunks(int n) { return (n + kQgcRows - 1) / kQgcRows; }
+__host__ __device__ inline int qgc_assign_chunks(int n) { return (n + kQgcAssignRows - 1) / kQgcAssignRows; }
+
+hipError_t launch_qgc(const QgcParams& p, int dtype, int units, int T, hipStream_t st);
+
+}  // namespace sda

@@ -22,12 +22,14 @@ LIB_PATH = os.path.join(_PKG, "libsda.so")
 SDA_OK, SDA_EINVAL, SDA_ESHAPE, SDA_EDTYPE, SDA_EWORKSPACE, SDA_EUNSUPPORTED, SDA_EHIP = 0, -1, -2, -3, -4, -5, -6
 SDA_BF16, SDA_F32 = 0, 1
 TAIL_NONE, TAIL_PROXY, TAIL_PRIOR, TAIL_SAMPLED = 0, 1, 2, 3
-OP_SPARSE, OP_DENSE, OP_BUILD_PROXIES, OP_BUILD_PRIOR, OP_BUILD_QGS, OP_SELECT_QGS = 0, 1, 2, 3, 4, 5
+OP_SPARSE, OP_DENSE, OP_BUILD_PROXIES, OP_BUILD_PRIOR, OP_BUILD_QGS, OP_SELECT_QGS, OP_BUILD_QGC = 0, 1, 2, 3, 4, 5, 6
 QGS_RANK = 32
+QGC_RANK = 16
 FLAG_IDX_RANGE, FLAG_IDX_ORDER, FLAG_SAMPLE_CAP, FLAG_CLUSTER, FLAG_LEN = 1, 2, 4, 8, 16
 
 EXPORTED = ["sda_workspace_bytes", "sda_build_tail_proxies", "sda_build_prior", "sda_sparse_decode_attn",
-            "sda_dense_decode_attn", "sda_build_qgs_codes", "sda_select_qgs", "sda_status_str", "sda_version"]
+            "sda_dense_decode_attn", "sda_build_qgs_codes", "sda_select_qgs", "sda_build_qgc_clusters",
+            "sda_status_str", "sda_version"]
 
 
 class SdaError(RuntimeError):
@@ -82,6 +84,8 @@ def lib() -> ctypes.CDLL:
     L.sda_build_tail_proxies.argtypes = [D, _vp, _vp, _vp, i32, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp]
     L.sda_build_qgs_codes.restype = i32
     L.sda_build_qgs_codes.argtypes = [D, _vp, _vp, _vp, _vp, _vp, sz, _vp]
+    L.sda_build_qgc_clusters.restype = i32
+    L.sda_build_qgc_clusters.argtypes = [D, _vp, _vp, i32, i32, _vp, _vp, _vp, sz, _vp]
     L.sda_select_qgs.restype = i32
     L.sda_select_qgs.argtypes = [D, _vp, ctypes.POINTER(Selector), i32, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp]
     L.sda_build_prior.restype = i32
@@ -377,6 +381,25 @@ def select_qgs(q: torch.Tensor, K: torch.Tensor, cluster_id: torch.Tensor, proxi
                               _ptr(idx_cluster), _ptr(budget), _ptr(flags), _ptr(ws), wsb, _stream(stream))
     _check(rc, "sda_select_qgs")
     return idx, idx_len, idx_cluster
+
+
+def build_qgc_clusters(K: torch.Tensor, V: torch.Tensor, C: int, T: int = 10,
+                       flags: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    """Query-geometry clustering of the keys: cluster ids [B, Hkv, n] int32
+    from the basis V [B, Hkv, d, 16] (k-means with T passes)."""
+    dims = make_dims(K, 1)
+    dims.Hq = dims.Hkv
+    B, Hkv, n, d = K.shape
+    V = _f32c(V, "V")
+    if tuple(V.shape) != (B, Hkv, d, QGC_RANK):
+        raise ValueError(f"V must be [B, Hkv, d, {QGC_RANK}]")
+    cid = torch.empty((B, Hkv, n), dtype=torch.int32, device=K.device)
+    ws, wsb = _workspace(workspace_bytes(dims, OP_BUILD_QGC, C=C), K.device, ws)
+    rc = lib().sda_build_qgc_clusters(ctypes.byref(dims), _ptr(K), _ptr(V), int(C), int(T), _ptr(cid), _ptr(flags),
+                                      _ptr(ws), wsb, _stream(stream))
+    _check(rc, "sda_build_qgc_clusters")
+    return cid
 
 
 def default_scale(d: int) -> float:

@@ -181,3 +181,23 @@ def test_selector_validation(L):
     assert wsel >= 4 * 1024 * 8                                 # one 8-byte key per row
     assert call(sel(), ws_bytes=wsel - 1) == sda.SDA_EWORKSPACE
     assert L.sda_workspace_bytes(ctypes.byref(dims), sda.OP_SELECT_QGS, 0, 0, 0) == 0
+
+
+def test_clustering_validation(L):
+    """Host-side checks of the clustering entry point (nothing launches)."""
+    dims = _dims()
+    need = L.sda_workspace_bytes(ctypes.byref(dims), sda.OP_BUILD_QGC, 0, 0, 64)
+    assert need >= 4 * 1024 * 16 * 4                           # 16 fixed-point coordinates per row
+    assert L.sda_workspace_bytes(ctypes.byref(dims), sda.OP_BUILD_QGC, 0, 0, 65) == 0
+
+    def call(C=64, T=10, K=FAKE, V=FAKE, cid=FAKE, ws_bytes=1 << 30):
+        return L.sda_build_qgc_clusters(ctypes.byref(dims), K, V, C, T, cid, None, FAKE, ws_bytes, None)
+
+    assert call(C=0) == sda.SDA_EUNSUPPORTED
+    assert call(C=65) == sda.SDA_EUNSUPPORTED
+    assert call(T=0) == sda.SDA_EINVAL
+    assert call(T=1001) == sda.SDA_EINVAL
+    assert call(V=None) == sda.SDA_EINVAL
+    assert call(cid=None) == sda.SDA_EINVAL
+    assert call(K=MISALIGNED) == sda.SDA_EINVAL
+    assert call(ws_bytes=need - 1) == sda.SDA_EWORKSPACE
