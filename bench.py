@@ -366,12 +366,28 @@ def measure_rows(a, dev):
                                                w.n_local, w.n_top, out=outs, ws=ws), 50, 5, graph=not a.no_graph)
     per_unit = (w.n * (w.r + 4) + w.C * (4 + 2 * w.d * 4) + w.d * w.r * 4 + w.r * 8 + w.m * 8 + 4)
     by = units * per_unit + w.B * w.Hq * w.d * w.elem_bytes
+    # query-geometry clustering (C = 64, 10 passes) and the selector on its clusters
+    V16 = U[..., :sda.QGC_RANK].contiguous()
+    ws_q = torch.empty(sda.workspace_bytes(sda.make_dims(K, w.Hq), sda.OP_BUILD_QGC, C=64), dtype=torch.uint8,
+                       device=dev)
+    qgc_ms = time_steps(lambda i: sda.build_qgc_clusters(K, V16, 64, T=10, ws=ws_q), 3, 1, graph=False)
+    cid64 = sda.build_qgc_clusters(K, V16, 64, T=10, ws=ws_q)
+    del ws_q
+    Vfull = to_dev(c.V, dev)
+    st64 = sda.build_tail_proxies(K, Vfull, cid64, 64, with_sumK2=True)
+    del Vfull
+    ws64 = torch.empty(sda.workspace_bytes(sda.make_dims(K, w.Hq), sda.OP_SELECT_QGS, C=64), dtype=torch.uint8,
+                       device=dev)
+    ms_s64 = time_steps(lambda i: sda.select_qgs(q, K, cid64, st64, copies[i % ncopy][0], w.n_sink, w.n_local,
+                                                 w.n_top, out=outs, ws=ws64), 50, 5, graph=not a.no_graph)
     out["qgs_select_b32_n32k"] = {"us_per_step": round(ms_s * 1e3, 2), "bytes_per_step": by,
                                   "gbs": round(by / (ms_s * 1e-3) / 1e9, 1),
                                   "frac_hbm_peak": round(by / (ms_s * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                   "rows_scored": units * w.n, "rows_picked": units * w.n_top,
                                   "build_codes_us": round(cbuild_ms * 1e3, 1),
-                                  "build_proxies_with_sq_us": round(pbuild_ms * 1e3, 1)}
+                                  "build_proxies_with_sq_us": round(pbuild_ms * 1e3, 1),
+                                  "qgc_clusters_c64_t10_us": round(qgc_ms * 1e3, 1),
+                                  "us_per_step_on_qgc_c64": round(ms_s64 * 1e3, 2)}
     return out
 
 
