@@ -527,12 +527,14 @@ __device__ __forceinline__ void sel_init(SelState& S, const int* budget, const i
 }
 
 // One pass's resolution, after its histograms are complete.
-__device__ __forceinline__ void sel_resolve(SelState& S, const int* hist, int C, int shift) {
+// Histograms hold nb = 2^W bins per cluster (W = 7 or 6).
+__device__ __forceinline__ void sel_resolve(SelState& S, const int* hist, int C, int shift, int nb = 128) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, nw = blockDim.x >> 6;
   for (int c = w; c < C; c += nw) {
     if (S.done[c]) continue;
     const int need = S.need[c];
-    const int chi = hist[c * 128 + 2 * lane + 1], clo = hist[c * 128 + 2 * lane];
+    const int chi = 2 * lane + 1 < nb ? hist[c * nb + 2 * lane + 1] : 0;
+    const int clo = 2 * lane < nb ? hist[c * nb + 2 * lane] : 0;
     const int pair = chi + clo;
     int incl = pair;  // rows in this lane's bins and every higher bin
 #pragma unroll
@@ -567,7 +569,7 @@ __device__ __forceinline__ void sel_resolve(SelState& S, const int* hist, int C,
       const uint64_t pref = S.pref[c] | ((uint64_t)tb << shift);
       S.pref[c] = pref;
       S.need[c] = rest;
-      if (hist[c * 128 + tb] == rest) {
+      if (hist[c * nb + tb] == rest) {
         S.T[c] = pref;
         S.done[c] = 1;
       }
@@ -575,9 +577,10 @@ __device__ __forceinline__ void sel_resolve(SelState& S, const int* hist, int C,
   }
 }
 
-__device__ __forceinline__ void pass_digits(int pass, int& top, int& shift, int& width) {
-  top = kKeyBits - 7 * pass;
-  shift = top > 7 ? top - 7 : 0;
+// Pass p of a W-bit radix select covers key bits [shift, top), top = 40 - W p.
+__device__ __forceinline__ void pass_digits(int pass, int& top, int& shift, int& width, int W = 7) {
+  top = kKeyBits - W * pass;
+  shift = top > W ? top - W : 0;
   width = top - shift;
 }
 
@@ -715,7 +718,7 @@ __global__ __launch_bounds__(kSelThreads) void qgs_select_kernel(const QgsSelect
 // selects and lists from LDS.  HBM traffic: the codes and cluster ids once.
 //   record: [19:0] S + 2^19, [26:20] cluster (127 = none), [27] eligible
 constexpr int kFusedMaxN = 32768;
-constexpr int kFusedMaxC = 32;
+constexpr int kFusedMaxC = kCmax;
 
 constexpr int kFusedSel = 1024;    // picked rows collected in LDS before they are ordered
 constexpr int kFusedCand = 1024;   // rows on a pending cluster's boundary after two digits
@@ -741,7 +744,7 @@ __host__ __device__ inline size_t fused_big(int n, int C) {
   return ((rec > prep ? rec : prep) + 15) / 16 * 16;
 }
 __host__ __device__ inline size_t fused_lds_bytes(int n, int C) {
-  return fused_big(n, C) + (size_t)C * 128 * 4 + sizeof(FusedState);
+  return fused_big(n, C) + (size_t)C * (C <= 32 ? 128 : 64) * 4 + sizeof(FusedState);
 }
 
 __device__ __forceinline__ uint64_t rec_key(uint32_t r, int j) {
@@ -755,7 +758,9 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
   const size_t big = fused_big(n, C);
   uint32_t* rec = reinterpret_cast<uint32_t*>(s_raw);
   int* hist = reinterpret_cast<int*>(s_raw + big);
-  FusedState& F = *reinterpret_cast<FusedState*>(s_raw + big + (size_t)C * 128 * 4);
+  // digits of W bits: 7 up to 32 clusters, 6 up to 64 (histograms C x 2^W)
+  const int W = C <= 32 ? 7 : 6, NB = 1 << W;
+  FusedState& F = *reinterpret_cast<FusedState*>(s_raw + big + (size_t)C * NB * 4);
   SelState& S = F.sel;
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
@@ -767,7 +772,7 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
   }
   __syncthreads();
   sel_init(S, F.budget, F.avail, C);
-  for (int i = tid; i < C * 128; i += kSelThreads) hist[i] = 0;
+  for (int i = tid; i < C * NB; i += kSelThreads) hist[i] = 0;
   __syncthreads();
 
   // scores, records and the first digit's histograms
@@ -803,20 +808,21 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
       const bool el = cl != kNoCluster && j >= lo && j < hi;
       const uint32_t s20 = (uint32_t)(Sc + (1 << 19));
       rec[j] = (el ? (1u << 27) : 0u) | ((uint32_t)cl << 20) | s20;
-      if (el && !S.done[cl]) atomicAdd(&hist[cl * 128 + (int)(s20 >> 13)], 1);
+      if (el && !S.done[cl]) atomicAdd(&hist[cl * NB + (int)(s20 >> (20 - W))], 1);
     }
   }
   if (bad) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
   __syncthreads();
 
-  // pass 0: its histograms came with the scores (key bits [33, 40) = S20 >> 13)
-  sel_resolve(S, hist, C, 33);
+  // pass 0: its histograms came with the scores (key bits [40 - W, 40) = S20 >> (20 - W))
+  sel_resolve(S, hist, C, kKeyBits - W, NB);
   __syncthreads();
 
-  // pass 1: key bits [26, 33) = (S20 >> 6) & 127 of the rows in each pending
-  // cluster's boundary digit; 32-bit arithmetic on the records
-  if (tid < C) F.match[tid] = S.done[tid] ? -1 : (int)(S.pref[tid] >> 33);
-  for (int i = tid; i < C * 128; i += kSelThreads) hist[i] = 0;
+  // pass 1: key bits [40 - 2W, 40 - W) = (S20 >> (20 - 2W)) & (NB - 1) of the
+  // rows in each pending cluster's boundary digit; 32-bit arithmetic on the
+  // records
+  if (tid < C) F.match[tid] = S.done[tid] ? -1 : (int)(S.pref[tid] >> (kKeyBits - W));
+  for (int i = tid; i < C * NB; i += kSelThreads) hist[i] = 0;
   __syncthreads();
   for (int j0 = tid; j0 < n; j0 += 8 * kSelThreads) {
     uint32_t rr[8];
@@ -831,27 +837,27 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const uint32_t r = rr[k], s20 = r & 0xfffffu;
-      const bool hit = (j0 + k * kSelThreads < n) & ((r >> 27) & 1) & ((int)(s20 >> 13) == mt[k]);
-      if (hit) atomicAdd(&hist[(int)((r >> 20) & 127) * 128 + (int)((s20 >> 6) & 127)], 1);
+      const bool hit = (j0 + k * kSelThreads < n) & ((r >> 27) & 1) & ((int)(s20 >> (20 - W)) == mt[k]);
+      if (hit) atomicAdd(&hist[(int)((r >> 20) & 127) * NB + (int)((s20 >> (20 - 2 * W)) & (NB - 1))], 1);
     }
   }
   __syncthreads();
-  sel_resolve(S, hist, C, 26);
+  sel_resolve(S, hist, C, kKeyBits - 2 * W, NB);
   __syncthreads();
 
   // Classify the rows between sink and local window once: a row of a done
   // cluster is picked when S20 >= A_c (its threshold's score part; those
   // thresholds have zero position bits); for a pending cluster, a row above
-  // its boundary (S20 >> 6 > P_c) is picked and a row on it (== P_c) is a
-  // candidate for the remaining digits.
+  // its boundary (S20 >> (20 - 2W) > P_c) is picked and a row on it (== P_c)
+  // is a candidate for the remaining digits.
   const int lane = tid & 63, w = tid >> 6;
   if (tid < C) {
     if (S.done[tid]) {
       F.thrA[tid] = (int)(S.T[tid] >> 20);
       F.thrB[tid] = -1;
     } else {
-      const int P = (int)(S.pref[tid] >> 26);
-      F.thrA[tid] = (P + 1) << 6;
+      const int P = (int)(S.pref[tid] >> (kKeyBits - 2 * W));
+      F.thrA[tid] = (P + 1) << (20 - 2 * W);
       F.thrB[tid] = P;
     }
   }
@@ -892,7 +898,7 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
         const int s20 = (int)(rr[k] & 0xfffffu);
         const bool el = (j < r1) & ((rr[k] >> 27) & 1);
         push(el & (s20 >= ta[k]), &F.nsel, F.picked, kFusedSel, j);
-        push(el & ((s20 >> 6) == tb[k]), &F.ncand, F.cand, kFusedCand, j);
+        push(el & ((s20 >> (20 - 2 * W)) == tb[k]), &F.ncand, F.cand, kFusedCand, j);
       }
     }
   }
@@ -901,14 +907,14 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
   if (F.ncand > kFusedCand || F.nsel > kFusedSel) {
     // too many rows for the LDS lists: the remaining digits over all rows,
     // then the ordered emission by scans
-    for (int pass = 2; pass < 6; ++pass) {
+    for (int pass = 2; pass * W < kKeyBits; ++pass) {
       int top, shift, width;
-      pass_digits(pass, top, shift, width);
+      pass_digits(pass, top, shift, width, W);
       if (tid < 64) {
         const int left = __popcll(__ballot(tid < C && !S.done[tid]));
         if (tid == 0) S.left = left;
       }
-      for (int i = tid; i < C * 128; i += kSelThreads) hist[i] = 0;
+      for (int i = tid; i < C * NB; i += kSelThreads) hist[i] = 0;
       __syncthreads();
       if (S.left == 0) break;
       for (int j = tid; j < n; j += kSelThreads) {
@@ -916,10 +922,10 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
         const int c = (int)((r >> 20) & 127);
         const uint64_t k40 = rec_key(r, j);
         const bool hit = ((r >> 27) & 1) && !S.done[c] && (k40 >> top) == (S.pref[c] >> top);
-        if (hit) atomicAdd(&hist[c * 128 + (int)((k40 >> shift) & ((1u << width) - 1))], 1);
+        if (hit) atomicAdd(&hist[c * NB + (int)((k40 >> shift) & ((1u << width) - 1))], 1);
       }
       __syncthreads();
-      sel_resolve(S, hist, C, shift);
+      sel_resolve(S, hist, C, shift, NB);
       __syncthreads();
     }
     emit_listed(p, u, S, [&](int j, bool& el, int& c, uint64_t& k40) {
@@ -933,14 +939,14 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
 
   // the remaining digits over the candidates only
   const int ncand = F.ncand;
-  for (int pass = 2; pass < 6; ++pass) {
+  for (int pass = 2; pass * W < kKeyBits; ++pass) {
     int top, shift, width;
-    pass_digits(pass, top, shift, width);
+    pass_digits(pass, top, shift, width, W);
     if (tid < 64) {
       const int left = __popcll(__ballot(tid < C && !S.done[tid]));
       if (tid == 0) S.left = left;
     }
-    for (int i = tid; i < C * 128; i += kSelThreads) hist[i] = 0;
+    for (int i = tid; i < C * NB; i += kSelThreads) hist[i] = 0;
     __syncthreads();
     if (S.left == 0) break;
     for (int t = tid; t < ncand; t += kSelThreads) {
@@ -949,10 +955,10 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
       const int c = (int)((r >> 20) & 127);
       const uint64_t k40 = rec_key(r, j);
       if (!S.done[c] && (k40 >> top) == (S.pref[c] >> top))
-        atomicAdd(&hist[c * 128 + (int)((k40 >> shift) & ((1u << width) - 1))], 1);
+        atomicAdd(&hist[c * NB + (int)((k40 >> shift) & ((1u << width) - 1))], 1);
     }
     __syncthreads();
-    sel_resolve(S, hist, C, shift);
+    sel_resolve(S, hist, C, shift, NB);
     __syncthreads();
   }
   for (int t0 = 0; t0 < ncand; t0 += kSelThreads) {

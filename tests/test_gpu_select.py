@@ -116,11 +116,13 @@ def test_squared_key_sums():
 
 
 @pytest.mark.parametrize("G,C,E,n", [(4, 16, 100, 4500), (1, 8, 60, 4500), (2, 32, 200, 4500),
-                                     (8, 64, 300, 4500), (4, 8, 120, 40000)])
+                                     (8, 64, 300, 4500), (4, 48, 150, 4500), (4, 8, 120, 40000),
+                                     (2, 64, 200, 40000)])
 def test_select_small(G, C, E, n):
-    """Whole selector on small workloads: G = 1..8, C up to 64, n with a
-    ragged last score chunk.  C = 64 and n = 40000 take the three-launch
-    path (workspace keys), the others the one-launch path (LDS records)."""
+    """Whole selector on small workloads: G = 1..8, C up to 64 (7-bit radix
+    digits up to 32 clusters, 6-bit beyond), n with a ragged last score
+    chunk.  n = 40000 takes the three-launch path (workspace keys), the
+    others the one-launch path (LDS records)."""
     w = _workload(B=2, Hkv=2, Hq=2 * G, n=n, n_top=E, C=C)
     c = synth.make_case(w)
     r = _gpu_select(c, w)
