@@ -60,8 +60,8 @@ def _load():
         "orc_sparse_proxy_def": (i32, [D, _P, _P, _P, _P, _P, _P, i32, _P, i32, _P, _P]),
         "orc_sparse_proxy": (i32, [D, _P, _P, _P, _P, _P, _P, i32, _P, i32, _P, _P, _P, _P, _P]),
         "orc_prior_build": (i32, [D, _P, _P, _P, _P, _P, _P, _P]),
-        "orc_sparse_prior_def": (i32, [D, _P, _P, _P, _P, _P, _P, i32, _P, f64, _P, _P]),
-        "orc_sparse_prior": (i32, [D, _P, _P, _P, _P, _P, _P, i32, _P, f64, _P, _P, _P, _P, _P, _P]),
+        "orc_sparse_prior_def": (i32, [D, _P, _P, _P, _P, _P, _P, i32, _P, f64, i32, _P, _P]),
+        "orc_sparse_prior": (i32, [D, _P, _P, _P, _P, _P, _P, i32, _P, f64, i32, _P, _P, _P, _P, _P, _P]),
         "orc_splitmix64_next": (u64, [ctypes.POINTER(ctypes.c_uint64)]),
         "orc_unit_key": (u64, [u64, i64]),
         "orc_draw_rank": (i64, [u64, i64, i64]),
@@ -196,26 +196,29 @@ def prior_build(K, V, mu_Q, scale=None):
     return muK, Oest, maxP, sumP
 
 
-def sparse_prior_def(q, K, V, idx, mu_Q, lam=1.0, idx_len=None, logw=None, scale=None):
+def sparse_prior_def(q, K, V, idx, mu_Q, lam=1.0, idx_len=None, logw=None, scale=None, prior_n=0):
+    """prior_n: rows [0, prior_n) covered by the prior (0 = all)."""
     q, K, V, mu_Q = _c(q), _c(K), _c(V), _c(mu_Q, np.float32)
     idx, idx_len, logw = _c(idx, np.int32), _c(idx_len, np.int32), _c(logw, np.float32)
     D = _dims(q, K, scale)
     out, lse = _out(D)
     _check(_load().orc_sparse_prior_def(ctypes.byref(D), _ptr(q), _ptr(K), _ptr(V), _ptr(idx), _ptr(idx_len),
-                                        _ptr(logw), idx.shape[-1], _ptr(mu_Q), float(lam), _ptr(out), _ptr(lse)),
+                                        _ptr(logw), idx.shape[-1], _ptr(mu_Q), float(lam), int(prior_n), _ptr(out),
+                                        _ptr(lse)),
            "sparse_prior_def")
     return out, lse
 
 
-def sparse_prior(q, K, V, idx, mu_Q, lam, muK, Oest, maxP, sumP, idx_len=None, logw=None, scale=None):
+def sparse_prior(q, K, V, idx, mu_Q, lam, muK, Oest, maxP, sumP, idx_len=None, logw=None, scale=None, prior_n=0):
+    """prior_n: rows [0, prior_n) the state was built over (0 = all)."""
     q, K, V, mu_Q = _c(q), _c(K), _c(V), _c(mu_Q, np.float32)
     idx, idx_len, logw = _c(idx, np.int32), _c(idx_len, np.int32), _c(logw, np.float32)
     muK, Oest, maxP, sumP = (_c(a, np.float64) for a in (muK, Oest, maxP, sumP))
     D = _dims(q, K, scale)
     out, lse = _out(D)
     _check(_load().orc_sparse_prior(ctypes.byref(D), _ptr(q), _ptr(K), _ptr(V), _ptr(idx), _ptr(idx_len),
-                                    _ptr(logw), idx.shape[-1], _ptr(mu_Q), float(lam), _ptr(muK), _ptr(Oest),
-                                    _ptr(maxP), _ptr(sumP), _ptr(out), _ptr(lse)), "sparse_prior")
+                                    _ptr(logw), idx.shape[-1], _ptr(mu_Q), float(lam), int(prior_n), _ptr(muK),
+                                    _ptr(Oest), _ptr(maxP), _ptr(sumP), _ptr(out), _ptr(lse)), "sparse_prior")
     return out, lse
 
 

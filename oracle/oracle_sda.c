@@ -450,9 +450,10 @@ int orc_prior_build(const orc_dims* D, const void* K, const void* V,
 int orc_sparse_prior_def(const orc_dims* D, const void* q, const void* K,
                          const void* V, const int32_t* idx,
                          const int32_t* idx_len, const float* logw, int m,
-                         const float* mu_Q, double lambda,
+                         const float* mu_Q, double lambda, int prior_n,
                          double* out, double* lse) {
-  if (check_dims(D) || m < 0 || lambda < 0.0) return -1;
+  if (check_dims(D) || m < 0 || lambda < 0.0 || prior_n > D->n) return -1;
+  const int64_t n0 = prior_n > 0 ? prior_n : D->n;   /* rows the prior covers */
   int G = D->Hq / D->Hkv, d = D->d;
   int U = D->B * D->Hkv;
   int err = 0;
@@ -472,9 +473,9 @@ int orc_sparse_prior_def(const orc_dims* D, const void* q, const void* K,
     if (!list_is_set(D, I, len, mark)) {
       err |= 4;
     } else {
-      for (int64_t j = 0; j < D->n; ++j)
+      for (int64_t j = 0; j < n0; ++j)
         for (int i = 0; i < d; ++i) muK[i] += elem(D->dtype, K, kv_row(D, s, g, j) + i);
-      for (int i = 0; i < d; ++i) muK[i] /= (double)D->n;
+      for (int i = 0; i < d; ++i) muK[i] /= (double)n0;
       for (int hh = 0; hh < G; ++hh) {
         int h = g * G + hh;
         double c = bias_shift(D, q, mu_Q, muK, s, h);
@@ -483,7 +484,7 @@ int orc_sparse_prior_def(const orc_dims* D, const void* q, const void* K,
           terms_add_row(&T, logit(D, q, K, s, h, g, I[t]) + (w ? (double)w[t] : 0.0),
                         kv_row(D, s, g, I[t]));
         if (lambda > 0.0)
-          for (int64_t j = 0; j < D->n; ++j)
+          for (int64_t j = 0; j < n0; ++j)
             if (!mark[j])
               terms_add_row(&T, log(lambda) + prior_logit(D, mu_Q, K, s, h, g, j) + c,
                             kv_row(D, s, g, j));
@@ -499,10 +500,11 @@ int orc_sparse_prior_def(const orc_dims* D, const void* q, const void* K,
 int orc_sparse_prior(const orc_dims* D, const void* q, const void* K,
                      const void* V, const int32_t* idx, const int32_t* idx_len,
                      const float* logw, int m, const float* mu_Q,
-                     double lambda, const double* mu_K, const double* O_est,
+                     double lambda, int prior_n, const double* mu_K, const double* O_est,
                      const double* maxP, const double* sumP,
                      double* out, double* lse) {
-  if (check_dims(D) || m < 0 || lambda < 0.0) return -1;
+  if (check_dims(D) || m < 0 || lambda < 0.0 || prior_n > D->n) return -1;
+  const int64_t n0 = prior_n > 0 ? prior_n : D->n;   /* rows the prior covers */
   int G = D->Hq / D->Hkv, d = D->d;
   int U = D->B * D->Hkv;
   int err = 0;
@@ -531,6 +533,7 @@ int orc_sparse_prior(const orc_dims* D, const void* q, const void* K,
         double SP = 0.0;
         for (int i = 0; i < d; ++i) SPv[i] = 0.0;
         for (int t = 0; t < len; ++t) {
+          if (I[t] >= n0) continue;   /* a row the prior does not cover */
           double e = exp(prior_logit(D, mu_Q, K, s, h, g, I[t]) - maxP[hq]);
           SP += e;
           for (int i = 0; i < d; ++i) SPv[i] += e * elem(D->dtype, V, kv_row(D, s, g, I[t]) + i);

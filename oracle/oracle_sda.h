@@ -104,25 +104,30 @@ int orc_prior_build(const orc_dims* D, const void* K, const void* V,
                     const float* mu_Q, double* mu_K, double* O_est,
                     double* maxP, double* sumP);
 
-/* Plain definition, O(n): with c_h = scale * <q_h - mu_Q_h, mu_K> (mu_K the
- * exact key mean), every listed row j weighs exp(logit_hj + w_j) and every
- * unlisted row weighs lambda * exp(P_hj + c_h); O = sum w v / sum w. */
+/* Plain definition, O(n): the prior covers rows [0, prior_n) (the cache as
+ * it was when the prior was built; prior_n <= 0 means all n).  With
+ * c_h = scale * <q_h - mu_Q_h, mu_K> (mu_K the exact mean of the covered
+ * keys), every listed row j weighs exp(logit_hj + w_j), every unlisted
+ * covered row weighs lambda * exp(P_hj + c_h), and an unlisted row past
+ * prior_n weighs nothing; O = sum w v / sum w. */
 int orc_sparse_prior_def(const orc_dims* D, const void* q, const void* K,
                          const void* V, const int32_t* idx,
                          const int32_t* idx_len, const float* logw, int m,
-                         const float* mu_Q, double lambda,
+                         const float* mu_Q, double lambda, int prior_n,
                          double* out, double* lse);
 
-/* Delta form, O(|I|) [RESA, Online Aggregator]: from the built state,
+/* Delta form, O(|I|) [RESA, Online Aggregator]: from the state built over
+ * rows [0, prior_n) (prior_n <= 0: all n), with I' = the listed rows below
+ * prior_n,
  *   E  = lambda exp(c_h + maxP_h)
- *   A  = E (sumP O_est - sum_{j in I} exp(P_j - maxP) v_j)
- *   Bt = max(0, E (sumP - sum_{j in I} exp(P_j - maxP)))
+ *   A  = E (sumP O_est - sum_{j in I'} exp(P_j - maxP) v_j)
+ *   Bt = max(0, E (sumP - sum_{j in I'} exp(P_j - maxP)))
  *   O  = (A + sum_I exp(s_j + w_j) v_j) / (Bt + sum_I exp(s_j + w_j)).
  * Requires distinct positions in each unit's list. */
 int orc_sparse_prior(const orc_dims* D, const void* q, const void* K,
                      const void* V, const int32_t* idx, const int32_t* idx_len,
                      const float* logw, int m, const float* mu_Q,
-                     double lambda, const double* mu_K, const double* O_est,
+                     double lambda, int prior_n, const double* mu_K, const double* O_est,
                      const double* maxP, const double* sumP,
                      double* out, double* lse);
 

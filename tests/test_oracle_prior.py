@@ -157,3 +157,48 @@ def test_duplicates_rejected(orc):
     built = _built(orc, K, V, muQ)
     with pytest.raises(ValueError):
         orc.sparse_prior(q, K, V, np.array([[[1, 1]]], np.int32), muQ, 1.0, *built)
+
+
+def test_grown_cache_delta_equals_definition(orc):
+    """A prior built over the first n0 rows, decoded after the cache grew to
+    n rows: the delta form (only listed rows below n0 leave the prior's mass)
+    equals the plain definition (unlisted rows past n0 weigh nothing)."""
+    rng = np.random.default_rng(21)
+    B, Hq, Hkv, n0, n, d = 2, 4, 2, 300, 340, 128
+    q, K, V, muQ = _rand(rng, B, Hq, Hkv, n, d)
+    built = orc.prior_build(np.ascontiguousarray(K[:, :, :n0]), np.ascontiguousarray(V[:, :, :n0]), muQ)
+    for trial in range(3):
+        idx = np.sort(np.stack([np.stack([rng.choice(n, size=60, replace=False) for _ in range(Hkv)])
+                                for _ in range(B)]), axis=-1).astype(np.int32)
+        for lam in (1.0, 0.4):
+            o1, l1 = orc.sparse_prior(q, K, V, idx, muQ, lam, *built, prior_n=n0)
+            o2, l2 = orc.sparse_prior_def(q, K, V, idx, muQ, lam, prior_n=n0)
+            np.testing.assert_allclose(o1, o2, rtol=1e-10, atol=1e-12)
+            np.testing.assert_allclose(l1, l2, rtol=1e-12)
+
+
+def test_grown_cache_splits_by_token_range(orc):
+    """Every new row listed: the output is the log-sum-exp merge of (a) the
+    prior decode over the first n0 rows with the old list and (b) plain
+    softmax attention over the new rows -- the new rows enter exactly once and
+    leave the prior's mass alone."""
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, n0, n, d = 1, 4, 1, 256, 288, 128
+    q, K, V, muQ = _rand(rng, B, Hq, Hkv, n, d)
+    K0, V0 = np.ascontiguousarray(K[:, :, :n0]), np.ascontiguousarray(V[:, :, :n0])
+    built = orc.prior_build(K0, V0, muQ)
+    I0 = np.sort(rng.choice(n0, size=40, replace=False)).astype(np.int32)
+    idx = np.concatenate([I0, np.arange(n0, n, dtype=np.int32)])[None, None]
+    o, l = orc.sparse_prior(q, K, V, idx, muQ, 1.0, *built, prior_n=n0)
+    oa, la = orc.sparse_prior(q, K0, V0, I0[None, None], muQ, 1.0, *built)
+    Kn, Vn = np.ascontiguousarray(K[:, :, n0:]), np.ascontiguousarray(V[:, :, n0:])
+    ob, lb = orc.dense(q, Kn, Vn)
+    lm = np.logaddexp(la, lb)
+    om = (np.exp(la - lm)[..., None] * oa + np.exp(lb - lm)[..., None] * ob)
+    np.testing.assert_allclose(o, om, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(l, lm, rtol=1e-12)
+    # prior_n = n is the same as covering every row
+    full = orc.prior_build(K, V, muQ)
+    o3, _ = orc.sparse_prior(q, K, V, idx, muQ, 1.0, *full, prior_n=n)
+    o4, _ = orc.sparse_prior(q, K, V, idx, muQ, 1.0, *full)
+    np.testing.assert_array_equal(o3, o4)
