@@ -125,17 +125,20 @@ typedef struct {
   const float* sumK;             /* [B,Hkv,C,d]                             */
   const float* sumV;             /* [B,Hkv,C,d]                             */
 
-  /* PRIOR (RESA): state from sda_build_prior.  With
-   * c_h = scale*<q_h - mu_Q_h, mu_K> every unlisted row j weighs
-   * lambda*exp(scale*<mu_Q_h, k_j> + c_h); listed rows weigh exp(logit).
-   * Evaluated in O(|I|) by the delta merge.  The list must hold distinct
-   * positions in increasing order. */
+  /* PRIOR (RESA): state from sda_build_prior over the rows [0, prior_n)
+   * the cache held then (the prefill; prior_n = 0 means all n rows).  With
+   * c_h = scale*<q_h - mu_Q_h, mu_K> every unlisted row j < prior_n weighs
+   * lambda*exp(scale*<mu_Q_h, k_j> + c_h); listed rows weigh exp(logit);
+   * rows appended later (j >= prior_n) count only when listed.  Evaluated
+   * in O(|I|) by the delta merge.  The list must hold distinct positions in
+   * increasing order. */
   const float* mu_Q;             /* [B,Hq,d]  mean (prefill) query          */
   const float* mu_K;             /* [B,Hkv,d] key mean                      */
   const float* O_est;            /* [B,Hq,d]                                */
   const float* maxP;             /* [B,Hq]                                  */
   const float* sumP;             /* [B,Hq]                                  */
   float lambda;                  /* prior weight, >= 0 (0 = plain sparse)   */
+  int32_t prior_n;               /* rows the prior covers, 0..n (0 = all)   */
 
   /* SAMPLED (vAttention): idx/idx_len carry the deterministic set I_f
    * (distinct, increasing).  b0 base draws from the unread rows estimate

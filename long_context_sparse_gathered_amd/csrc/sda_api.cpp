@@ -407,12 +407,14 @@ SDA_EXPORT sda_status sda_sparse_decode_attn(const sda_dims* dims, const void* q
     if (!tail->mu_Q || !tail->mu_K || !tail->O_est || !tail->maxP || !tail->sumP) return SDA_EINVAL;
     if (!aligned16(tail->mu_Q) || !aligned16(tail->mu_K)) return SDA_EINVAL;
     if (!(tail->lambda >= 0.f) || !isfinite(tail->lambda)) return SDA_EINVAL;
+    if (tail->prior_n < 0 || tail->prior_n > r.n) return SDA_EINVAL;
     p.mu_Q = tail->mu_Q;
     p.mu_K = tail->mu_K;
     p.O_est = tail->O_est;
     p.maxP = tail->maxP;
     p.sumP = tail->sumP;
     p.lambda = tail->lambda;
+    p.prior_n = tail->prior_n > 0 ? tail->prior_n : r.n;
   } else if (kind == SDA_TAIL_SAMPLED) {
     if (!(tail->eps > 0.0) || !(tail->z > 0.0) || !isfinite(tail->eps) || !isfinite(tail->z)) return SDA_EINVAL;
     if (tail->b0 < 2 || tail->b0 > kSampMaxB0) return SDA_EUNSUPPORTED;

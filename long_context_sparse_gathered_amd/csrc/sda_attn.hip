@@ -1025,6 +1025,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const AttnParams p) {
   for (int tb = t0; tb < t1; tb += STEP) {
     int off[NSB];
     float lw[NSB];
+    bool cov[PRIOR ? NSB : 1];   // the prior covers the slot's row
     bool lane_ok = false;
     if constexpr (!DENSE) {
       const int t = list_t(tb);
@@ -1042,6 +1043,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const AttnParams p) {
         const bool ok = shfl_i(lane_ok ? 1 : 0, src) != 0;
         off[k] = ok ? row_off<T>(j, p.sn, r16) : kOOB;
         lw[k] = ok ? shfl_f(lwv, src) * kLog2e : kNegInf;
+        if constexpr (PRIOR) cov[k] = ok && j < p.prior_n;
       }
     }
     RowChunk<T> kc[NSB], vc[NSB];
@@ -1085,7 +1087,7 @@ __global__ __launch_bounds__(256) void stream_kernel(const AttnParams p) {
         float ap[G];
         dot_heads<G>(qp, kf, ap);
 #pragma unroll
-        for (int h = 0; h < G; ++h) pl[k][h] = (off[k] == kOOB) ? kNegInf : ap[h] - mP[h];
+        for (int h = 0; h < G; ++h) pl[k][h] = cov[k] ? ap[h] - mP[h] : kNegInf;
       }
     }
 #pragma unroll
@@ -1355,6 +1357,7 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
     bool valid;
     int row;
     float lw_own;
+    bool cov_own = false;  // the prior covers this lane's row
     if constexpr (DENSE) {
       valid = lane < KB && e < t1;
       row = valid ? e : 0;
@@ -1364,6 +1367,7 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
       valid = live && (unsigned)li < (unsigned)p.n;
       row = li;
       lw_own = valid ? (p.logw ? lwv * kLog2e : 0.f) : kNegInf;
+      if constexpr (PRIOR) cov_own = valid && li < p.prior_n;
       int bad = 0;
       if (live && (unsigned)li >= (unsigned)p.n) bad |= SDA_FLAG_IDX_RANGE;
       if (PRIOR && live && e > 0 && lp >= li) bad |= SDA_FLAG_IDX_ORDER;
@@ -1411,6 +1415,7 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
                                                     __builtin_bit_cast(bf16x8_t, kt[t][st]), d, 0, 0, 0);
       const int kk = 16 * t + r16;
       const float lwk = shfl_f(lw_own, kk);
+      const bool cvk = PRIOR && shfl_i(cov_own ? 1 : 0, kk) != 0;   // the prior covers this key
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * sub + i;
@@ -1419,7 +1424,7 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
           s_x[w][r][kk] = xv;
           bmx[i] = fmaxf(bmx[i], xv);
         } else if (r < RA) {
-          s_x[w][r][kk] = lwk == kNegInf ? kNegInf : d[i];
+          s_x[w][r][kk] = cvk ? d[i] : kNegInf;
         }
       }
     }

@@ -44,6 +44,7 @@ struct AttnParams {
   const float* maxP;
   const float* sumP;
   float lambda;
+  int32_t prior_n;             // rows [0, prior_n) covered by the prior
 
   // SAMPLED
   float scale;                 // logit scale (fp32 value, widened for fp64 statistics)

@@ -53,7 +53,7 @@ class Tail(ctypes.Structure):
                 ("C", ctypes.c_int32), ("idx_cluster", _vp), ("cluster_id", _vp), ("count", _vp),
                 ("sumK", _vp), ("sumV", _vp),
                 ("mu_Q", _vp), ("mu_K", _vp), ("O_est", _vp), ("maxP", _vp), ("sumP", _vp),
-                ("lam", ctypes.c_float),
+                ("lam", ctypes.c_float), ("prior_n", ctypes.c_int32),
                 ("eps", ctypes.c_double), ("z", ctypes.c_double), ("b0", ctypes.c_int32),
                 ("seed", ctypes.c_uint64), ("b_cap", ctypes.c_int32), ("b_out", _vp), ("bstar_out", _vp),
                 ("samples_out", _vp)]
@@ -188,12 +188,15 @@ class ProxyState:
 
 @dataclass
 class PriorState:
-    """Rank-1 prior state from build_prior (plus the mean query it came from)."""
+    """Rank-1 prior state from build_prior (plus the mean query it came from).
+    n_covered: the cache rows it was built over; a decode over a cache that
+    has grown since treats the later rows as exact-only."""
     mu_Q: torch.Tensor      # [B,Hq,d] fp32
     mu_K: torch.Tensor      # [B,Hkv,d]
     O_est: torch.Tensor     # [B,Hq,d]
     maxP: torch.Tensor      # [B,Hq]
     sumP: torch.Tensor      # [B,Hq]
+    n_covered: int = 0
 
 
 @dataclass
@@ -230,6 +233,7 @@ def _tail_struct(tail, idx_cluster, cluster_id, lam, keep) -> Tail:
         for name in ("mu_Q", "mu_K", "O_est", "maxP", "sumP"):
             setattr(t, name, _ptr(_f32c(getattr(tail, name), name)))
         t.lam = float(lam)
+        t.prior_n = int(tail.n_covered)
     elif isinstance(tail, SampledTail):
         t.kind = TAIL_SAMPLED
         t.eps, t.z, t.b0, t.seed, t.b_cap = tail.eps, tail.z, tail.b0, tail.seed & (2**64 - 1), tail.b_cap
@@ -277,7 +281,7 @@ def build_prior(K: torch.Tensor, V: torch.Tensor, mu_Q: torch.Tensor, scale: Opt
     rc = lib().sda_build_prior(ctypes.byref(dims), _ptr(K), _ptr(V), _ptr(mu_Q), _ptr(mu_K), _ptr(O_est),
                                _ptr(maxP), _ptr(sumP), _ptr(ws), wsb, _stream(stream))
     _check(rc, "sda_build_prior")
-    return PriorState(mu_Q=mu_Q, mu_K=mu_K, O_est=O_est, maxP=maxP, sumP=sumP)
+    return PriorState(mu_Q=mu_Q, mu_K=mu_K, O_est=O_est, maxP=maxP, sumP=sumP, n_covered=n)
 
 
 def dense_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, scale: Optional[float] = None,

@@ -115,6 +115,11 @@ def test_prior_tail_validation(L):
     t.lam = float("nan")
     assert _sparse(L, dims, tail=t) == sda.SDA_EINVAL
     t.lam = 1.0
+    t.prior_n = dims.n + 1                      # more rows than the cache holds
+    assert _sparse(L, dims, tail=t) == sda.SDA_EINVAL
+    t.prior_n = -1
+    assert _sparse(L, dims, tail=t) == sda.SDA_EINVAL
+    t.prior_n = 0
     # B*Hkv = 4 units: the split-K path needs a workspace
     need = L.sda_workspace_bytes(ctypes.byref(dims), sda.OP_SPARSE, sda.TAIL_PRIOR, 2000, 0)
     assert need > 0

@@ -158,3 +158,27 @@ def test_prior_full_size_b16_n128k(orc):
         rows = slice(g * w.G, (g + 1) * w.G)
         assert rel_err(got[s, rows], ref[0]) <= TOL, (s, g)
         assert np.abs(got_lse[s, rows] - ref_lse[0]).max() <= LSE_TOL, (s, g)
+
+
+@pytest.mark.parametrize("G", [4, 8])
+def test_prior_on_grown_cache(orc, G):
+    """The prior built over the first n0 rows (the prefill), the decode after
+    the cache grew to n rows with the new rows in the local window: rows past
+    n0 are exact-only (matrix-core stream at G = 4, vector stream at G = 8)."""
+    w = _grouped(synth.WORKLOADS["prior_bf16_b16_n128k"], G, 2).replace(B=2, n=6000, n_top=900)
+    n0 = 5800
+    c = synth.make_case(w)
+    d = case_to_dev(c)
+    ps = sda.build_prior(d["K"][:, :, :n0], d["V"][:, :, :n0], d["mu_Q"])
+    assert ps.n_covered == n0
+    _sync()
+    K0, V0 = np.ascontiguousarray(c.K[:, :, :n0]), np.ascontiguousarray(c.V[:, :, :n0])
+    built = orc.prior_build(K0, V0, c.mu_Q)
+    for lam in (1.0, 0.3):
+        out, lse = sda.sparse_decode_attn(d["q"], d["K"], d["V"], d["idx"], tail=ps, lam=lam)
+        _sync()
+        ref, ref_lse = orc.sparse_prior_def(c.q, c.K, c.V, c.idx, c.mu_Q, lam, prior_n=n0)
+        ref2, _ = orc.sparse_prior(c.q, c.K, c.V, c.idx, c.mu_Q, lam, *built, prior_n=n0)
+        assert rel_err(ref2, ref) <= 1e-10
+        assert rel_err(out, ref) <= TOL, lam
+        assert lse_err(lse, ref_lse) <= LSE_TOL, lam
