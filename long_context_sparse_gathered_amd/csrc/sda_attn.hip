@@ -487,32 +487,41 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   __shared__ __attribute__((aligned(16))) unsigned char s_vt[W][NT][kVTile];
 
   // ---- prologue ------------------------------------------------------------
-  const int64_t qrow0 = (int64_t)s * p.Hq + (int64_t)g * G;
-  uint4 qa[4];  // MFMA A operand: head r16 (zero past G), dims 32*st + 8*sub
-#pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    qa[st] = make_uint4(0, 0, 0, 0);
-    if (r16 < G)
-      qa[st] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(p.q) + (qrow0 + r16) * kD +
-                                                32 * st + 8 * sub);
-  }
-  float qf[PROXY ? G : 1][8];  // row-layout query for the cluster-sum logits
-  if constexpr (PROXY) load_query<bf16_t, G>(p.q, qrow0, r16, p.qscale, qf);
-
+  // Every load that does not depend on the list is issued before the first
+  // use of any loaded value, in one branch-free block: the query, the list
+  // entries and the cluster sums share a single memory round trip. (With no
+  // list, and for absent optional arrays, the loads read a valid dummy
+  // address and the values are discarded.)
   const int64_t lbase = (int64_t)u * p.m;
   const int e = w * CH + lane;
   const bool in_list = (lane < CH) && (e < p.m);
-  int li = -1, lp = -1, lc = -1;
-  float lwv = 0.f;
-  if (p.m > 0) {
-    const int64_t ea = lbase + (in_list ? e : 0);
-    li = p.idx[ea];
-    if constexpr (PROXY) {
-      lp = p.idx[lbase + ((in_list && e > 0) ? e - 1 : 0)];
-      if (p.idx_cluster) lc = p.idx_cluster[ea];
-    }
-    if (p.logw) lwv = p.logw[ea];
+  const int32_t* lst = p.m > 0 ? p.idx : reinterpret_cast<const int32_t*>(p.q);
+  const int64_t ea = lbase + (in_list ? e : 0);
+  int li = lst[ea];
+  int lp = -1, lc = -1;
+  if constexpr (PROXY) {
+    lp = lst[lbase + ((in_list && e > 0) ? e - 1 : 0)];
+    lc = (p.idx_cluster ? p.idx_cluster : lst)[ea];
   }
+  const float lwv = (p.logw ? p.logw : reinterpret_cast<const float*>(lst))[ea];
+  // the rows this lane fetches: key tile t takes entry 16t + r16, value slot
+  // k entry 4k + sub (read straight from the list: no shuffle round trips)
+  auto entry = [&](int pos) { return w * CH + pos; };
+  auto listed = [&](int pos) { return pos < CH && entry(pos) < p.m; };
+  int jk[NT], jv[NS];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) jk[t] = lst[lbase + (listed(16 * t + r16) ? entry(16 * t + r16) : 0)];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) jv[k] = lst[lbase + (listed(4 * k + sub) ? entry(4 * k + sub) : 0)];
+
+  const int64_t qrow0 = (int64_t)s * p.Hq + (int64_t)g * G;
+  uint4 qa[4];  // MFMA A operand: head r16 (zero past G), dims 32*st + 8*sub
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+    qa[st] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(p.q) + (qrow0 + hr) * kD + 32 * st +
+                                             8 * sub);
+  float qf[PROXY ? G : 1][8];  // row-layout query for the cluster-sum logits
+  if constexpr (PROXY) load_query<bf16_t, G>(p.q, qrow0, r16, p.qscale, qf);
 
   // cluster sums and counts of the two clusters this lane owns: b0 = 4w + sub
   // and b1 = b0 + 32 (dims 8*r16 .. +8 of the sums)
@@ -521,18 +530,15 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   float skf[8], svf[8], sk1[8], sv1[8];
   int cnt0 = 0, cnt1 = 0;
   if constexpr (PROXY) {
-    const int64_t rb = ((int64_t)u * p.C + (has0 ? b0 : 0)) * kD + 8 * r16;
-    load8f(p.sumK + rb, skf);
-    load8f(p.sumV + rb, svf);
-    cnt0 = p.count[(int64_t)u * p.C + (has0 ? b0 : 0)];
+    const int64_t c0 = (int64_t)u * p.C + (has0 ? b0 : 0);
+    load8f(p.sumK + c0 * kD + 8 * r16, skf);
+    load8f(p.sumV + c0 * kD + 8 * r16, svf);
+    cnt0 = p.count[c0];
     if (has1) {
-      const int64_t rb1 = ((int64_t)u * p.C + b1) * kD + 8 * r16;
-      load8f(p.sumK + rb1, sk1);
-      load8f(p.sumV + rb1, sv1);
-      cnt1 = p.count[(int64_t)u * p.C + b1];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sk1[i] = sv1[i] = 0.f;
+      const int64_t c1 = (int64_t)u * p.C + b1;
+      load8f(p.sumK + c1 * kD + 8 * r16, sk1);
+      load8f(p.sumV + c1 * kD + 8 * r16, sv1);
+      cnt1 = p.count[c1];
     }
   }
 
@@ -546,41 +552,35 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     len = L;
   }
 
-  // ---- addresses --------------------------------------------------------------
+  // ---- addresses ------------------------------------------------------------
+  // The unit's rows span less than 2^31 bytes (checked on the host), so byte
+  // offsets are 32-bit; an absent row reads past the resource and returns
+  // zeros.
   const bool live = in_list && e < len;
   const bool in_range = (unsigned)li < (unsigned)p.n;
   const bool valid = live && in_range;
-  const float lw_own = valid ? (p.logw ? lwv * kLog2e : 0.f) : kNegInf;
-  const bool bad_cluster = PROXY && p.idx_cluster && valid && (lc < -1 || lc >= p.C);
-  if (bad_cluster) lc = -1;
-
+  const int rs = 2 * (int)p.sn;
+  // (an unpredictable select keeps each product unconditional: left to
+  // itself the compiler branches around it)
+  auto row_byte = [&](int pos, int j, int c) {
+    const bool ok = (pos < CH) & (entry(pos) < len) & ((unsigned)j < (unsigned)p.n);
+    return __builtin_unpredictable(ok) ? j * rs + c : kOOB;
+  };
   int koff[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int src = 16 * t + r16;
-    const int j = shfl_i(li, src);
-    const bool ok = shfl_i(valid ? 1 : 0, src) != 0;
-    koff[t] = ok ? (int)(((int64_t)j * p.sn + 8 * sub) * 2) : kOOB;
-  }
+  for (int t = 0; t < NT; ++t) koff[t] = row_byte(16 * t + r16, jk[t], 16 * sub);
+  // value slot k = 4t + kq (entries 16t + 4kq + sub) fills tile t, rows
+  // 4kq .. 4kq+3: lane (sub, r16) lands at row 4kq + sub, chunk position r16,
+  // so it fetches the chunk that the swizzle puts there
   int voff[NS];
 #pragma unroll
-  for (int k = 0; k < NS; ++k) {
-    const int src = 4 * k + sub;
-    const int j = shfl_i(li, src);
-    const bool ok = shfl_i(valid ? 1 : 0, src) != 0;
-    voff[k] = ok ? row_off<bf16_t>(j, p.sn, r16) : kOOB;
-  }
+  for (int k = 0; k < NS; ++k) voff[k] = row_byte(4 * k + sub, jv[k], 16 * vt_chunk(4 * (k & 3) + sub, r16));
 
-  // ---- checks and cluster lookups, ahead of the row loads ------------------
-  {
-    int bad = 0;
-    if (live && !in_range) bad |= SDA_FLAG_IDX_RANGE;
-    if (PROXY && live && e > 0 && lp >= li) bad |= SDA_FLAG_IDX_ORDER;
-    if (bad_cluster) bad |= SDA_FLAG_CLUSTER;
-    if (bad) flag_unit(p.flags, u, bad);
-  }
+  // cluster of this lane's entry from the per-row ids when the list carries
+  // none: issued ahead of the row loads, so that its use does not wait for
+  // them (loads complete in issue order)
   if constexpr (PROXY) {
-    if (!p.idx_cluster) lc = valid ? p.cluster_id[(int64_t)u * p.n + (valid ? li : 0)] : -1;
+    if (!p.idx_cluster) lc = valid ? p.cluster_id[(int64_t)u * p.n + li] : -1;
   }
 
   // ---- row loads (streaming: read once) -------------------------------------
@@ -595,15 +595,34 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
       auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[t] + 64 * st, 0, kLoadNT);
       kt[t][st] = make_uint4(v[0], v[1], v[2], v[3]);
     }
-  // value slot k = 4t + kq (entries 16t + 4kq + sub) fills tile t, rows
-  // 4kq .. 4kq+3: lane (sub, r16) lands at row 4kq + sub, chunk position r16,
-  // so it fetches the chunk that the swizzle puts there
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
-    const int t = k >> 2, kq = k & 3;
-    const int off = voff[k] == kOOB ? kOOB : voff[k] - 16 * r16 + 16 * vt_chunk(4 * kq + sub, r16);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)&s_vt[w][t][kq * 1024], 16, off,
-                                             0, 0, kLoadNT);
+    const int off = voff[k];  // (a plain local: the host pass mishandles an array element here)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)&s_vt[w][k >> 2][(k & 3) * 1024],
+                                             16, off, 0, 0, kLoadNT);
+  }
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+    if (r16 >= G) qa[st] = make_uint4(0, 0, 0, 0);
+
+  // ---- checks and cluster lookups, behind the row loads ---------------------
+  const float lw_own = valid ? (p.logw ? lwv * kLog2e : 0.f) : kNegInf;
+  const bool bad_cluster = PROXY && p.idx_cluster && valid && (lc < -1 || lc >= p.C);
+  if (bad_cluster) lc = -1;
+  {
+    int bad = 0;
+    if (live && !in_range) bad |= SDA_FLAG_IDX_RANGE;
+    if (PROXY && live && e > 0 && lp >= li) bad |= SDA_FLAG_IDX_ORDER;
+    if (bad_cluster) bad |= SDA_FLAG_CLUSTER;
+    if (bad) flag_unit(p.flags, u, bad);
+  }
+  if constexpr (PROXY) {
+    if (!has0) cnt0 = 0;
+    if (!has1) {
+      cnt1 = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sk1[i] = sv1[i] = 0.f;
+    }
   }
   float qk0 = 0.f, qk1 = 0.f;  // q . (sum of keys) of clusters b0, b1 for head r16
   if constexpr (PROXY) {
