@@ -72,6 +72,32 @@ __device__ __forceinline__ void dot_heads(const float (&qf)[G][8], const float (
 }
 
 __device__ __forceinline__ int shfl_i(int v, int src) { return __shfl(v, src, 64); }
+// DPP move within 16-lane rows; lanes whose source lies outside the row
+// receive zero.
+template <int CTRL>
+__device__ __forceinline__ float dppz(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+// 4 x 4 transpose of (row group, register): out[j] of row group r is in[r]
+// of row group j. v_permlane32_swap exchanges row groups 2-3 of its first
+// operand with 0-1 of its second, v_permlane16_swap the odd row groups of
+// the first with the even ones of the second.
+__device__ __forceinline__ void transpose_rows(const float (&in)[4], float (&out)[4]) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(in[0]), __float_as_uint(in[2]), false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(in[1]), __float_as_uint(in[3]), false, false);
+  auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  out[0] = __uint_as_float(c[0]);
+  out[1] = __uint_as_float(c[1]);
+  out[2] = __uint_as_float(d[0]);
+  out[3] = __uint_as_float(d[1]);
+}
+// Integer DPP move within 16-lane rows; lanes whose source lies outside the
+// row receive `edge`.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v, int edge) {
+  return __builtin_amdgcn_update_dpp(edge, v, CTRL, 0xF, 0xF, false);
+}
 __device__ __forceinline__ float shfl_f(float v, int src) { return __shfl(v, src, 64); }
 
 // ---------------------------------------------------------------------------
@@ -672,11 +698,39 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
       // lanes of the row group); the last lane of each run adds the run total
       const int cm = (key_ok && ck >= 0 && ck < p.C) ? ck : -1;
       if (sub == 0) s_kc[w][kk] = cm;
-      if (cm >= 0) {
+      // run start: the first lane of the row group, or a change of cluster
+      // from the lane before; then a max-scan gives each lane its run's start
+      const int cprev = dpp_i<0x111>(cm, -2), cnext = dpp_i<0x101>(cm, -2);  // row_shr:1, row_shl:1
+      int start = cprev != cm ? r16 : 0;
+      start = max(start, dpp_i<0x111>(start, 0));
+      start = max(start, dpp_i<0x112>(start, 0));
+      start = max(start, dpp_i<0x114>(start, 0));
+      start = max(start, dpp_i<0x118>(start, 0));
+      // heads to row groups: after the transpose, row group sub holds head
+      // 4j + sub in hv[j] (the MFMA left heads 4*sub + i in sv[i])
+      constexpr int NV = G < 4 ? 1 : G / 4;
+      float hv[4];
+      transpose_rows(sv, hv);
+      // inclusive sums within runs (Hillis-Steele: a step takes the partial
+      // of the lane s back only while that lane is in the same run). Every
+      // lane takes part in every move (a 0/1 factor, not a branch: a move
+      // must not read a lane that sits out), and the partials are finite.
+      const float f1 = r16 - 1 >= start ? 1.f : 0.f, f2 = r16 - 2 >= start ? 1.f : 0.f;
+      const float f4 = r16 - 4 >= start ? 1.f : 0.f, f8 = r16 - 8 >= start ? 1.f : 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * sub + i < G) lds_add(&s_csum[w][cm][4 * sub + i], sv[i]);
-        if (sub == 0) lds_add(&s_ccnt[w][cm], 1);
+      for (int j = 0; j < NV; ++j) {
+        float x = hv[j];
+        x = fmaf(f1, dppz<0x111>(x), x);
+        x = fmaf(f2, dppz<0x112>(x), x);
+        x = fmaf(f4, dppz<0x114>(x), x);
+        x = fmaf(f8, dppz<0x118>(x), x);
+        hv[j] = x;
+      }
+      if (cm >= 0 && cnext != cm) {  // last lane of a run
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+          if (4 * j + sub < G) lds_add(&s_csum[w][cm][4 * j + sub], hv[j]);
+        if (sub == 0) lds_add(&s_ccnt[w][cm], r16 - start + 1);
       }
     }
   }
