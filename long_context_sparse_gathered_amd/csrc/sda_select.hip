@@ -20,20 +20,78 @@ namespace sda {
 
 // Wave-wide reductions by butterfly: at every step a lane and its partner add
 // (or compare) the same two values, so all lanes end with the same bits.
+// Wave reductions from register-to-register lane moves (no LDS round trips):
+// DPP quad permutes and mirrors within each 16-lane row, then the row-swap
+// instructions across rows. Each step combines a pair of lanes in both
+// orders, so every lane ends with the same bits.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint64_t lo = dpp_u32<CTRL>((uint32_t)b), hi = dpp_u32<CTRL>((uint32_t)(b >> 32));
+  return __longlong_as_double((long long)((hi << 32) | lo));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_int(int v) {
+  return (int)dpp_u32<CTRL>((uint32_t)v);
+}
+// (even-row value, odd-row value) for row pairs 0-1 and 2-3 (16-lane swap)
+// or 0-2 and 1-3 (32-lane swap), the same on every lane of a pair.
+template <bool S32>
+__device__ __forceinline__ void row_pair_u32(uint32_t v, uint32_t& e, uint32_t& o) {
+  if constexpr (S32) {
+    auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    e = r[0];
+    o = r[1];
+  } else {
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    e = r[0];
+    o = r[1];
+  }
+}
+template <bool S32>
+__device__ __forceinline__ void row_pair(double v, double& e, double& o) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  uint32_t el, ol, eh, oh;
+  row_pair_u32<S32>((uint32_t)b, el, ol);
+  row_pair_u32<S32>((uint32_t)(b >> 32), eh, oh);
+  e = __longlong_as_double((long long)(((uint64_t)eh << 32) | el));
+  o = __longlong_as_double((long long)(((uint64_t)oh << 32) | ol));
+}
+template <bool S32>
+__device__ __forceinline__ void row_pair(int v, int& e, int& o) {
+  uint32_t a, b;
+  row_pair_u32<S32>((uint32_t)v, a, b);
+  e = (int)a;
+  o = (int)b;
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  if constexpr (sizeof(T) == 8) {
+    v = op(v, dpp_f64<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = op(v, dpp_f64<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = op(v, dpp_f64<0x141>(v));  // row_half_mirror
+    v = op(v, dpp_f64<0x140>(v));  // row_mirror
+  } else {
+    v = op(v, dpp_int<0xB1>(v));
+    v = op(v, dpp_int<0x4E>(v));
+    v = op(v, dpp_int<0x141>(v));
+    v = op(v, dpp_int<0x140>(v));
+  }
+  T e, o;
+  row_pair<false>(v, e, o);
+  v = op(e, o);
+  row_pair<true>(v, e, o);
+  return op(e, o);
+}
 __device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+  return wave_reduce(v, [](double a, double b) { return a + b; });
 }
 __device__ __forceinline__ int wave_sum_i32(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
-__device__ __forceinline__ double lane_f64(double v, int l) {
-  const uint64_t b = __double_as_longlong(v);
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, l), hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), l);
-  return __longlong_as_double(((uint64_t)hi << 32) | lo);
+  return wave_reduce(v, [](int a, int b) { return a + b; });
 }
 
 // 16 bytes read once (non-temporal).
@@ -44,9 +102,7 @@ __device__ __forceinline__ uint4 load_nt_u4(const void* p) {
 }
 
 __device__ __forceinline__ double wave_max_f64(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off, 64));
-  return v;
+  return wave_reduce(v, [](double a, double b) { return fmax(a, b); });
 }
 
 // ---------------------------------------------------------------------------
@@ -191,8 +247,16 @@ hipError_t launch_qgs_build(const QgsBuildParams& p, int dtype, int units, hipSt
 //
 // The unit's query, basis and cluster sums are first staged in LDS with
 // coalesced loads; the fp64 loops then read LDS only.
+// Rows of the query and of the staged cluster sums in LDS: dims 0-63, four
+// pad floats, dims 64-127 (and four spare), so that the lanes of a wave that
+// read the same dim of different clusters, heads and 32-dim parts hit
+// distinct banks.
+constexpr int kPadRow = kD + 8;
+static_assert(kD == 128, "the padded rows assume 128 dims");
+__device__ __forceinline__ int pad_at(int d) { return d + ((d >> 6) << 2); }
+
 struct PrepLds {
-  float qf[kQgsMaxG][kD];
+  float qf[kQgsMaxG][kPadRow];
   float u[kD * kQgsRank];
   double w[kQgsMaxG][kQgsRank];
   double top[kCmax][kQgsMaxG];
@@ -203,11 +267,12 @@ struct PrepLds {
   double wmax;
   int loc[kCmax];
   int avail[kCmax];
-  // followed in LDS by the cluster sums: sumK [C][kD], then sumK2 [C][kD] (fp32)
+  int cnt[kCmax];  // cluster sizes N_b
+  // followed in LDS by the cluster sums: sumK [C][kPadRow], then sumK2 [C][kPadRow] (fp32)
 };
 
 __host__ __device__ inline size_t prep_lds_bytes(int C) {
-  return (sizeof(PrepLds) + 15) / 16 * 16 + (size_t)2 * C * kD * sizeof(float);
+  return (sizeof(PrepLds) + 15) / 16 * 16 + (size_t)2 * C * kPadRow * sizeof(float);
 }
 
 template <typename T>
@@ -232,20 +297,24 @@ __device__ void prep_unit(const QgsSelectParams& p, int u, PrepLds& L, float* su
   const T* q = reinterpret_cast<const T*>(p.q) + ((int64_t)s * p.Hq + (int64_t)g * G) * kD;
   const double* km = p.kmax + (int64_t)u * kQgsRank;
   float* sk = sums;
-  float* sk2 = sums + C * kD;
+  float* sk2 = sums + C * kPadRow;
 
-  for (int t = tid; t < G * kD; t += nt) L.qf[t / kD][t % kD] = elem_f32<T>(q, t);
+  for (int t = tid; t < G * kD; t += nt) L.qf[t / kD][pad_at(t % kD)] = elem_f32<T>(q, t);
   {
     const float4* src = reinterpret_cast<const float4*>(p.U + (int64_t)u * kD * kQgsRank);
     for (int t = tid; t < kD * kQgsRank / 4; t += nt) reinterpret_cast<float4*>(L.u)[t] = src[t];
     const float4* s1 = reinterpret_cast<const float4*>(p.sumK + (int64_t)u * C * kD);
     const float4* s2 = reinterpret_cast<const float4*>(p.sumK2 + (int64_t)u * C * kD);
     for (int t = tid; t < C * kD / 4; t += nt) {
-      reinterpret_cast<float4*>(sk)[t] = s1[t];
-      reinterpret_cast<float4*>(sk2)[t] = s2[t];
+      const int c4 = t & 31, at = (t >> 5) * (kPadRow / 4) + c4 + (c4 >> 4);
+      reinterpret_cast<float4*>(sk)[at] = s1[t];
+      reinterpret_cast<float4*>(sk2)[at] = s2[t];
     }
   }
-  for (int c = tid; c < C; c += nt) L.loc[c] = 0;
+  for (int c = tid; c < C; c += nt) {
+    L.loc[c] = 0;
+    L.cnt[c] = p.count[(int64_t)u * C + c];
+  }
   // cluster ids of the always-read sink and local window (counted below)
   const int32_t* cidu = p.cid + (int64_t)u * p.n;
   const int sink_end = min(p.n_sink, p.n);
@@ -268,7 +337,7 @@ __device__ void prep_unit(const QgsSelectParams& p, int u, PrepLds& L, float* su
       float qv[16], uv[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        qv[e] = L.qf[h][d0 + e];
+        qv[e] = L.qf[h][pad_at(d0) + e];
         uv[e] = L.u[(d0 + e) * kQgsRank + i];
       }
 #pragma unroll
@@ -285,15 +354,15 @@ __device__ void prep_unit(const QgsSelectParams& p, int u, PrepLds& L, float* su
     const bool on = t < C * G * 4;
     const int pair = on ? t >> 2 : 0, part = t & 3;
     const int b = pair / G, h = pair - b * G;
-    const int N = on ? p.count[(int64_t)u * C + b] : 0;
+    const int N = on ? L.cnt[b] : 0;
     const double inv = N > 0 ? 1.0 / (double)N : 0.0;
     double zb = 0.0, v2 = 0.0;
     if (N > 0) {
 #pragma unroll 8
       for (int d = 32 * part; d < 32 * part + 32; ++d) {
-        const double qd = (double)L.qf[h][d];
-        const double mu = (double)sk[b * kD + d] * inv;
-        const double nu = fmax((double)sk2[b * kD + d] * inv - mu * mu, 0.0);
+        const double qd = (double)L.qf[h][pad_at(d)];
+        const double mu = (double)sk[b * kPadRow + pad_at(d)] * inv;
+        const double nu = fmax((double)sk2[b * kPadRow + pad_at(d)] * inv - mu * mu, 0.0);
         zb = fma(qd, mu, zb);
         v2 = fma(qd * qd, nu, v2);
       }
@@ -370,7 +439,7 @@ __device__ void prep_unit(const QgsSelectParams& p, int u, PrepLds& L, float* su
     wq_out[h * (kQgsRank / 4) + k] = word;
   }
   if (tid < C) {
-    const int N = p.count[(int64_t)u * C + tid];
+    const int N = L.cnt[tid];
     double eps = 0.0;
     if (N > 0) {
       for (int h = 0; h < G; ++h) eps += L.e[tid][h] / L.Z[h];
@@ -402,11 +471,26 @@ __device__ void prep_unit(const QgsSelectParams& p, int u, PrepLds& L, float* su
       const int ib = (int)base;
       const int rem = R - wave_sum_i32(ib);
       const double fr = act ? frac : -1.0;
+      // rank of this lane's remainder among the active ones (larger first,
+      // ties to the lower cluster), from LDS broadcast reads
+      L.frac[lane] = fr;
+      wave_lds_sync();
+      // (eight reads in flight, then branch-free compares; every lane wrote
+      // its entry, -1 when inactive)
       int rank = 0;
-      for (int b = 0; b < C; ++b) {
-        const double fb = lane_f64(fr, b);
-        if (fb >= 0.0 && (fb > frac || (fb == frac && b < lane))) ++rank;
+#pragma unroll
+      for (int b0 = 0; b0 < kCmax; b0 += 8) {
+        if (b0 >= C) break;
+        double f8[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) f8[k] = L.frac[b0 + k];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const double fb = f8[k];
+          rank += (int)((fb >= 0.0) & ((fb > frac) | ((fb == frac) & (b0 + k < lane))));
+        }
       }
+      wave_lds_sync();
       const int tent = ib + ((act && rank < rem) ? 1 : 0);
       const bool over = act && tent > Ab;
       if (__ballot(over) == 0) {
