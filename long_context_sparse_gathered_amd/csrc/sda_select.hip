@@ -38,6 +38,11 @@ template <int CTRL>
 __device__ __forceinline__ int dpp_int(int v) {
   return (int)dpp_u32<CTRL>((uint32_t)v);
 }
+// Integer DPP move whose lanes with a source outside the row receive zero.
+template <int CTRL>
+__device__ __forceinline__ int dppz_int(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
 // (even-row value, odd-row value) for row pairs 0-1 and 2-3 (16-lane swap)
 // or 0-2 and 1-3 (32-lane swap), the same on every lane of a pair.
 template <bool S32>
@@ -620,11 +625,19 @@ __device__ __forceinline__ void sel_resolve(SelState& S, const int* hist, int C,
     const int chi = 2 * lane + 1 < nb ? hist[c * nb + 2 * lane + 1] : 0;
     const int clo = 2 * lane < nb ? hist[c * nb + 2 * lane] : 0;
     const int pair = chi + clo;
-    int incl = pair;  // rows in this lane's bins and every higher bin
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int v = __shfl_down(incl, off, 64);
-      if (lane + off < 64) incl += v;
+    // rows in this lane's bins and every higher bin: a suffix scan within
+    // each 16-lane row (DPP shifts toward lower lanes, zero past the row),
+    // then the totals of the rows above, read from their first lanes
+    int incl = pair;
+    incl += dppz_int<0x101>(incl);  // row_shl:1
+    incl += dppz_int<0x102>(incl);  // row_shl:2
+    incl += dppz_int<0x104>(incl);  // row_shl:4
+    incl += dppz_int<0x108>(incl);  // row_shl:8
+    {
+      const int t1 = __builtin_amdgcn_readlane(incl, 16), t2 = __builtin_amdgcn_readlane(incl, 32),
+                t3 = __builtin_amdgcn_readlane(incl, 48);
+      const int row = lane >> 4;
+      incl += (row < 1 ? t1 : 0) + (row < 2 ? t2 : 0) + (row < 3 ? t3 : 0);
     }
     const int excl = incl - pair;
     int t = -1, above = 0;
@@ -646,8 +659,8 @@ __device__ __forceinline__ void sel_resolve(SelState& S, const int* hist, int C,
       continue;
     }
     const int src = __builtin_ctzll(hit);
-    const int tb = __shfl(t, src, 64);
-    const int ab = __shfl(above, src, 64);
+    const int tb = __builtin_amdgcn_readlane(t, src);
+    const int ab = __builtin_amdgcn_readlane(above, src);
     if (lane == 0) {
       const int rest = need - ab;
       const uint64_t pref = S.pref[c] | ((uint64_t)tb << shift);
@@ -813,8 +826,7 @@ struct FusedState {
   int budget[kCmax];
   int avail[kCmax];
   int match[kCmax];
-  int thrA[kCmax];
-  int thrB[kCmax];
+  int2 thr[kCmax];  // (score threshold of a pick, boundary prefix of a candidate)
   int nsel, ncand;
   int picked[kFusedSel];
   int cand[kFusedCand];
@@ -937,12 +949,10 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
   const int lane = tid & 63, w = tid >> 6;
   if (tid < C) {
     if (S.done[tid]) {
-      F.thrA[tid] = (int)(S.T[tid] >> 20);
-      F.thrB[tid] = -1;
+      F.thr[tid] = make_int2((int)(S.T[tid] >> 20), -1);
     } else {
       const int P = (int)(S.pref[tid] >> (kKeyBits - 2 * W));
-      F.thrA[tid] = (P + 1) << (20 - 2 * W);
-      F.thrB[tid] = P;
+      F.thr[tid] = make_int2((P + 1) << (20 - 2 * W), P);
     }
   }
   if (tid == 0) {
@@ -955,7 +965,7 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
     if (bal) {
       int base = 0;
       if (lane == 0) base = atomicAdd(cnt, __popcll(bal));
-      base = __shfl(base, 0, 64);
+      base = __builtin_amdgcn_readfirstlane(base);
       const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
       if (on && pos < cap) list[pos] = j;
@@ -973,8 +983,9 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int c = (int)((rr[k] >> 20) & 127);
-        ta[k] = F.thrA[c < C ? c : 0];
-        tb[k] = F.thrB[c < C ? c : 0];
+        const int2 th = F.thr[c < C ? c : 0];
+        ta[k] = th.x;
+        tb[k] = th.y;
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
