@@ -117,9 +117,10 @@ constexpr int kSampMaxUnits = 4096;
 constexpr int kDrawGrid = 768;           // draw workgroups (upper bound): three per CU
 __host__ __device__ inline int sampled_max_items(int n) { return (n + kDrawChunk - 1) / kDrawChunk; }
 // Workgroups per unit that share the exact pass over I_f (about 256 in all).
+constexpr int kSampMaxSplits = 8;  // exact-part workgroups per unit (at most)
 inline int sampled_exact_splits(int units) {
   const int s = 256 / units;
-  return s < 1 ? 1 : (s > 8 ? 8 : s);
+  return s < 1 ? 1 : (s > kSampMaxSplits ? kSampMaxSplits : s);
 }
 hipError_t launch_proxy_build(const ProxyBuildParams& p, int dtype, int units, hipStream_t st);
 // Row chunks of the proxy builder: 4096 rows each (a workgroup holds C*2*kD

@@ -195,6 +195,7 @@ __global__ __launch_bounds__(512) void sampled_exact_kernel(const AttnParams p) 
 
   __shared__ double s_part[kW][G][kD];
   __shared__ double s_pm[kW][G], s_pd[kW][G];
+  __shared__ double s_wf[kW][G], s_wM[G];
 
   int mf = p.m;
   if (p.idx_len) {
@@ -311,7 +312,10 @@ __global__ __launch_bounds__(512) void sampled_exact_kernel(const AttnParams p) 
     for (int h = 0; h < G; ++h) {
       const RowPairD mm = pass ? swap_d<true>(mh[h]) : swap_d<false>(mh[h]);
       const double M = fmax(mm.even, mm.odd);
-      const double fa = rescale_d(mm.even, M), fb = rescale_d(mm.odd, M);
+      // the larger side scales by exp(0) = 1: one exponential per pair
+      const bool ev_big = mm.even >= mm.odd;
+      const double fs = rescale_d(ev_big ? mm.odd : mm.even, M);
+      const double fa = ev_big ? (M == -kInf ? 0.0 : 1.0) : fs, fb = ev_big ? fs : 1.0;
       const RowPairD dd = pass ? swap_d<true>(Df[h]) : swap_d<false>(Df[h]);
       Df[h] = dd.even * fa + dd.odd * fb;
 #pragma unroll
@@ -334,16 +338,24 @@ __global__ __launch_bounds__(512) void sampled_exact_kernel(const AttnParams p) 
     }
   }
   __syncthreads();
+  // the waves' scale factors, once per (wave, head)
+  if (tid < G) {
+    double M = -kInf;
+#pragma unroll
+    for (int ww = 0; ww < kW; ++ww) M = fmax(M, s_pm[ww][tid]);
+    s_wM[tid] = M;
+#pragma unroll
+    for (int ww = 0; ww < kW; ++ww) s_wf[ww][tid] = rescale_d(s_pm[ww][tid], M);
+  }
+  __syncthreads();
   double* rec = p.wexact + ((int64_t)u * p.splits + c) * G * (2 + kD);
   for (int e = tid; e < G * kD; e += 512) {
     const int h = e / kD, i = e - h * kD;
-    double M = -kInf;
-#pragma unroll
-    for (int ww = 0; ww < kW; ++ww) M = fmax(M, s_pm[ww][h]);
+    const double M = s_wM[h];
     double a = 0.0, d = 0.0;
 #pragma unroll
     for (int ww = 0; ww < kW; ++ww) {
-      const double f = rescale_d(s_pm[ww][h], M);
+      const double f = s_wf[ww][h];
       a += s_part[ww][h][i] * f;
       d += s_pd[ww][h] * f;
     }
@@ -375,6 +387,7 @@ __global__ __launch_bounds__(512) void sampled_stats_kernel(const AttnParams p) 
   __shared__ double s_Nf[G][kD], s_mN[G][kD];
   __shared__ double s_hs[G][4];           // per head: two halves of |Nhat|^2
   __shared__ double s_bh[G];
+  __shared__ double s_sf[kSampMaxSplits][G];  // the exact-part splits' scale factors
   __shared__ int s_b;
 
   // ---- the deterministic set, as A[i] = I_f[i] - i ---------------------------
@@ -435,25 +448,41 @@ __global__ __launch_bounds__(512) void sampled_stats_kernel(const AttnParams p) 
     }
   };
 
+  // the first batch of base rows (keys and values) goes out now, so that its
+  // latency overlaps the merge of the exact-part records below; the values
+  // stay in registers for the two passes over them
+  __syncthreads();  // the draw positions
+  RowChunk<T> kc0[NSB], vc0[NSB];
+#pragma unroll
+  for (int k = 0; k < NSB; ++k) {
+    const int r = 4 * (k * kW + w) + sub;
+    const int off = r < b0 ? off_of<T>(s_bj[r], p.sn, r16) : kOOBs;
+    gather(kc0[k], rk, off);
+    gather(vc0[k], rv, off);
+  }
+
   // ---- I_f: merge the exact-part records of the splits (log-sum-exp, fp64) ---
   {
     const double* rec = p.wexact + (int64_t)u * p.splits * G * (2 + kD);
+    // the splits' scale factors, once per (split, head)
+    if (tid < G) {
+      double M = -kInf;
+      for (int c = 0; c < p.splits; ++c) M = fmax(M, rec[(int64_t)c * G * (2 + kD) + tid]);
+      s_Mf[tid] = M;
+      for (int c = 0; c < p.splits; ++c) s_sf[c][tid] = rescale_d(rec[(int64_t)c * G * (2 + kD) + tid], M);
+    }
+    __syncthreads();
     for (int e = tid; e < G * kD; e += 512) {
       const int h = e / kD, i = e - h * kD;
-      double M = -kInf;
-      for (int c = 0; c < p.splits; ++c) M = fmax(M, rec[(int64_t)c * G * (2 + kD) + h]);
       double a = 0.0, d = 0.0;
       for (int c = 0; c < p.splits; ++c) {
         const double* rc = rec + (int64_t)c * G * (2 + kD);
-        const double f = rescale_d(rc[h], M);
+        const double f = s_sf[c][h];
         a += rc[2 * G + e] * f;
         d += rc[G + h] * f;
       }
       s_Nf[h][i] = a;
-      if (i == 0) {
-        s_Df[h] = d;
-        s_Mf[h] = M;
-      }
+      if (i == 0) s_Df[h] = d;
     }
   }
   __syncthreads();
@@ -467,7 +496,10 @@ __global__ __launch_bounds__(512) void sampled_stats_kernel(const AttnParams p) 
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
       const int r = rb + 4 * (k * kW + w) + sub;
-      gather(kc[k], rk, r < b0 ? off_of<T>(s_bj[r], p.sn, r16) : kOOBs);
+      if (rb == 0)
+        kc[k] = kc0[k];
+      else
+        gather(kc[k], rk, r < b0 ? off_of<T>(s_bj[r], p.sn, r16) : kOOBs);
     }
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
@@ -499,9 +531,11 @@ __global__ __launch_bounds__(512) void sampled_stats_kernel(const AttnParams p) 
     s_M[tid] = M;
   }
   __syncthreads();
+  if (tid < G) s_bh[tid] = rescale_d(s_Mf[tid], s_M[tid]);  // (s_bh reused before the budget)
+  __syncthreads();
   for (int e = tid; e < G * kD; e += 512) {
     const int h = e / kD, i = e - h * kD;
-    const double f = rescale_d(s_Mf[h], s_M[h]);
+    const double f = s_bh[h];
     s_Nf[h][i] *= f;
     if (i == 0) s_Df[h] *= f;
   }
@@ -516,7 +550,10 @@ __global__ __launch_bounds__(512) void sampled_stats_kernel(const AttnParams p) 
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
       const int r = rb + 4 * (k * kW + w) + sub;
-      gather(vc[k], rv, r < b0 ? off_of<T>(s_bj[r], p.sn, r16) : kOOBs);
+      if (rb == 0)
+        vc[k] = vc0[k];
+      else
+        gather(vc[k], rv, r < b0 ? off_of<T>(s_bj[r], p.sn, r16) : kOOBs);
     }
   };
   {
