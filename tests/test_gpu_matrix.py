@@ -182,3 +182,19 @@ def test_prior_on_grown_cache(orc, G):
         assert rel_err(ref2, ref) <= 1e-10
         assert rel_err(out, ref) <= TOL, lam
         assert lse_err(lse, ref_lse) <= LSE_TOL, lam
+
+
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_proxy_without_listed_rows(orc, G):
+    """m = 0: every unit's output is its cluster proxies alone (the
+    matrix-core unit kernel reads no list)."""
+    w = _grouped(synth.WORKLOADS["proxy_bf16_b1_n32k"], G, 2).replace(B=2, n=2048, n_top=40, C=13)
+    c = synth.make_case(w)
+    d = case_to_dev(c)
+    st = sda.build_tail_proxies(d["K"], d["V"], d["cid"], w.C)
+    idx = np.zeros((w.B, w.Hkv, 0), np.int32)
+    out, lse = sda.sparse_decode_attn(d["q"], d["K"], d["V"], to_dev(idx), tail=st, cluster_id=d["cid"])
+    _sync()
+    ref, ref_lse = orc.sparse_proxy_def(c.q, c.K, c.V, idx, c.cid, w.C)
+    assert rel_err(out, ref) <= TOL
+    assert lse_err(lse, ref_lse) <= LSE_TOL
