@@ -987,13 +987,45 @@ __global__ __launch_bounds__(kSelThreads) void qgs_fused_kernel(const QgsSelectP
         ta[k] = th.x;
         tb[k] = th.y;
       }
+      // all eight rows' decisions, then one reservation per list for the
+      // step (a reservation is an LDS round trip); rows are written only
+      // for the ballots that hold any
+      uint64_t bp[8], bc[8];
+      int np = 0, nc = 0;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int j = j0 + 64 * k + lane;
         const int s20 = (int)(rr[k] & 0xfffffu);
         const bool el = (j < r1) & ((rr[k] >> 27) & 1);
-        push(el & (s20 >= ta[k]), &F.nsel, F.picked, kFusedSel, j);
-        push(el & ((s20 >> (20 - 2 * W)) == tb[k]), &F.ncand, F.cand, kFusedCand, j);
+        bp[k] = __ballot(el & (s20 >= ta[k]));
+        bc[k] = __ballot(el & ((s20 >> (20 - 2 * W)) == tb[k]));
+        np += __popcll(bp[k]);
+        nc += __popcll(bc[k]);
+      }
+      if (np + nc > 0) {
+        int basep = 0, basec = 0;
+        if (lane == 0) {
+          if (np) basep = atomicAdd(&F.nsel, np);
+          if (nc) basec = atomicAdd(&F.ncand, nc);
+        }
+        basep = __builtin_amdgcn_readfirstlane(basep);
+        basec = __builtin_amdgcn_readfirstlane(basec);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int j = j0 + 64 * k + lane;
+          if (bp[k]) {
+            const int pos = basep + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bp[k] >> 32),
+                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bp[k], 0));
+            if (((bp[k] >> lane) & 1) && pos < kFusedSel) F.picked[pos] = j;
+            basep += __popcll(bp[k]);
+          }
+          if (bc[k]) {
+            const int pos = basec + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bc[k] >> 32),
+                                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)bc[k], 0));
+            if (((bc[k] >> lane) & 1) && pos < kFusedCand) F.cand[pos] = j;
+            basec += __popcll(bc[k]);
+          }
+        }
       }
     }
   }
