@@ -18,8 +18,6 @@
 
 namespace sda {
 
-// Wave-wide reductions by butterfly: at every step a lane and its partner add
-// (or compare) the same two values, so all lanes end with the same bits.
 // Wave reductions from register-to-register lane moves (no LDS round trips):
 // DPP quad permutes and mirrors within each 16-lane row, then the row-swap
 // instructions across rows. Each step combines a pair of lanes in both
