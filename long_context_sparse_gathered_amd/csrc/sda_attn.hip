@@ -511,6 +511,12 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   // partial sums.
   static_assert(G * kD * 4 <= kVTile, "partials must fit a tile");
   __shared__ __attribute__((aligned(16))) unsigned char s_vt[W][NT][kVTile];
+  // The cluster-sum tile (below) gets a per-wave buffer of its own where it
+  // fits next to the value tiles, so that it is written and read while the
+  // keys are still being processed; otherwise it reuses tile 0 late.
+  constexpr int kLdsOther = (W * G * KW + PW * PC * G + PW * PC + PC * G + PW * (PROXY ? KW : 4)) * 4 + 1024;
+  constexpr bool SEP = PROXY && (W * (NT + 1) * kVTile + kLdsOther <= 160 * 1024);
+  __shared__ __attribute__((aligned(16))) unsigned char s_pt[SEP ? W : 1][SEP ? kVTile : 16];
 
   // ---- prologue ------------------------------------------------------------
   // Every load that does not depend on the list is issued before the first
@@ -668,6 +674,36 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     }
   }
 
+  // Transposed tile reads (see the value phase) and the cluster-sum tile's
+  // rows: row `row` of a tile holds the bf16 high part (lo = false) or
+  // remainder of the eight sums of this lane's dims.
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  const int tr_row = 4 * sub + (r16 >> 2);
+  auto tile_read = [&](const unsigned char* tile, bf16x4_t (&b)[8]) {
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      auto src = (__attribute__((address_space(3))) bf16x4_t*)(tile + tr_row * 256 +
+                                                               16 * vt_chunk(tr_row, 2 * nb + ((r16 & 3) >> 1)) +
+                                                               8 * (r16 & 1));
+      b[nb] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(src);
+    }
+  };
+  auto put = [&](unsigned char* ct, int row, const float (&f)[8], bool lo) {
+    bf16x8_t v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 hi = (__bf16)f[i];
+      v[i] = lo ? (__bf16)(f[i] - (float)hi) : hi;
+    }
+    *reinterpret_cast<bf16x8_t*>(ct + row * 256 + 16 * vt_chunk(row, r16)) = v;
+  };
+  auto put_cluster_tile = [&](unsigned char* ct) {
+    put(ct, sub, svf, false);
+    put(ct, 4 + sub, svf, true);
+    put(ct, 8 + sub, sv1, false);
+    put(ct, 12 + sub, sv1, true);
+  };
+
   // ---- logits on the matrix cores ------------------------------------------
   float mx[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
@@ -740,6 +776,12 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     const int h = 4 * sub + i;
     if (r16 == 0 && h < G) s_wmax[w][h] = v;
   }
+  bf16x4_t bc[8];  // the cluster-sum tile's B operand
+  if constexpr (SEP) {
+    put_cluster_tile(&s_pt[w][0]);
+    wave_lds_sync();  // the tile's rows, written by other lanes
+    tile_read(&s_pt[w][0], bc);
+  }
   lds_barrier();
 
   // ---- proxy logits of the clusters this wave owns ------------------------
@@ -803,20 +845,9 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   // column 16*nb + n when lane s of the group points at row 4*sub + s/4,
   // column 16*nb + 4*(s%4). Each wave batches its LDS traffic: logits and
   // clusters of all tiles, then all weights, then all value reads.
-  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
   floatx4_t oacc[8];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) oacc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  const int tr_row = 4 * sub + (r16 >> 2);
-  auto tile_read = [&](const unsigned char* tile, bf16x4_t (&b)[8]) {
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      auto src = (__attribute__((address_space(3))) bf16x4_t*)(tile + tr_row * 256 +
-                                                               16 * vt_chunk(tr_row, 2 * nb + ((r16 & 3) >> 1)) +
-                                                               8 * (r16 & 1));
-      b[nb] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(src);
-    }
-  };
   auto tile_products = [&](const bf16x8_t a, const bf16x4_t (&b4)[8]) {
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
@@ -869,32 +900,22 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   bf16x4_t bv[NT][8];
 #pragma unroll
   for (int t = 0; t < NT; ++t) tile_read(&s_vt[w][t][0], bv[t]);
-  bf16x4_t bc[8];
   bf16x8_t acl;
   if constexpr (PROXY) {
     // Proxy value terms exp2(mu_b - M) * (sum of cluster b's values), as one
-    // more tile in the consumed tile 0: rows sub and 4 + sub hold the bf16
-    // high part and remainder of cluster b0's value sum, rows 8 + sub and
-    // 12 + sub those of cluster b1 (zero when absent); each row's weight is
-    // split as above. (The writes follow this wave's reads of tile 0.)
-    unsigned char* ct = &s_vt[w][0][0];
-    auto put = [&](int row, const float (&f)[8], bool lo) {
-      bf16x8_t v;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const __bf16 hi = (__bf16)f[i];
-        v[i] = lo ? (__bf16)(f[i] - (float)hi) : hi;
-      }
-      *reinterpret_cast<bf16x8_t*>(ct + row * 256 + 16 * vt_chunk(row, r16)) = v;
-    };
-    put(sub, svf, false);
-    put(4 + sub, svf, true);
-    put(8 + sub, sv1, false);
-    put(12 + sub, sv1, true);
+    // more tile: rows sub and 4 + sub hold the bf16 high part and remainder
+    // of cluster b0's value sum, rows 8 + sub and 12 + sub those of cluster
+    // b1 (zero when absent); each row's weight is split as above. Without a
+    // buffer of its own the tile goes into the consumed tile 0 (the writes
+    // follow this wave's reads of tile 0).
+    if constexpr (!SEP) {
+      unsigned char* ct = &s_vt[w][0][0];
+      put_cluster_tile(ct);
+      wave_lds_sync();  // the tile's rows, written by other lanes
+      tile_read(ct, bc);
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) split(acl, j, cws[j]);
-    wave_lds_sync();  // the tile's rows, written by other lanes
-    tile_read(ct, bc);
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) tile_products(aw[t], bv[t]);
