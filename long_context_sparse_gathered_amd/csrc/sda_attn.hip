@@ -470,7 +470,7 @@ __device__ __forceinline__ int vt_chunk(int r, int c) { return c ^ (2 * (r & 3))
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // LDS atomic adds without a return value. Written out so that the compiler
 // does not order them behind the loads that fill the value tiles (it treats
-// any LDS atomic as possibly overlapping those); the targets here never do.
+// them as possibly overlapping those); the targets here never do.
 __device__ __forceinline__ void lds_add(float* p, float v) {
   const unsigned a = (unsigned)(uintptr_t)(__attribute__((address_space(3))) float*)p;
   asm volatile("ds_add_f32 %0, %1" ::"v"(a), "v"(v) : "memory");
@@ -478,6 +478,12 @@ __device__ __forceinline__ void lds_add(float* p, float v) {
 __device__ __forceinline__ void lds_add(int* p, int v) {
   const unsigned a = (unsigned)(uintptr_t)(__attribute__((address_space(3))) int*)p;
   asm volatile("ds_add_u32 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+// A 16-bit LDS store, written out for the same reason.
+__device__ __forceinline__ void lds_store(unsigned char* p, __bf16 v) {
+  const unsigned a = (unsigned)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)p;
+  const unsigned x = __builtin_bit_cast(unsigned short, v);
+  asm volatile("ds_write_b16 %0, %1" ::"v"(a), "v"(x) : "memory");
 }
 
 template <int G, bool PROXY, int NT>
@@ -495,26 +501,34 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   const int CH = p.chunk;      // entries of this wave: [w*CH, (w+1)*CH), CH <= KW
   const int hr = r16 < G ? r16 : 0;  // head of this lane in the [head][..] layouts (clamped)
 
-  __shared__ __attribute__((aligned(16))) float s_x[W][G][KW];  // logits (log2 units), per wave
-  __shared__ __attribute__((aligned(16))) int s_kc[PW][PROXY ? KW : 4];  // cluster of each key, -1 if none
+  constexpr int NV = G < 4 ? 1 : G / 4;  // heads per lane in the key layout
+  constexpr int NP = (NT + 1) / 2;       // key tile pairs (the last may be single)
   __shared__ float s_wmax[W][G];
   __shared__ float s_pmax[PW][G];
   __shared__ float s_M[G];
   __shared__ float s_l[W][G];
   __shared__ float s_csum[PW][PC][G];
   __shared__ int s_ccnt[PW][PC];
-  __shared__ float s_mu[PC][G];  // mean logit of a cluster's unread members (-inf if none)
+  // mean logit of a cluster's unread members (-inf if none); row PC is a
+  // -inf sentinel for keys outside every cluster
+  __shared__ float s_mu[PC + 1][G];
+  // Weights handed from the key layout to the matrix-core layout: per wave,
+  // bf16 high part (0) and remainder (1), per pair of key tiles, head and
+  // group of four keys, 16 bytes: four keys of the even tile, then four of
+  // the odd one.
+  __shared__ __attribute__((aligned(16))) unsigned char s_wt[W][2][NP][G][4][16];
   // Value tiles, written by the row loads straight into LDS: per wave NT
   // tiles of 16 rows x 256 bytes, 16-byte chunks swizzled (vt_chunk) so that
   // the transposed reads are free of bank conflicts. After the products, tile
-  // 0 of each wave holds the cluster-sum tile and then the wave's [G][kD]
-  // partial sums.
+  // 0 of each wave holds the wave's [G][kD] partial sums (and, when the
+  // cluster-sum tile has no buffer of its own, that tile before them).
   static_assert(G * kD * 4 <= kVTile, "partials must fit a tile");
   __shared__ __attribute__((aligned(16))) unsigned char s_vt[W][NT][kVTile];
   // The cluster-sum tile (below) gets a per-wave buffer of its own where it
   // fits next to the value tiles, so that it is written and read while the
-  // keys are still being processed; otherwise it reuses tile 0 late.
-  constexpr int kLdsOther = (W * G * KW + PW * PC * G + PW * PC + PC * G + PW * (PROXY ? KW : 4)) * 4 + 1024;
+  // rows are still in flight; otherwise it reuses tile 0 late.
+  constexpr int kLdsOther =
+      (2 * W * G + PW * G + G + PW * PC * G + PW * PC + (PC + 1) * G) * 4 + W * 2 * NP * G * 64 + 256;
   constexpr bool SEP = PROXY && (W * (NT + 1) * kVTile + kLdsOther <= 160 * 1024);
   __shared__ __attribute__((aligned(16))) unsigned char s_pt[SEP ? W : 1][SEP ? kVTile : 16];
 
@@ -703,9 +717,25 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     put(ct, 8 + sub, sv1, false);
     put(ct, 12 + sub, sv1, true);
   };
+  // the cluster-sum tile's B operand; with a buffer of its own it is built
+  // now, while the rows are in flight
+  bf16x4_t bc[8];
+  if constexpr (SEP) {
+    put_cluster_tile(&s_pt[w][0]);
+    wave_lds_sync();  // the tile's rows, written by other lanes
+    tile_read(&s_pt[w][0], bc);
+  }
 
   // ---- logits on the matrix cores ------------------------------------------
-  float mx[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+  // The MFMA leaves lane (key r16, group sub) the logits of heads 4*sub + i;
+  // a 4 x 4 transpose of row groups turns that into the key layout used from
+  // here to the weights: lane (sub, r16) holds heads 4j + sub (j < NV) of key
+  // 16t + r16 of tile t, so each (head, key) pair sits in one lane only.
+  float xr[NT][NV];  // logit plus log-weight (log2 units)
+  int cmr[NT];       // cluster of the key, -1 if none
+  float mxr[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) mxr[j] = kNegInf;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     floatx4_t d = {0.f, 0.f, 0.f, 0.f};
@@ -713,27 +743,25 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     for (int st = 0; st < 4; ++st)
       d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
                                                   __builtin_bit_cast(bf16x8_t, kt[t][st]), d, 0, 0, 0);
-    const int kk = 16 * t + r16;            // this lane's key within the wave's entries
+    const int kk = 16 * t + r16;  // this lane's key within the wave's entries
     const float lwk = shfl_f(lw_own, kk);
-    const int ck = PROXY ? shfl_i(lc, kk) : -1;
-    const bool key_ok = lwk != kNegInf;
-    float sv[4];
+    float sv[4], hv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * sub + i;
-      sv[i] = d[i] * p.qscale;
-      if (h < G) {
-        const float xv = sv[i] + lwk;
-        s_x[w][h][kk] = xv;
-        mx[i] = fmaxf(mx[i], xv);
-      }
+    for (int i = 0; i < 4; ++i) sv[i] = d[i] * p.qscale;
+    transpose_rows(sv, hv);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      xr[t][j] = hv[j] + lwk;
+      mxr[j] = fmaxf(mxr[j], xr[t][j]);
     }
+    cmr[t] = -1;
     if constexpr (PROXY) {
       // read members' logit sums and counts per cluster (this wave's slice):
       // a segmented sum over runs of keys with the same cluster (consecutive
       // lanes of the row group); the last lane of each run adds the run total
-      const int cm = (key_ok && ck >= 0 && ck < p.C) ? ck : -1;
-      if (sub == 0) s_kc[w][kk] = cm;
+      const int ck = shfl_i(lc, kk);
+      const int cm = (lwk != kNegInf && ck >= 0 && ck < p.C) ? ck : -1;
+      cmr[t] = cm;
       // run start: the first lane of the row group, or a change of cluster
       // from the lane before; then a max-scan gives each lane its run's start
       const int cprev = dpp_i<0x111>(cm, -2), cnext = dpp_i<0x101>(cm, -2);  // row_shr:1, row_shl:1
@@ -742,11 +770,6 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
       start = max(start, dpp_i<0x112>(start, 0));
       start = max(start, dpp_i<0x114>(start, 0));
       start = max(start, dpp_i<0x118>(start, 0));
-      // heads to row groups: after the transpose, row group sub holds head
-      // 4j + sub in hv[j] (the MFMA left heads 4*sub + i in sv[i])
-      constexpr int NV = G < 4 ? 1 : G / 4;
-      float hv[4];
-      transpose_rows(sv, hv);
       // inclusive sums within runs (Hillis-Steele: a step takes the partial
       // of the lane s back only while that lane is in the same run). Every
       // lane takes part in every move (a 0/1 factor, not a branch: a move
@@ -771,16 +794,9 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float v = max16(mx[i]);
-    const int h = 4 * sub + i;
-    if (r16 == 0 && h < G) s_wmax[w][h] = v;
-  }
-  bf16x4_t bc[8];  // the cluster-sum tile's B operand
-  if constexpr (SEP) {
-    put_cluster_tile(&s_pt[w][0]);
-    wave_lds_sync();  // the tile's rows, written by other lanes
-    tile_read(&s_pt[w][0], bc);
+  for (int j = 0; j < NV; ++j) {
+    const float v = max16(mxr[j]);
+    if (r16 == 0 && 4 * j + sub < G) s_wmax[w][4 * j + sub] = v;
   }
   lds_barrier();
 
@@ -810,6 +826,7 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     };
     if (has0) mean_logit(b0, qk0, cnt0, pi0);
     if (has1) mean_logit(b1, qk1, cnt1, pi1);
+    if (w == 0 && sub == 0 && r16 < G) s_mu[PC][r16] = kNegInf;
     if (r16 >= G) pi0 = pi1 = kNegInf;
     const float pm = max_rowgroups(fmaxf(pi0, pi1));
     if (sub == 0 && r16 < G) s_pmax[w][r16] = pm;
@@ -817,7 +834,7 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   }
 
   // ---- unit maximum (every wave, same value) --------------------------------
-  float Mh = kNegInf;
+  float Mh = kNegInf;  // head hr
 #pragma unroll
   for (int ww = 0; ww < W; ++ww) {
     Mh = fmaxf(Mh, s_wmax[ww][hr]);
@@ -825,58 +842,45 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   }
   if (Mh == kNegInf) Mh = 0.f;
   if (w == 0 && sub == 0 && r16 < G) s_M[r16] = Mh;
-  // the proxies' share of the normaliser (lane sums, combined below)
+  float Mr[NV];  // the same in the key layout: head 4j + sub
+#pragma unroll
+  for (int j = 0; j < NV; ++j) Mr[j] = shfl_f(Mh, 4 * j + sub < G ? 4 * j + sub : 0);
+
+  // ---- weights, in the key layout -------------------------------------------
+  // w = exp2(x - M), minus exp2(mu_b - M) for a read member of cluster b
+  // (whose value the proxy term counts in the cluster's sum), stored as a
+  // bf16 high part and a bf16 remainder for the value products.
+  float lsr[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) lsr[j] = 0.f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int h = 4 * j + sub;
+      const float ev = fast_exp2(xr[t][j] - Mr[j]);
+      lsr[j] += ev;
+      float wv = ev;
+      if constexpr (PROXY) {
+        const float mu = s_mu[cmr[t] >= 0 ? cmr[t] : PC][h < G ? h : 0];
+        wv = ev - fast_exp2(mu - Mr[j]);
+      }
+      const __bf16 hi = (__bf16)wv;
+      const __bf16 lo = (__bf16)(wv - (float)hi);
+      if (h < G) {
+        const int at = 8 * (t & 1) + 2 * (r16 & 3);
+        lds_store(&s_wt[w][0][t >> 1][h][r16 >> 2][at], hi);
+        lds_store(&s_wt[w][1][t >> 1][h][r16 >> 2][at], lo);
+      }
+    }
+  }
+  // the proxies' share of the normaliser (lanes of head r16, clusters b0, b1)
   float lsum = 0.f;
+  float cws[4] = {0.f, 0.f, 0.f, 0.f};  // cluster-tile weights of the rows below
+  const bool head_lane = r16 < G;
   if constexpr (PROXY) {
     if (pi0 != kNegInf) lsum += fast_exp2(pi0 - Mh);
     if (pi1 != kNegInf) lsum += fast_exp2(pi1 - Mh);
-  }
-
-  // ---- weighted values on the matrix cores ---------------------------------
-  // One v_mfma_f32_16x16x32_bf16 per 16 keys and 16 dims. The weights
-  // w = exp2(x - M) (minus exp2(mu_b - M) for a read member of cluster b,
-  // whose value the proxy term counts in the cluster's sum) go in as a bf16
-  // high part and a bf16 remainder: lane (m = r16, group sub) holds, for head
-  // m and keys 4*sub + j, the high parts as A elements j and the remainders
-  // as elements 4 + j; the B operand repeats the four value elements, so one
-  // product sums both parts (about 16 significant bits of each weight, exact
-  // bf16 x bf16 products, fp32 accumulation). The values pass through LDS:
-  // ds_read_b64_tr_b16 gives lane n of group sub the rows 4*sub .. 4*sub+3 at
-  // column 16*nb + n when lane s of the group points at row 4*sub + s/4,
-  // column 16*nb + 4*(s%4). Each wave batches its LDS traffic: logits and
-  // clusters of all tiles, then all weights, then all value reads.
-  floatx4_t oacc[8];
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) oacc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  auto tile_products = [&](const bf16x8_t a, const bf16x4_t (&b4)[8]) {
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const bf16x8_t b = {b4[nb][0], b4[nb][1], b4[nb][2], b4[nb][3], b4[nb][0], b4[nb][1], b4[nb][2], b4[nb][3]};
-      oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, oacc[nb], 0, 0, 0);
-    }
-  };
-  auto split = [](bf16x8_t& a, int j, float v) {
-    const __bf16 hi = (__bf16)v;
-    a[j] = hi;
-    a[4 + j] = (__bf16)(v - (float)hi);
-  };
-  const bool head_lane = r16 < G;
-  float4 x4[NT];
-  int4 k4[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    x4[t] = *reinterpret_cast<const float4*>(&s_x[w][hr][16 * t + 4 * sub]);
-    if constexpr (PROXY) k4[t] = *reinterpret_cast<const int4*>(&s_kc[w][16 * t + 4 * sub]);
-  }
-  float mus[NT][4];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int kc[4] = {PROXY ? k4[t].x : -1, PROXY ? k4[t].y : -1, PROXY ? k4[t].z : -1, PROXY ? k4[t].w : -1};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) mus[t][j] = (PROXY && kc[j] >= 0) ? s_mu[kc[j]][hr] : kNegInf;
-  }
-  float cws[4] = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (PROXY) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int b = 4 * w + j + (sub >= 2 ? 4 * W : 0);
@@ -884,42 +888,71 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
       cws[j] = (head_lane && b < p.C && mu != kNegInf) ? fast_exp2(mu - Mh) : 0.f;
     }
   }
-  bf16x8_t aw[NT];
+
+  // ---- weighted values on the matrix cores ---------------------------------
+  // v_mfma_f32_16x16x32_bf16 with the values as B: ds_read_b64_tr_b16 gives
+  // lane n of group sub the tile rows 4*sub .. 4*sub+3 at column 16*nb + n
+  // when lane s of the group points at row 4*sub + s/4, column
+  // 16*nb + 4*(s%4). Two tiles share a product: B holds the four rows of
+  // tile a (elements 0-3) and of tile b (4-7), A (lane m = head, group sub)
+  // the matching weights, one product for the bf16 high parts and one for the
+  // remainders (about 16 significant bits of each weight, exact bf16 x bf16
+  // products, fp32 accumulation). A lone tile repeats its rows in both halves
+  // and takes the high parts and remainders in one product. The cluster-sum
+  // tile is the last tile: rows sub and 4 + sub hold the high part and
+  // remainder of cluster b0's value sum, rows 8 + sub and 12 + sub those of
+  // cluster b1 (zero when absent), weighted exp2(mu_b - M).
+  floatx4_t oacc[8];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const float xs[4] = {x4[t].x, x4[t].y, x4[t].z, x4[t].w};
+  for (int nb = 0; nb < 8; ++nb) oacc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  auto product = [&](const bf16x8_t a, const bf16x4_t (&ba)[8], const bf16x4_t (&bb)[8]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float ev = head_lane ? fast_exp2(xs[j] - Mh) : 0.f;
-      lsum += ev;
-      const float wv = (head_lane && mus[t][j] != kNegInf) ? ev - fast_exp2(mus[t][j] - Mh) : ev;
-      split(aw[t], j, wv);
+    for (int nb = 0; nb < 8; ++nb) {
+      const bf16x8_t b = __builtin_shufflevector(ba[nb], bb[nb], 0, 1, 2, 3, 4, 5, 6, 7);
+      oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, oacc[nb], 0, 0, 0);
     }
+  };
+  bf16x4_t chi, clo;  // cluster-tile weights, high parts and remainders
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    chi[j] = (__bf16)cws[j];
+    clo[j] = (__bf16)(cws[j] - (float)chi[j]);
   }
+  wave_lds_sync();  // the weights, written by other lanes
+  auto wt8 = [&](int hl, int t) {  // 4 keys of tile t (pair half t & 1)
+    return *reinterpret_cast<const bf16x4_t*>(&s_wt[w][hl][t >> 1][hr][sub][8 * (t & 1)]);
+  };
+  auto wt16 = [&](int hl, int pr) {  // 4 keys of both tiles of pair pr
+    return *reinterpret_cast<const bf16x8_t*>(&s_wt[w][hl][pr][hr][sub][0]);
+  };
   __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // the value tiles have landed
   bf16x4_t bv[NT][8];
 #pragma unroll
   for (int t = 0; t < NT; ++t) tile_read(&s_vt[w][t][0], bv[t]);
-  bf16x8_t acl;
-  if constexpr (PROXY) {
-    // Proxy value terms exp2(mu_b - M) * (sum of cluster b's values), as one
-    // more tile: rows sub and 4 + sub hold the bf16 high part and remainder
-    // of cluster b0's value sum, rows 8 + sub and 12 + sub those of cluster
-    // b1 (zero when absent); each row's weight is split as above. Without a
-    // buffer of its own the tile goes into the consumed tile 0 (the writes
-    // follow this wave's reads of tile 0).
-    if constexpr (!SEP) {
-      unsigned char* ct = &s_vt[w][0][0];
-      put_cluster_tile(ct);
-      wave_lds_sync();  // the tile's rows, written by other lanes
-      tile_read(ct, bc);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) split(acl, j, cws[j]);
+  if constexpr (PROXY && !SEP) {
+    // no buffer of its own: the tile goes into the consumed tile 0 (the
+    // writes follow this wave's reads of tile 0)
+    unsigned char* ct = &s_vt[w][0][0];
+    put_cluster_tile(ct);
+    wave_lds_sync();  // the tile's rows, written by other lanes
+    tile_read(ct, bc);
   }
 #pragma unroll
-  for (int t = 0; t < NT; ++t) tile_products(aw[t], bv[t]);
-  if constexpr (PROXY) tile_products(acl, bc);
+  for (int pr = 0; pr < NT / 2; ++pr) {
+    product(wt16(0, pr), bv[2 * pr], bv[2 * pr + 1]);
+    product(wt16(1, pr), bv[2 * pr], bv[2 * pr + 1]);
+  }
+  if constexpr (NT % 2 == 1) {
+    constexpr int t = NT - 1;
+    if constexpr (PROXY) {
+      product(__builtin_shufflevector(wt8(0, t), chi, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bc);
+      product(__builtin_shufflevector(wt8(1, t), clo, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bc);
+    } else {
+      product(__builtin_shufflevector(wt8(0, t), wt8(1, t), 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bv[t]);
+    }
+  } else if constexpr (PROXY) {
+    product(__builtin_shufflevector(chi, clo, 0, 1, 2, 3, 4, 5, 6, 7), bc, bc);
+  }
 
   // ---- per-wave partials, then the unit's combine ---------------------------
   // accumulator element i of lane (n, group sub): head 4*sub + i, dim 16*nb + n
@@ -932,8 +965,15 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
       for (int nb = 0; nb < 8; ++nb) red[h * kD + 16 * nb + r16] = oacc[nb][i];
     }
   }
-  lsum = sum_rowgroups(lsum);  // all keys and owned proxies of the wave, head r16
-  if (sub == 0 && r16 < G) s_l[w][r16] = lsum;
+  // normaliser of the wave: its keys (key layout) and owned proxies (head
+  // r16), gathered at the lanes of head 4j + sub
+  lsum = sum_rowgroups(lsum);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int h = 4 * j + sub;
+    const float tot = sum16(lsr[j]) + shfl_f(lsum, h < G ? h : 0);
+    if (r16 == 0 && h < G) s_l[w][h] = tot;
+  }
   __syncthreads();
 
   for (int ei = tid; ei < G * kD; ei += 512) {
