@@ -630,6 +630,8 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   }
 
   // ---- row loads (streaming: read once) -------------------------------------
+  // Keys first; the work below that needs no row runs while they are in
+  // flight (the memory queues are full by then), and the value loads follow.
   const int64_t kvoff = (int64_t)s * p.sb + (int64_t)g * p.sh;
   const rsrc_t rk = make_rsrc<bf16_t>(reinterpret_cast<const bf16_t*>(p.K) + kvoff, p.n, p.sn);
   const rsrc_t rv = make_rsrc<bf16_t>(reinterpret_cast<const bf16_t*>(p.V) + kvoff, p.n, p.sn);
@@ -642,16 +644,10 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
       kt[t][st] = make_uint4(v[0], v[1], v[2], v[3]);
     }
 #pragma unroll
-  for (int k = 0; k < NS; ++k) {
-    const int off = voff[k];  // (a plain local: the host pass mishandles an array element here)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)&s_vt[w][k >> 2][(k & 3) * 1024],
-                                             16, off, 0, 0, kLoadNT);
-  }
-#pragma unroll
   for (int st = 0; st < 4; ++st)
     if (r16 >= G) qa[st] = make_uint4(0, 0, 0, 0);
 
-  // ---- checks and cluster lookups, behind the row loads ---------------------
+  // ---- checks and cluster lookups, behind the key loads ---------------------
   const float lw_own = valid ? (p.logw ? lwv * kLog2e : 0.f) : kNegInf;
   const bool bad_cluster = PROXY && p.idx_cluster && valid && (lc < -1 || lc >= p.C);
   if (bad_cluster) lc = -1;
@@ -726,13 +722,60 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     tile_read(&s_pt[w][0], bc);
   }
 
+  // ---- per key tile: log-weight and cluster of this lane's key -------------
+  // (key layout, below) and the controls of the segmented sums over runs of
+  // keys with the same cluster (consecutive lanes of a row group). The read
+  // members' counts per cluster are added here; their logit sums follow the
+  // logits.
+  float lwk[NT];
+  int cmr[NT];  // cluster of the key, -1 if none
+  float sf[NT][4];
+  bool run_end[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int kk = 16 * t + r16;  // this lane's key within the wave's entries
+    lwk[t] = shfl_f(lw_own, kk);
+    cmr[t] = -1;
+    run_end[t] = false;
+    if constexpr (PROXY) {
+      const int ck = shfl_i(lc, kk);
+      const int cm = (lwk[t] != kNegInf && ck >= 0 && ck < p.C) ? ck : -1;
+      cmr[t] = cm;
+      // run start: the first lane of the row group, or a change of cluster
+      // from the lane before; then a max-scan gives each lane its run's start
+      const int cprev = dpp_i<0x111>(cm, -2), cnext = dpp_i<0x101>(cm, -2);  // row_shr:1, row_shl:1
+      int start = cprev != cm ? r16 : 0;
+      start = max(start, dpp_i<0x111>(start, 0));
+      start = max(start, dpp_i<0x112>(start, 0));
+      start = max(start, dpp_i<0x114>(start, 0));
+      start = max(start, dpp_i<0x118>(start, 0));
+      // 0/1 factors of the Hillis-Steele steps: a step takes the partial of
+      // the lane s back only while that lane is in the same run
+      sf[t][0] = r16 - 1 >= start ? 1.f : 0.f;
+      sf[t][1] = r16 - 2 >= start ? 1.f : 0.f;
+      sf[t][2] = r16 - 4 >= start ? 1.f : 0.f;
+      sf[t][3] = r16 - 8 >= start ? 1.f : 0.f;
+      run_end[t] = cm >= 0 && cnext != cm;  // last lane of a run
+      if (run_end[t] && sub == 0) lds_add(&s_ccnt[w][cm], r16 - start + 1);
+    }
+  }
+
+  // ---- value rows, straight into LDS ----------------------------------------
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const int off = voff[k];  // (a plain local: the host pass mishandles an array element here)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)&s_vt[w][k >> 2][(k & 3) * 1024],
+                                             16, off, 0, 0, kLoadNT);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
   // ---- logits on the matrix cores ------------------------------------------
   // The MFMA leaves lane (key r16, group sub) the logits of heads 4*sub + i;
   // a 4 x 4 transpose of row groups turns that into the key layout used from
   // here to the weights: lane (sub, r16) holds heads 4j + sub (j < NV) of key
   // 16t + r16 of tile t, so each (head, key) pair sits in one lane only.
   float xr[NT][NV];  // logit plus log-weight (log2 units)
-  int cmr[NT];       // cluster of the key, -1 if none
   float mxr[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) mxr[j] = kNegInf;
@@ -743,53 +786,33 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     for (int st = 0; st < 4; ++st)
       d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
                                                   __builtin_bit_cast(bf16x8_t, kt[t][st]), d, 0, 0, 0);
-    const int kk = 16 * t + r16;  // this lane's key within the wave's entries
-    const float lwk = shfl_f(lw_own, kk);
     float sv[4], hv[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) sv[i] = d[i] * p.qscale;
     transpose_rows(sv, hv);
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
-      xr[t][j] = hv[j] + lwk;
+      xr[t][j] = hv[j] + lwk[t];
       mxr[j] = fmaxf(mxr[j], xr[t][j]);
     }
-    cmr[t] = -1;
     if constexpr (PROXY) {
-      // read members' logit sums and counts per cluster (this wave's slice):
-      // a segmented sum over runs of keys with the same cluster (consecutive
-      // lanes of the row group); the last lane of each run adds the run total
-      const int ck = shfl_i(lc, kk);
-      const int cm = (lwk != kNegInf && ck >= 0 && ck < p.C) ? ck : -1;
-      cmr[t] = cm;
-      // run start: the first lane of the row group, or a change of cluster
-      // from the lane before; then a max-scan gives each lane its run's start
-      const int cprev = dpp_i<0x111>(cm, -2), cnext = dpp_i<0x101>(cm, -2);  // row_shr:1, row_shl:1
-      int start = cprev != cm ? r16 : 0;
-      start = max(start, dpp_i<0x111>(start, 0));
-      start = max(start, dpp_i<0x112>(start, 0));
-      start = max(start, dpp_i<0x114>(start, 0));
-      start = max(start, dpp_i<0x118>(start, 0));
-      // inclusive sums within runs (Hillis-Steele: a step takes the partial
-      // of the lane s back only while that lane is in the same run). Every
-      // lane takes part in every move (a 0/1 factor, not a branch: a move
-      // must not read a lane that sits out), and the partials are finite.
-      const float f1 = r16 - 1 >= start ? 1.f : 0.f, f2 = r16 - 2 >= start ? 1.f : 0.f;
-      const float f4 = r16 - 4 >= start ? 1.f : 0.f, f8 = r16 - 8 >= start ? 1.f : 0.f;
+      // read members' logit sums per cluster (this wave's slice): inclusive
+      // sums within runs (every lane takes part in every move: a 0/1 factor,
+      // not a branch, since a move must not read a lane that sits out; the
+      // partials are finite); the last lane of each run adds the run total
 #pragma unroll
       for (int j = 0; j < NV; ++j) {
         float x = hv[j];
-        x = fmaf(f1, dppz<0x111>(x), x);
-        x = fmaf(f2, dppz<0x112>(x), x);
-        x = fmaf(f4, dppz<0x114>(x), x);
-        x = fmaf(f8, dppz<0x118>(x), x);
+        x = fmaf(sf[t][0], dppz<0x111>(x), x);
+        x = fmaf(sf[t][1], dppz<0x112>(x), x);
+        x = fmaf(sf[t][2], dppz<0x114>(x), x);
+        x = fmaf(sf[t][3], dppz<0x118>(x), x);
         hv[j] = x;
       }
-      if (cm >= 0 && cnext != cm) {  // last lane of a run
+      if (run_end[t]) {
 #pragma unroll
         for (int j = 0; j < NV; ++j)
-          if (4 * j + sub < G) lds_add(&s_csum[w][cm][4 * j + sub], hv[j]);
-        if (sub == 0) lds_add(&s_ccnt[w][cm], r16 - start + 1);
+          if (4 * j + sub < G) lds_add(&s_csum[w][cmr[t]][4 * j + sub], hv[j]);
       }
     }
   }
