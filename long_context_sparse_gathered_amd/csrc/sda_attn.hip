@@ -520,9 +520,8 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   // Value tiles, written by the row loads straight into LDS: per wave NT
   // tiles of 16 rows x 256 bytes, 16-byte chunks swizzled (vt_chunk) so that
   // the transposed reads are free of bank conflicts. After the products, tile
-  // 0 of each wave holds the wave's [G][kD] partial sums (and, when the
-  // cluster-sum tile has no buffer of its own, that tile before them).
-  static_assert(G * kD * 4 <= kVTile, "partials must fit a tile");
+  // 0 of each wave holds the wave's partial sums (and, when the cluster-sum
+  // tile has no buffer of its own, that tile before them).
   __shared__ __attribute__((aligned(16))) unsigned char s_vt[W][NT][kVTile];
   // The cluster-sum tile (below) gets a per-wave buffer of its own where it
   // fits next to the value tiles, so that it is written and read while the
@@ -842,7 +841,7 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
       float mu = kNegInf;
       if (nb > 0) {
         const float nbf = (float)nb;
-        mu = (qk - ssum) / nbf;
+        mu = (qk - ssum) * __builtin_amdgcn_rcpf(nbf);  // (hardware reciprocal, ~1 ulp)
         pi = mu + __builtin_amdgcn_logf(nbf);
       }
       if (r16 < G) s_mu[b][r16] = mu;
@@ -857,11 +856,20 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   }
 
   // ---- unit maximum (every wave, same value) --------------------------------
-  float Mh = kNegInf;  // head hr
+  // Rows of the value products' A operand: with at most four heads, rows
+  // 0 .. G-1 take the weights' bf16 high parts and rows G .. 2G-1 their
+  // remainders (one product covers both; the two row sets are added in the
+  // combine), otherwise row h takes head h and the two parts take one product
+  // each. This lane's row: head ah, part al (rows past those: any finite
+  // weights, their outputs are dropped).
+  constexpr bool HLR = G <= 4;
+  const int ah = HLR ? (r16 < G ? r16 : (r16 < 2 * G ? r16 - G : 0)) : hr;
+  const int al = HLR && r16 >= G && r16 < 2 * G ? 1 : 0;
+  float Mh = kNegInf;  // head ah (= hr where r16 < G)
 #pragma unroll
   for (int ww = 0; ww < W; ++ww) {
-    Mh = fmaxf(Mh, s_wmax[ww][hr]);
-    if constexpr (PROXY) Mh = fmaxf(Mh, s_pmax[ww][hr]);
+    Mh = fmaxf(Mh, s_wmax[ww][ah]);
+    if constexpr (PROXY) Mh = fmaxf(Mh, s_pmax[ww][ah]);
   }
   if (Mh == kNegInf) Mh = 0.f;
   if (w == 0 && sub == 0 && r16 < G) s_M[r16] = Mh;
@@ -900,14 +908,14 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   // the proxies' share of the normaliser (lanes of head r16, clusters b0, b1)
   float lsum = 0.f;
   float cws[4] = {0.f, 0.f, 0.f, 0.f};  // cluster-tile weights of the rows below
-  const bool head_lane = r16 < G;
+  const bool head_lane = r16 < (HLR ? 2 * G : G);
   if constexpr (PROXY) {
     if (pi0 != kNegInf) lsum += fast_exp2(pi0 - Mh);
     if (pi1 != kNegInf) lsum += fast_exp2(pi1 - Mh);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int b = 4 * w + j + (sub >= 2 ? 4 * W : 0);
-      const float mu = s_mu[b][hr];
+      const float mu = s_mu[b][ah];
       cws[j] = (head_lane && b < p.C && mu != kNegInf) ? fast_exp2(mu - Mh) : 0.f;
     }
   }
@@ -917,14 +925,15 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   // lane n of group sub the tile rows 4*sub .. 4*sub+3 at column 16*nb + n
   // when lane s of the group points at row 4*sub + s/4, column
   // 16*nb + 4*(s%4). Two tiles share a product: B holds the four rows of
-  // tile a (elements 0-3) and of tile b (4-7), A (lane m = head, group sub)
-  // the matching weights, one product for the bf16 high parts and one for the
-  // remainders (about 16 significant bits of each weight, exact bf16 x bf16
-  // products, fp32 accumulation). A lone tile repeats its rows in both halves
-  // and takes the high parts and remainders in one product. The cluster-sum
-  // tile is the last tile: rows sub and 4 + sub hold the high part and
-  // remainder of cluster b0's value sum, rows 8 + sub and 12 + sub those of
-  // cluster b1 (zero when absent), weighted exp2(mu_b - M).
+  // tile a (elements 0-3) and of tile b (4-7), A (lane m = row, group sub)
+  // the matching weights of the row's head and part (about 16 significant
+  // bits of each weight, exact bf16 x bf16 products, fp32 accumulation). A
+  // lone tile repeats its rows in both halves, with zero weights in the
+  // second (with one row per head, its high parts and remainders go in the
+  // two halves instead). The cluster-sum tile is the last tile: rows sub and
+  // 4 + sub hold the high part and remainder of cluster b0's value sum, rows
+  // 8 + sub and 12 + sub those of cluster b1 (zero when absent), weighted
+  // exp2(mu_b - M).
   floatx4_t oacc[8];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) oacc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
@@ -943,11 +952,12 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   }
   wave_lds_sync();  // the weights, written by other lanes
   auto wt8 = [&](int hl, int t) {  // 4 keys of tile t (pair half t & 1)
-    return *reinterpret_cast<const bf16x4_t*>(&s_wt[w][hl][t >> 1][hr][sub][8 * (t & 1)]);
+    return *reinterpret_cast<const bf16x4_t*>(&s_wt[w][hl][t >> 1][ah][sub][8 * (t & 1)]);
   };
   auto wt16 = [&](int hl, int pr) {  // 4 keys of both tiles of pair pr
-    return *reinterpret_cast<const bf16x8_t*>(&s_wt[w][hl][pr][hr][sub][0]);
+    return *reinterpret_cast<const bf16x8_t*>(&s_wt[w][hl][pr][ah][sub][0]);
   };
+  const bf16x4_t zero4 = {};
   __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // the value tiles have landed
   bf16x4_t bv[NT][8];
 #pragma unroll
@@ -960,30 +970,47 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     wave_lds_sync();  // the tile's rows, written by other lanes
     tile_read(ct, bc);
   }
+  if constexpr (HLR) {
+    const bf16x4_t cw = al ? clo : chi;
 #pragma unroll
-  for (int pr = 0; pr < NT / 2; ++pr) {
-    product(wt16(0, pr), bv[2 * pr], bv[2 * pr + 1]);
-    product(wt16(1, pr), bv[2 * pr], bv[2 * pr + 1]);
-  }
-  if constexpr (NT % 2 == 1) {
-    constexpr int t = NT - 1;
-    if constexpr (PROXY) {
-      product(__builtin_shufflevector(wt8(0, t), chi, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bc);
-      product(__builtin_shufflevector(wt8(1, t), clo, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bc);
-    } else {
-      product(__builtin_shufflevector(wt8(0, t), wt8(1, t), 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bv[t]);
+    for (int pr = 0; pr < NT / 2; ++pr) product(wt16(al, pr), bv[2 * pr], bv[2 * pr + 1]);
+    if constexpr (NT % 2 == 1) {
+      constexpr int t = NT - 1;
+      if constexpr (PROXY)
+        product(__builtin_shufflevector(wt8(al, t), cw, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bc);
+      else
+        product(__builtin_shufflevector(wt8(al, t), zero4, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bv[t]);
+    } else if constexpr (PROXY) {
+      product(__builtin_shufflevector(cw, zero4, 0, 1, 2, 3, 4, 5, 6, 7), bc, bc);
     }
-  } else if constexpr (PROXY) {
-    product(__builtin_shufflevector(chi, clo, 0, 1, 2, 3, 4, 5, 6, 7), bc, bc);
+  } else {
+#pragma unroll
+    for (int pr = 0; pr < NT / 2; ++pr) {
+      product(wt16(0, pr), bv[2 * pr], bv[2 * pr + 1]);
+      product(wt16(1, pr), bv[2 * pr], bv[2 * pr + 1]);
+    }
+    if constexpr (NT % 2 == 1) {
+      constexpr int t = NT - 1;
+      if constexpr (PROXY) {
+        product(__builtin_shufflevector(wt8(0, t), chi, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bc);
+        product(__builtin_shufflevector(wt8(1, t), clo, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bc);
+      } else {
+        product(__builtin_shufflevector(wt8(0, t), wt8(1, t), 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bv[t]);
+      }
+    } else if constexpr (PROXY) {
+      product(__builtin_shufflevector(chi, clo, 0, 1, 2, 3, 4, 5, 6, 7), bc, bc);
+    }
   }
 
   // ---- per-wave partials, then the unit's combine ---------------------------
-  // accumulator element i of lane (n, group sub): head 4*sub + i, dim 16*nb + n
+  // accumulator element i of lane (n, group sub): row 4*sub + i, dim 16*nb + n
+  constexpr int NR = HLR ? 2 * G : G;  // rows kept
+  static_assert(NR * kD * 4 <= kVTile, "partials must fit a tile");
   float* red = reinterpret_cast<float*>(&s_vt[w][0][0]);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int h = 4 * sub + i;
-    if (h < G) {
+    if (h < NR) {
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) red[h * kD + 16 * nb + r16] = oacc[nb][i];
     }
@@ -1004,7 +1031,8 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     float a = 0.f, L = 0.f;
 #pragma unroll
     for (int ww = 0; ww < W; ++ww) {
-      a += reinterpret_cast<const float*>(&s_vt[ww][0][0])[ei];
+      const float* rw = reinterpret_cast<const float*>(&s_vt[ww][0][0]);
+      a += HLR ? rw[ei] + rw[G * kD + ei] : rw[ei];
       L += s_l[ww][h];
     }
     const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
