@@ -822,54 +822,68 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   }
   lds_barrier();
 
+  // ---- rows of the value products ------------------------------------------
+  // With at most four heads, rows 0 .. G-1 of the value products' A operand
+  // take the weights' bf16 high parts and rows G .. 2G-1 their remainders (one
+  // product covers both; the two row sets are added in the combine);
+  // otherwise row h takes head h and the two parts take one product each.
+  // This lane's row: head ah, part al (rows past those: any finite weights,
+  // their outputs are dropped).
+  constexpr bool HLR = G <= 4;
+  const int ah = HLR ? (r16 < G ? r16 : (r16 < 2 * G ? r16 - G : 0)) : hr;
+  const int al = HLR && r16 >= G && r16 < 2 * G ? 1 : 0;
+
   // ---- proxy logits of the clusters this wave owns ------------------------
   // Unread members of cluster b: n_b = count - (read members); their mean
   // logit mu_b = (q.sumK_b - sum of the read members' logits) / n_b; the
-  // proxy logit is mu_b + log2(n_b).
+  // proxy logit is mu_b + log2(n_b). Every read of this phase is issued at
+  // once (branch-free; both clusters' rows exist for every lane).
+  float Mk = kNegInf;  // maximum of the read logits, head ah
+#pragma unroll
+  for (int ww = 0; ww < W; ++ww) Mk = fmaxf(Mk, s_wmax[ww][ah]);
   float pi0 = kNegInf, pi1 = kNegInf;
   if constexpr (PROXY) {
-    auto mean_logit = [&](int b, float qk, int cntb, float& pi) {
-      float ssum = 0.f;
-      int rc = 0;
+    float cs0 = 0.f, cs1 = 0.f;
+    int rc0 = 0, rc1 = 0;
 #pragma unroll
-      for (int ww = 0; ww < W; ++ww) {
-        ssum += s_csum[ww][b][hr];
-        rc += s_ccnt[ww][b];
-      }
+    for (int ww = 0; ww < W; ++ww) {
+      cs0 += s_csum[ww][b0][hr];
+      rc0 += s_ccnt[ww][b0];
+      cs1 += s_csum[ww][b1][hr];
+      rc1 += s_ccnt[ww][b1];
+    }
+    auto mean_logit = [&](int b, bool has, float qk, int cntb, float cs, int rc, float& pi) {
       const int nb = cntb - rc;
-      if (nb < 0 && r16 == 0) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
-      float mu = kNegInf;
-      if (nb > 0) {
-        const float nbf = (float)nb;
-        mu = (qk - ssum) * __builtin_amdgcn_rcpf(nbf);  // (hardware reciprocal, ~1 ulp)
-        pi = mu + __builtin_amdgcn_logf(nbf);
-      }
+      if (has && nb < 0 && r16 == 0) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
+      const bool ok = has && nb > 0;
+      const float nbf = (float)(ok ? nb : 1);
+      const float mu = ok ? (qk - cs) * __builtin_amdgcn_rcpf(nbf) : kNegInf;  // (hardware reciprocal, ~1 ulp)
+      pi = (ok && r16 < G) ? mu + __builtin_amdgcn_logf(nbf) : kNegInf;
       if (r16 < G) s_mu[b][r16] = mu;
     };
-    if (has0) mean_logit(b0, qk0, cnt0, pi0);
-    if (has1) mean_logit(b1, qk1, cnt1, pi1);
+    mean_logit(b0, has0, qk0, cnt0, cs0, rc0, pi0);
+    mean_logit(b1, has1, qk1, cnt1, cs1, rc1, pi1);
     if (w == 0 && sub == 0 && r16 < G) s_mu[PC][r16] = kNegInf;
-    if (r16 >= G) pi0 = pi1 = kNegInf;
     const float pm = max_rowgroups(fmaxf(pi0, pi1));
     if (sub == 0 && r16 < G) s_pmax[w][r16] = pm;
     lds_barrier();
   }
 
   // ---- unit maximum (every wave, same value) --------------------------------
-  // Rows of the value products' A operand: with at most four heads, rows
-  // 0 .. G-1 take the weights' bf16 high parts and rows G .. 2G-1 their
-  // remainders (one product covers both; the two row sets are added in the
-  // combine), otherwise row h takes head h and the two parts take one product
-  // each. This lane's row: head ah, part al (rows past those: any finite
-  // weights, their outputs are dropped).
-  constexpr bool HLR = G <= 4;
-  const int ah = HLR ? (r16 < G ? r16 : (r16 < 2 * G ? r16 - G : 0)) : hr;
-  const int al = HLR && r16 >= G && r16 < 2 * G ? 1 : 0;
-  float Mh = kNegInf;  // head ah (= hr where r16 < G)
+  // and the cluster means the weights need, in the same LDS round trip
+  float mus[NT][NV], cmu[4];
+  if constexpr (PROXY) {
 #pragma unroll
-  for (int ww = 0; ww < W; ++ww) {
-    Mh = fmaxf(Mh, s_wmax[ww][ah]);
-    if constexpr (PROXY) Mh = fmaxf(Mh, s_pmax[ww][ah]);
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < NV; ++j) mus[t][j] = s_mu[cmr[t] >= 0 ? cmr[t] : PC][4 * j + sub < G ? 4 * j + sub : 0];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cmu[j] = s_mu[4 * w + j + (sub >= 2 ? 4 * W : 0)][ah];
+  }
+  float Mh = Mk;  // head ah (= hr where r16 < G)
+  if constexpr (PROXY) {
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww) Mh = fmaxf(Mh, s_pmax[ww][ah]);
   }
   if (Mh == kNegInf) Mh = 0.f;
   if (w == 0 && sub == 0 && r16 < G) s_M[r16] = Mh;
@@ -892,10 +906,7 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
       const float ev = fast_exp2(xr[t][j] - Mr[j]);
       lsr[j] += ev;
       float wv = ev;
-      if constexpr (PROXY) {
-        const float mu = s_mu[cmr[t] >= 0 ? cmr[t] : PC][h < G ? h : 0];
-        wv = ev - fast_exp2(mu - Mr[j]);
-      }
+      if constexpr (PROXY) wv = ev - fast_exp2(mus[t][j] - Mr[j]);
       const __bf16 hi = (__bf16)wv;
       const __bf16 lo = (__bf16)(wv - (float)hi);
       if (h < G) {
@@ -905,18 +916,17 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
       }
     }
   }
-  // the proxies' share of the normaliser (lanes of head r16, clusters b0, b1)
+  // the proxies' share of the normaliser (lanes of head r16, clusters b0, b1;
+  // exp2(-inf) = 0 for the absent ones)
   float lsum = 0.f;
   float cws[4] = {0.f, 0.f, 0.f, 0.f};  // cluster-tile weights of the rows below
   const bool head_lane = r16 < (HLR ? 2 * G : G);
   if constexpr (PROXY) {
-    if (pi0 != kNegInf) lsum += fast_exp2(pi0 - Mh);
-    if (pi1 != kNegInf) lsum += fast_exp2(pi1 - Mh);
+    lsum = fast_exp2(pi0 - Mh) + fast_exp2(pi1 - Mh);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int b = 4 * w + j + (sub >= 2 ? 4 * W : 0);
-      const float mu = s_mu[b][ah];
-      cws[j] = (head_lane && b < p.C && mu != kNegInf) ? fast_exp2(mu - Mh) : 0.f;
+      cws[j] = fast_exp2(((head_lane && b < p.C) ? cmu[j] : kNegInf) - Mh);
     }
   }
 
