@@ -503,15 +503,19 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
 
   constexpr int NV = G < 4 ? 1 : G / 4;  // heads per lane in the key layout
   constexpr int NP = (NT + 1) / 2;       // key tile pairs (the last may be single)
-  __shared__ float s_wmax[W][G];
-  __shared__ float s_pmax[PW][G];
+  // Per-wave results, the wave index last so that a lane reads all waves'
+  // values of one head or cluster with two 16-byte loads.
+  static_assert(W % 4 == 0, "per-wave results are read four at a time");
+  __shared__ __attribute__((aligned(16))) float s_wmax[G][W];
+  __shared__ __attribute__((aligned(16))) float s_pmax[G][PW];
   __shared__ float s_M[G];
-  __shared__ float s_l[W][G];
-  __shared__ float s_csum[PW][PC][G];
-  __shared__ int s_ccnt[PW][PC];
-  // mean logit of a cluster's unread members (-inf if none); row PC is a
-  // -inf sentinel for keys outside every cluster
-  __shared__ float s_mu[PC + 1][G];
+  __shared__ __attribute__((aligned(16))) float s_l[G][W];
+  __shared__ __attribute__((aligned(16))) float s_csum[PC][G][PW];
+  __shared__ __attribute__((aligned(16))) int s_ccnt[PC][PW];
+  // mean logit of a cluster's unread members (-inf if none), per head; entry
+  // PC is a -inf sentinel for keys outside every cluster (rows padded to 16
+  // bytes)
+  __shared__ __attribute__((aligned(16))) float s_mu[G][PC + 4];
   // Weights handed from the key layout to the matrix-core layout: per wave,
   // bf16 high part (0) and remainder (1), per pair of key tiles, head and
   // group of four keys, 16 bytes: four keys of the even tile, then four of
@@ -668,8 +672,8 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   float qk0 = 0.f, qk1 = 0.f;  // q . (sum of keys) of clusters b0, b1 for head r16
   if constexpr (PROXY) {
 #pragma unroll
-    for (int i = lane; i < PC * G; i += 64) (&s_csum[w][0][0])[i] = 0.f;
-    for (int i = lane; i < PC; i += 64) s_ccnt[w][i] = 0;
+    for (int i = lane; i < PC * G; i += 64) s_csum[i / G][i % G][w] = 0.f;
+    for (int i = lane; i < PC; i += 64) s_ccnt[i][w] = 0;
     float a[G];
     dot_heads<G>(qf, skf, a);
 #pragma unroll
@@ -755,7 +759,7 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
       sf[t][2] = r16 - 4 >= start ? 1.f : 0.f;
       sf[t][3] = r16 - 8 >= start ? 1.f : 0.f;
       run_end[t] = cm >= 0 && cnext != cm;  // last lane of a run
-      if (run_end[t] && sub == 0) lds_add(&s_ccnt[w][cm], r16 - start + 1);
+      if (run_end[t] && sub == 0) lds_add(&s_ccnt[cm][w], r16 - start + 1);
     }
   }
 
@@ -811,14 +815,14 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
       if (run_end[t]) {
 #pragma unroll
         for (int j = 0; j < NV; ++j)
-          if (4 * j + sub < G) lds_add(&s_csum[w][cmr[t]][4 * j + sub], hv[j]);
+          if (4 * j + sub < G) lds_add(&s_csum[cmr[t]][4 * j + sub][w], hv[j]);
       }
     }
   }
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const float v = max16(mxr[j]);
-    if (r16 == 0 && 4 * j + sub < G) s_wmax[w][4 * j + sub] = v;
+    if (r16 == 0 && 4 * j + sub < G) s_wmax[4 * j + sub][w] = v;
   }
   lds_barrier();
 
@@ -840,17 +844,24 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   // once (branch-free; both clusters' rows exist for every lane).
   float Mk = kNegInf;  // maximum of the read logits, head ah
 #pragma unroll
-  for (int ww = 0; ww < W; ++ww) Mk = fmaxf(Mk, s_wmax[ww][ah]);
+  for (int ww = 0; ww < W; ww += 4) {
+    const float4 m4 = *reinterpret_cast<const float4*>(&s_wmax[ah][ww]);
+    Mk = fmaxf(Mk, fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w)));
+  }
   float pi0 = kNegInf, pi1 = kNegInf;
   if constexpr (PROXY) {
     float cs0 = 0.f, cs1 = 0.f;
     int rc0 = 0, rc1 = 0;
 #pragma unroll
-    for (int ww = 0; ww < W; ++ww) {
-      cs0 += s_csum[ww][b0][hr];
-      rc0 += s_ccnt[ww][b0];
-      cs1 += s_csum[ww][b1][hr];
-      rc1 += s_ccnt[ww][b1];
+    for (int ww = 0; ww < W; ww += 4) {
+      const float4 a0 = *reinterpret_cast<const float4*>(&s_csum[b0][hr][ww]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&s_csum[b1][hr][ww]);
+      const int4 n0 = *reinterpret_cast<const int4*>(&s_ccnt[b0][ww]);
+      const int4 n1 = *reinterpret_cast<const int4*>(&s_ccnt[b1][ww]);
+      cs0 += (a0.x + a0.y) + (a0.z + a0.w);
+      cs1 += (a1.x + a1.y) + (a1.z + a1.w);
+      rc0 += n0.x + n0.y + n0.z + n0.w;
+      rc1 += n1.x + n1.y + n1.z + n1.w;
     }
     auto mean_logit = [&](int b, bool has, float qk, int cntb, float cs, int rc, float& pi) {
       const int nb = cntb - rc;
@@ -859,13 +870,13 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
       const float nbf = (float)(ok ? nb : 1);
       const float mu = ok ? (qk - cs) * __builtin_amdgcn_rcpf(nbf) : kNegInf;  // (hardware reciprocal, ~1 ulp)
       pi = (ok && r16 < G) ? mu + __builtin_amdgcn_logf(nbf) : kNegInf;
-      if (r16 < G) s_mu[b][r16] = mu;
+      if (r16 < G) s_mu[r16][b] = mu;
     };
     mean_logit(b0, has0, qk0, cnt0, cs0, rc0, pi0);
     mean_logit(b1, has1, qk1, cnt1, cs1, rc1, pi1);
-    if (w == 0 && sub == 0 && r16 < G) s_mu[PC][r16] = kNegInf;
+    if (w == 0 && sub == 0 && r16 < G) s_mu[r16][PC] = kNegInf;
     const float pm = max_rowgroups(fmaxf(pi0, pi1));
-    if (sub == 0 && r16 < G) s_pmax[w][r16] = pm;
+    if (sub == 0 && r16 < G) s_pmax[r16][w] = pm;
     lds_barrier();
   }
 
@@ -876,14 +887,20 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int j = 0; j < NV; ++j) mus[t][j] = s_mu[cmr[t] >= 0 ? cmr[t] : PC][4 * j + sub < G ? 4 * j + sub : 0];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) cmu[j] = s_mu[4 * w + j + (sub >= 2 ? 4 * W : 0)][ah];
+      for (int j = 0; j < NV; ++j) mus[t][j] = s_mu[4 * j + sub < G ? 4 * j + sub : 0][cmr[t] >= 0 ? cmr[t] : PC];
+    const float4 c4 = *reinterpret_cast<const float4*>(&s_mu[ah][4 * w + (sub >= 2 ? 4 * W : 0)]);
+    cmu[0] = c4.x;
+    cmu[1] = c4.y;
+    cmu[2] = c4.z;
+    cmu[3] = c4.w;
   }
   float Mh = Mk;  // head ah (= hr where r16 < G)
   if constexpr (PROXY) {
 #pragma unroll
-    for (int ww = 0; ww < W; ++ww) Mh = fmaxf(Mh, s_pmax[ww][ah]);
+    for (int ww = 0; ww < W; ww += 4) {
+      const float4 m4 = *reinterpret_cast<const float4*>(&s_pmax[ah][ww]);
+      Mh = fmaxf(Mh, fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w)));
+    }
   }
   if (Mh == kNegInf) Mh = 0.f;
   if (w == 0 && sub == 0 && r16 < G) s_M[r16] = Mh;
@@ -1032,7 +1049,7 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   for (int j = 0; j < NV; ++j) {
     const int h = 4 * j + sub;
     const float tot = sum16(lsr[j]) + shfl_f(lsum, h < G ? h : 0);
-    if (r16 == 0 && h < G) s_l[w][h] = tot;
+    if (r16 == 0 && h < G) s_l[h][w] = tot;
   }
   __syncthreads();
 
@@ -1043,7 +1060,11 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     for (int ww = 0; ww < W; ++ww) {
       const float* rw = reinterpret_cast<const float*>(&s_vt[ww][0][0]);
       a += HLR ? rw[ei] + rw[G * kD + ei] : rw[ei];
-      L += s_l[ww][h];
+    }
+#pragma unroll
+    for (int ww = 0; ww < W; ww += 4) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&s_l[h][ww]);
+      L += (l4.x + l4.y) + (l4.z + l4.w);
     }
     const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
     p.out[qh * kD + (ei - h * kD)] = (L > 0.f) ? a / L : 0.f;
