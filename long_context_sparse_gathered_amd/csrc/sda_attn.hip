@@ -509,7 +509,8 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   __shared__ __attribute__((aligned(16))) float s_wmax[G][W];
   __shared__ __attribute__((aligned(16))) float s_pmax[G][PW];
   __shared__ float s_M[G];
-  __shared__ __attribute__((aligned(16))) float s_l[G][W];
+  __shared__ __attribute__((aligned(16))) float s_l[G][W];   // normaliser: the wave's keys
+  __shared__ __attribute__((aligned(16))) float s_lp[G][PW]; // and its proxies
   __shared__ __attribute__((aligned(16))) float s_csum[PC][G][PW];
   __shared__ __attribute__((aligned(16))) int s_ccnt[PC][PW];
   // mean logit of a cluster's unread members (-inf if none), per head; entry
@@ -1030,45 +1031,53 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   }
 
   // ---- per-wave partials, then the unit's combine ---------------------------
-  // accumulator element i of lane (n, group sub): row 4*sub + i, dim 16*nb + n
+  // Accumulator element i of lane (n, group sub): row 4*sub + i, dim
+  // 16*nb + n. The partials are stored dim-major, [dim][row] with NR4 rows
+  // per dim, so that a lane writes each accumulator as one 16-byte store.
   constexpr int NR = HLR ? 2 * G : G;  // rows kept
-  static_assert(NR * kD * 4 <= kVTile, "partials must fit a tile");
+  constexpr int NR4 = NR < 4 ? 4 : NR;
+  static_assert(kD * NR4 * 4 <= kVTile, "partials must fit a tile");
   float* red = reinterpret_cast<float*>(&s_vt[w][0][0]);
+  if (4 * sub < NR) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int h = 4 * sub + i;
-    if (h < NR) {
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) red[h * kD + 16 * nb + r16] = oacc[nb][i];
-    }
+    for (int nb = 0; nb < 8; ++nb)
+      *reinterpret_cast<floatx4_t*>(red + (16 * nb + r16) * NR4 + 4 * sub) = oacc[nb];
   }
-  // normaliser of the wave: its keys (key layout) and owned proxies (head
-  // r16), gathered at the lanes of head 4j + sub
-  lsum = sum_rowgroups(lsum);
+  // normaliser of the wave: its keys (key layout, head 4j + sub) and its
+  // proxies (head r16)
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int h = 4 * j + sub;
-    const float tot = sum16(lsr[j]) + shfl_f(lsum, h < G ? h : 0);
+    const float tot = sum16(lsr[j]);
     if (r16 == 0 && h < G) s_l[h][w] = tot;
+  }
+  if constexpr (PROXY) {
+    lsum = sum_rowgroups(lsum);
+    if (sub == 0 && r16 < G) s_lp[r16][w] = lsum;
   }
   __syncthreads();
 
   for (int ei = tid; ei < G * kD; ei += 512) {
-    const int h = ei / kD;
+    const int dim = ei / G, h = ei - dim * G;
     float a = 0.f, L = 0.f;
 #pragma unroll
     for (int ww = 0; ww < W; ++ww) {
-      const float* rw = reinterpret_cast<const float*>(&s_vt[ww][0][0]);
-      a += HLR ? rw[ei] + rw[G * kD + ei] : rw[ei];
+      const float* rw = reinterpret_cast<const float*>(&s_vt[ww][0][0]) + dim * NR4 + h;
+      a += HLR ? rw[0] + rw[G] : rw[0];
     }
 #pragma unroll
     for (int ww = 0; ww < W; ww += 4) {
       const float4 l4 = *reinterpret_cast<const float4*>(&s_l[h][ww]);
       L += (l4.x + l4.y) + (l4.z + l4.w);
+      if constexpr (PROXY) {
+        const float4 p4 = *reinterpret_cast<const float4*>(&s_lp[h][ww]);
+        L += (p4.x + p4.y) + (p4.z + p4.w);
+      }
     }
     const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
-    p.out[qh * kD + (ei - h * kD)] = (L > 0.f) ? a / L : 0.f;
-    if (ei - h * kD == 0 && p.lse) p.lse[qh] = (L > 0.f) ? (s_M[h] + log2f(L)) * kLn2 : kNegInf;
+    // (hardware reciprocal and logarithm, ~1 ulp)
+    p.out[qh * kD + dim] = (L > 0.f) ? a * __builtin_amdgcn_rcpf(L) : 0.f;
+    if (dim == 0 && p.lse) p.lse[qh] = (L > 0.f) ? (s_M[h] + __builtin_amdgcn_logf(L)) * kLn2 : kNegInf;
   }
 }
 
