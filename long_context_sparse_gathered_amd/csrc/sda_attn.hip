@@ -522,6 +522,9 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   // group of four keys, 16 bytes: four keys of the even tile, then four of
   // the odd one.
   __shared__ __attribute__((aligned(16))) unsigned char s_wt[W][2][NP][G][4][16];
+  // The value loads' list entries, handed from the key loads' lanes: entry
+  // 16t + 4kq + sub at [w][t][sub][kq].
+  __shared__ __attribute__((aligned(16))) int s_jv[W][NT][4][4];
   // Value tiles, written by the row loads straight into LDS: per wave NT
   // tiles of 16 rows x 256 bytes, 16-byte chunks swizzled (vt_chunk) so that
   // the transposed reads are free of bank conflicts. After the products, tile
@@ -554,15 +557,13 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     lc = (p.idx_cluster ? p.idx_cluster : lst)[ea];
   }
   const float lwv = (p.logw ? p.logw : reinterpret_cast<const float*>(lst))[ea];
-  // the rows this lane fetches: key tile t takes entry 16t + r16, value slot
-  // k entry 4k + sub (read straight from the list: no shuffle round trips)
+  // the key rows this lane fetches: entry 16t + r16 of tile t, read straight
+  // from the list (no shuffle round trip)
   auto entry = [&](int pos) { return w * CH + pos; };
   auto listed = [&](int pos) { return pos < CH && entry(pos) < p.m; };
-  int jk[NT], jv[NS];
+  int jk[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) jk[t] = lst[lbase + (listed(16 * t + r16) ? entry(16 * t + r16) : 0)];
-#pragma unroll
-  for (int k = 0; k < NS; ++k) jv[k] = lst[lbase + (listed(4 * k + sub) ? entry(4 * k + sub) : 0)];
 
   const int64_t qrow0 = (int64_t)s * p.Hq + (int64_t)g * G;
   uint4 qa[4];  // MFMA A operand: head r16 (zero past G), dims 32*st + 8*sub
@@ -619,12 +620,27 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   int koff[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) koff[t] = row_byte(16 * t + r16, jk[t], 16 * sub);
-  // value slot k = 4t + kq (entries 16t + 4kq + sub) fills tile t, rows
+  // value slot k = 4t + kq (entry 16t + 4kq + sub) fills tile t, rows
   // 4kq .. 4kq+3: lane (sub, r16) lands at row 4kq + sub, chunk position r16,
-  // so it fetches the chunk that the swizzle puts there
+  // so it fetches the chunk that the swizzle puts there. The entries come
+  // from the key lanes through LDS (the value loads are issued late, so the
+  // round trip hides behind the key loads).
+  if (sub == 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) s_jv[w][t][r16 & 3][r16 >> 2] = jk[t];
+  }
+  wave_lds_sync();
   int voff[NS];
 #pragma unroll
-  for (int k = 0; k < NS; ++k) voff[k] = row_byte(4 * k + sub, jv[k], 16 * vt_chunk(4 * (k & 3) + sub, r16));
+  for (int t = 0; t < NT; ++t) {
+    const int4 j4 = *reinterpret_cast<const int4*>(&s_jv[w][t][sub][0]);
+    const int jv[4] = {j4.x, j4.y, j4.z, j4.w};
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      const int k = 4 * t + kq;
+      voff[k] = row_byte(4 * k + sub, jv[kq], 16 * vt_chunk(4 * kq + sub, r16));
+    }
+  }
 
   // cluster of this lane's entry from the per-row ids when the list carries
   // none: issued ahead of the row loads, so that its use does not wait for
