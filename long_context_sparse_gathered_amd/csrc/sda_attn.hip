@@ -503,6 +503,8 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
 
   constexpr int NV = G < 4 ? 1 : G / 4;  // heads per lane in the key layout
   constexpr int NP = (NT + 1) / 2;       // key tile pairs (the last may be single)
+  constexpr int NBT = NT + (PROXY ? 1 : 0);  // value tiles per wave, the cluster-sum tile last
+  constexpr int NPW = (NBT + 1) / 2;         // their pairs
   // Per-wave results, the wave index last so that a lane reads all waves'
   // values of one head or cluster with two 16-byte loads.
   static_assert(W % 4 == 0, "per-wave results are read four at a time");
@@ -521,7 +523,7 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   // bf16 high part (0) and remainder (1), per pair of key tiles, head and
   // group of four keys, 16 bytes: four keys of the even tile, then four of
   // the odd one.
-  __shared__ __attribute__((aligned(16))) unsigned char s_wt[W][2][NP][G][4][16];
+  __shared__ __attribute__((aligned(16))) unsigned char s_wt[W][2][NPW][G][4][16];
   // The value loads' list entries, handed from the key loads' lanes: entry
   // 16t + 4kq + sub at [w][t][sub][kq].
   __shared__ __attribute__((aligned(16))) int s_jv[W][NT][4][4];
@@ -535,7 +537,7 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   // fits next to the value tiles, so that it is written and read while the
   // rows are still in flight; otherwise it reuses tile 0 late.
   constexpr int kLdsOther =
-      (2 * W * G + PW * G + G + PW * PC * G + PW * PC + (PC + 1) * G) * 4 + W * 2 * NP * G * 64 + 256;
+      (2 * W * G + PW * G + G + PW * PC * G + PW * PC + (PC + 1) * G) * 4 + W * 2 * NPW * G * 64 + W * NT * 64 + 256;
   constexpr bool SEP = PROXY && (W * (NT + 1) * kVTile + kLdsOther <= 160 * 1024);
   __shared__ __attribute__((aligned(16))) unsigned char s_pt[SEP ? W : 1][SEP ? kVTile : 16];
 
@@ -859,30 +861,37 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   // logit mu_b = (q.sumK_b - sum of the read members' logits) / n_b; the
   // proxy logit is mu_b + log2(n_b). Every read of this phase is issued at
   // once (branch-free; both clusters' rows exist for every lane).
+  float4 wm4[W / 4], a04[W / 4], a14[W / 4];
+  int4 n04[W / 4], n14[W / 4];
+#pragma unroll
+  for (int q = 0; q < W / 4; ++q) {
+    wm4[q] = *reinterpret_cast<const float4*>(&s_wmax[ah][4 * q]);
+    if constexpr (PROXY) {
+      a04[q] = *reinterpret_cast<const float4*>(&s_csum[b0][hr][4 * q]);
+      a14[q] = *reinterpret_cast<const float4*>(&s_csum[b1][hr][4 * q]);
+      n04[q] = *reinterpret_cast<const int4*>(&s_ccnt[b0][4 * q]);
+      n14[q] = *reinterpret_cast<const int4*>(&s_ccnt[b1][4 * q]);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);  // (every read above in flight before the first use)
   float Mk = kNegInf;  // maximum of the read logits, head ah
 #pragma unroll
-  for (int ww = 0; ww < W; ww += 4) {
-    const float4 m4 = *reinterpret_cast<const float4*>(&s_wmax[ah][ww]);
-    Mk = fmaxf(Mk, fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w)));
-  }
+  for (int q = 0; q < W / 4; ++q) Mk = fmaxf(Mk, fmaxf(fmaxf(wm4[q].x, wm4[q].y), fmaxf(wm4[q].z, wm4[q].w)));
   float pi0 = kNegInf, pi1 = kNegInf;
+  bool neg_count = false;  // more read members than the cluster holds
   if constexpr (PROXY) {
     float cs0 = 0.f, cs1 = 0.f;
     int rc0 = 0, rc1 = 0;
 #pragma unroll
-    for (int ww = 0; ww < W; ww += 4) {
-      const float4 a0 = *reinterpret_cast<const float4*>(&s_csum[b0][hr][ww]);
-      const float4 a1 = *reinterpret_cast<const float4*>(&s_csum[b1][hr][ww]);
-      const int4 n0 = *reinterpret_cast<const int4*>(&s_ccnt[b0][ww]);
-      const int4 n1 = *reinterpret_cast<const int4*>(&s_ccnt[b1][ww]);
-      cs0 += (a0.x + a0.y) + (a0.z + a0.w);
-      cs1 += (a1.x + a1.y) + (a1.z + a1.w);
-      rc0 += n0.x + n0.y + n0.z + n0.w;
-      rc1 += n1.x + n1.y + n1.z + n1.w;
+    for (int q = 0; q < W / 4; ++q) {
+      cs0 += (a04[q].x + a04[q].y) + (a04[q].z + a04[q].w);
+      cs1 += (a14[q].x + a14[q].y) + (a14[q].z + a14[q].w);
+      rc0 += n04[q].x + n04[q].y + n04[q].z + n04[q].w;
+      rc1 += n14[q].x + n14[q].y + n14[q].z + n14[q].w;
     }
     auto mean_logit = [&](int b, bool has, float qk, int cntb, float cs, int rc, float& pi) {
       const int nb = cntb - rc;
-      if (has && nb < 0 && r16 == 0) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
+      neg_count |= has && nb < 0 && r16 == 0;
       const bool ok = has && nb > 0;
       const float nbf = (float)(ok ? nb : 1);
       const float mu = ok ? (qk - cs) * __builtin_amdgcn_rcpf(nbf) : kNegInf;  // (hardware reciprocal, ~1 ulp)
@@ -895,6 +904,7 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
     const float pm = max_rowgroups(fmaxf(pi0, pi1));
     if (sub == 0 && r16 < G) s_pmax[r16][w] = pm;
     lds_barrier();
+    if (neg_count) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
   }
 
   // ---- unit maximum (every wave, same value) --------------------------------
@@ -978,122 +988,241 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
   // 4 + sub hold the high part and remainder of cluster b0's value sum, rows
   // 8 + sub and 12 + sub those of cluster b1 (zero when absent), weighted
   // exp2(mu_b - M).
-  floatx4_t oacc[8];
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) oacc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-  auto product = [&](const bf16x8_t a, const bf16x4_t (&ba)[8], const bf16x4_t (&bb)[8]) {
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const bf16x8_t b = __builtin_shufflevector(ba[nb], bb[nb], 0, 1, 2, 3, 4, 5, 6, 7);
-      oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, oacc[nb], 0, 0, 0);
-    }
-  };
   bf16x4_t chi, clo;  // cluster-tile weights, high parts and remainders
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     chi[j] = (__bf16)cws[j];
     clo[j] = (__bf16)(cws[j] - (float)chi[j]);
   }
-  wave_lds_sync();  // the weights, written by other lanes
-  auto wt8 = [&](int hl, int t) {  // 4 keys of tile t (pair half t & 1)
-    return *reinterpret_cast<const bf16x4_t*>(&s_wt[w][hl][t >> 1][ah][sub][8 * (t & 1)]);
-  };
-  auto wt16 = [&](int hl, int pr) {  // 4 keys of both tiles of pair pr
-    return *reinterpret_cast<const bf16x8_t*>(&s_wt[w][hl][pr][ah][sub][0]);
-  };
-  const bf16x4_t zero4 = {};
-  __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // the value tiles have landed
-  bf16x4_t bv[NT][8];
+  // With the cluster-sum tile in a buffer of its own (or none), each wave
+  // computes 16 of the 128 output dims over the keys of every wave: the
+  // products then sum across waves in the matrix cores, and no partials
+  // pass through LDS. Otherwise each wave takes all dims of its own keys and
+  // the waves' partials are added in a combine.
+  constexpr bool DIMS = !PROXY || SEP;
+  if constexpr (DIMS) {
+    static_assert(W * 16 == kD, "one 16-dim block per wave");
+    // ---- everything the other waves read: normalisers, cluster weights ----
 #pragma unroll
-  for (int t = 0; t < NT; ++t) tile_read(&s_vt[w][t][0], bv[t]);
-  if constexpr (PROXY && !SEP) {
-    // no buffer of its own: the tile goes into the consumed tile 0 (the
-    // writes follow this wave's reads of tile 0)
-    unsigned char* ct = &s_vt[w][0][0];
-    put_cluster_tile(ct);
-    wave_lds_sync();  // the tile's rows, written by other lanes
-    tile_read(ct, bc);
-  }
-  if constexpr (HLR) {
-    const bf16x4_t cw = al ? clo : chi;
-#pragma unroll
-    for (int pr = 0; pr < NT / 2; ++pr) product(wt16(al, pr), bv[2 * pr], bv[2 * pr + 1]);
-    if constexpr (NT % 2 == 1) {
-      constexpr int t = NT - 1;
-      if constexpr (PROXY)
-        product(__builtin_shufflevector(wt8(al, t), cw, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bc);
-      else
-        product(__builtin_shufflevector(wt8(al, t), zero4, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bv[t]);
-    } else if constexpr (PROXY) {
-      product(__builtin_shufflevector(cw, zero4, 0, 1, 2, 3, 4, 5, 6, 7), bc, bc);
+    for (int j = 0; j < NV; ++j) {
+      const int h = 4 * j + sub;
+      const float tot = sum16(lsr[j]);
+      if (r16 == 0 && h < G) s_l[h][w] = tot;
     }
-  } else {
-#pragma unroll
-    for (int pr = 0; pr < NT / 2; ++pr) {
-      product(wt16(0, pr), bv[2 * pr], bv[2 * pr + 1]);
-      product(wt16(1, pr), bv[2 * pr], bv[2 * pr + 1]);
-    }
-    if constexpr (NT % 2 == 1) {
-      constexpr int t = NT - 1;
-      if constexpr (PROXY) {
-        product(__builtin_shufflevector(wt8(0, t), chi, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bc);
-        product(__builtin_shufflevector(wt8(1, t), clo, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bc);
-      } else {
-        product(__builtin_shufflevector(wt8(0, t), wt8(1, t), 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bv[t]);
+    if constexpr (PROXY) {
+      lsum = sum_rowgroups(lsum);
+      if (sub == 0 && r16 < G) s_lp[r16][w] = lsum;
+      // the cluster-sum tile's weights go in the weight slots as tile NT
+      unsigned char* cs = &s_wt[w][0][NT >> 1][0][sub][8 * (NT & 1)];
+      constexpr int hstep = sizeof(s_wt[0][0][0][0]);
+      constexpr int pstep = sizeof(s_wt[0][0]);
+      if constexpr (HLR) {
+        if (head_lane) *reinterpret_cast<bf16x4_t*>(cs + al * pstep + ah * hstep) = al ? clo : chi;
+      } else if (r16 < G) {
+        *reinterpret_cast<bf16x4_t*>(cs + r16 * hstep) = chi;
+        *reinterpret_cast<bf16x4_t*>(cs + pstep + r16 * hstep) = clo;
       }
-    } else if constexpr (PROXY) {
-      product(__builtin_shufflevector(chi, clo, 0, 1, 2, 3, 4, 5, 6, 7), bc, bc);
     }
-  }
-
-  // ---- per-wave partials, then the unit's combine ---------------------------
-  // Accumulator element i of lane (n, group sub): row 4*sub + i, dim
-  // 16*nb + n. The partials are stored dim-major, [dim][row] with NR4 rows
-  // per dim, so that a lane writes each accumulator as one 16-byte store.
-  constexpr int NR = HLR ? 2 * G : G;  // rows kept
-  constexpr int NR4 = NR < 4 ? 4 : NR;
-  static_assert(kD * NR4 * 4 <= kVTile, "partials must fit a tile");
-  float* red = reinterpret_cast<float*>(&s_vt[w][0][0]);
-  if (4 * sub < NR) {
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-      *reinterpret_cast<floatx4_t*>(red + (16 * nb + r16) * NR4 + 4 * sub) = oacc[nb];
-  }
-  // normaliser of the wave: its keys (key layout, head 4j + sub) and its
-  // proxies (head r16)
-#pragma unroll
-  for (int j = 0; j < NV; ++j) {
-    const int h = 4 * j + sub;
-    const float tot = sum16(lsr[j]);
-    if (r16 == 0 && h < G) s_l[h][w] = tot;
-  }
-  if constexpr (PROXY) {
-    lsum = sum_rowgroups(lsum);
-    if (sub == 0 && r16 < G) s_lp[r16][w] = lsum;
-  }
-  __syncthreads();
-
-  for (int ei = tid; ei < G * kD; ei += 512) {
-    const int dim = ei / G, h = ei - dim * G;
-    float a = 0.f, L = 0.f;
-#pragma unroll
-    for (int ww = 0; ww < W; ++ww) {
-      const float* rw = reinterpret_cast<const float*>(&s_vt[ww][0][0]) + dim * NR4 + h;
-      a += HLR ? rw[0] + rw[G] : rw[0];
+    if constexpr (NBT % 2 == 1) {
+      // a lone last tile: zero weights in the second half of its pair
+      if (r16 < G) {
+        const bf16x4_t z = {};
+        *reinterpret_cast<bf16x4_t*>(&s_wt[w][0][NPW - 1][r16][sub][8]) = z;
+        *reinterpret_cast<bf16x4_t*>(&s_wt[w][1][NPW - 1][r16][sub][8]) = z;
+      }
     }
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this wave's value tiles have landed
+    lds_barrier();                           // and every wave's, with the weights
+
+    // ---- products: dims 16w .. 16w+15, every wave's tiles --------------------
+    auto read1 = [&](const unsigned char* tile) {
+      auto src = (__attribute__((address_space(3))) bf16x4_t*)(tile + tr_row * 256 +
+                                                               16 * vt_chunk(tr_row, 2 * w + ((r16 & 3) >> 1)) +
+                                                               8 * (r16 & 1));
+      return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(src);
+    };
+    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sw = 0; sw < W; ++sw) {
+#pragma unroll
+      for (int pp = 0; pp < NPW; ++pp) {
+        const int ta = 2 * pp, tb = 2 * pp + 1 < NBT ? 2 * pp + 1 : 2 * pp;
+        const unsigned char* pa = ta < NT ? &s_vt[sw][ta < NT ? ta : 0][0] : &s_pt[SEP ? sw : 0][0];
+        const unsigned char* pb = tb < NT ? &s_vt[sw][tb < NT ? tb : 0][0] : &s_pt[SEP ? sw : 0][0];
+        const bf16x8_t b = __builtin_shufflevector(read1(pa), read1(pb), 0, 1, 2, 3, 4, 5, 6, 7);
+        if constexpr (HLR) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              *reinterpret_cast<const bf16x8_t*>(&s_wt[sw][al][pp][ah][sub][0]), b, acc, 0, 0, 0);
+        } else {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              *reinterpret_cast<const bf16x8_t*>(&s_wt[sw][0][pp][ah][sub][0]), b, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              *reinterpret_cast<const bf16x8_t*>(&s_wt[sw][1][pp][ah][sub][0]), b, acc, 0, 0, 0);
+        }
+      }
+    }
+
+    // ---- outputs ----------------------------------------------------------
+    // normaliser of head hr (all waves' keys and proxies), then per head in
+    // scalar registers
+    float LA = 0.f;
 #pragma unroll
     for (int ww = 0; ww < W; ww += 4) {
-      const float4 l4 = *reinterpret_cast<const float4*>(&s_l[h][ww]);
-      L += (l4.x + l4.y) + (l4.z + l4.w);
+      const float4 l4 = *reinterpret_cast<const float4*>(&s_l[hr][ww]);
+      LA += (l4.x + l4.y) + (l4.z + l4.w);
       if constexpr (PROXY) {
-        const float4 p4 = *reinterpret_cast<const float4*>(&s_lp[h][ww]);
-        L += (p4.x + p4.y) + (p4.z + p4.w);
+        const float4 p4 = *reinterpret_cast<const float4*>(&s_lp[hr][ww]);
+        LA += (p4.x + p4.y) + (p4.z + p4.w);
       }
     }
-    const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
-    // (hardware reciprocal and logarithm, ~1 ulp)
-    p.out[qh * kD + dim] = (L > 0.f) ? a * __builtin_amdgcn_rcpf(L) : 0.f;
-    if (dim == 0 && p.lse) p.lse[qh] = (L > 0.f) ? (s_M[h] + __builtin_amdgcn_logf(L)) * kLn2 : kNegInf;
+    // accumulator element i of lane (n, group sub): row 4*sub + i, dim
+    // 16w + n; rows G .. 2G-1 hold the remainders' share when HLR
+    float tot[4];
+    int hb = 0;          // first head of this lane's totals
+    bool store = false;  // lanes whose totals are complete
+    if constexpr (HLR && G == 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const RowPair r = swap16(acc[i]);
+        tot[i] = r.even + r.odd;
+      }
+      store = sub == 0;
+    } else if constexpr (HLR && G == 2) {
+      tot[0] = acc[0] + acc[2];
+      tot[1] = acc[1] + acc[3];
+      store = sub == 0;
+    } else if constexpr (HLR) {
+      tot[0] = acc[0] + acc[1];
+      store = sub == 0;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tot[i] = acc[i];
+      hb = 4 * sub;
+      store = 4 * sub < G;
+    }
+    constexpr int NH = G < 4 ? G : 4;  // heads per storing lane
+#pragma unroll
+    for (int i = 0; i < NH; ++i) {
+      const int h = hb + i;
+      // (a uniform lane index when G <= 4; per row group otherwise)
+      const float L = (G <= 4) ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(LA), i))
+                               : shfl_f(LA, h < G ? h : 0);
+      if (store) p.out[(qrow0 + h) * kD + 16 * w + r16] = (L > 0.f) ? tot[i] * __builtin_amdgcn_rcpf(L) : 0.f;
+    }
+    if (w == 0 && sub == 0 && r16 < G && p.lse)
+      p.lse[qrow0 + r16] = (LA > 0.f) ? (Mh + __builtin_amdgcn_logf(LA)) * kLn2 : kNegInf;
+  } else {
+    floatx4_t oacc[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) oacc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    auto product = [&](const bf16x8_t a, const bf16x4_t (&ba)[8], const bf16x4_t (&bb)[8]) {
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const bf16x8_t b = __builtin_shufflevector(ba[nb], bb[nb], 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, oacc[nb], 0, 0, 0);
+      }
+    };
+    wave_lds_sync();  // the weights, written by other lanes
+    auto wt8 = [&](int hl, int t) {  // 4 keys of tile t (pair half t & 1)
+      return *reinterpret_cast<const bf16x4_t*>(&s_wt[w][hl][t >> 1][ah][sub][8 * (t & 1)]);
+    };
+    auto wt16 = [&](int hl, int pr) {  // 4 keys of both tiles of pair pr
+      return *reinterpret_cast<const bf16x8_t*>(&s_wt[w][hl][pr][ah][sub][0]);
+    };
+    const bf16x4_t zero4 = {};
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // the value tiles have landed
+    bf16x4_t bv[NT][8];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) tile_read(&s_vt[w][t][0], bv[t]);
+    if constexpr (PROXY && !SEP) {
+      // no buffer of its own: the tile goes into the consumed tile 0 (the
+      // writes follow this wave's reads of tile 0)
+      unsigned char* ct = &s_vt[w][0][0];
+      put_cluster_tile(ct);
+      wave_lds_sync();  // the tile's rows, written by other lanes
+      tile_read(ct, bc);
+    }
+    if constexpr (HLR) {
+      const bf16x4_t cw = al ? clo : chi;
+#pragma unroll
+      for (int pr = 0; pr < NT / 2; ++pr) product(wt16(al, pr), bv[2 * pr], bv[2 * pr + 1]);
+      if constexpr (NT % 2 == 1) {
+        constexpr int t = NT - 1;
+        if constexpr (PROXY)
+          product(__builtin_shufflevector(wt8(al, t), cw, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bc);
+        else
+          product(__builtin_shufflevector(wt8(al, t), zero4, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bv[t]);
+      } else if constexpr (PROXY) {
+        product(__builtin_shufflevector(cw, zero4, 0, 1, 2, 3, 4, 5, 6, 7), bc, bc);
+      }
+    } else {
+#pragma unroll
+      for (int pr = 0; pr < NT / 2; ++pr) {
+        product(wt16(0, pr), bv[2 * pr], bv[2 * pr + 1]);
+        product(wt16(1, pr), bv[2 * pr], bv[2 * pr + 1]);
+      }
+      if constexpr (NT % 2 == 1) {
+        constexpr int t = NT - 1;
+        if constexpr (PROXY) {
+          product(__builtin_shufflevector(wt8(0, t), chi, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bc);
+          product(__builtin_shufflevector(wt8(1, t), clo, 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bc);
+        } else {
+          product(__builtin_shufflevector(wt8(0, t), wt8(1, t), 0, 1, 2, 3, 4, 5, 6, 7), bv[t], bv[t]);
+        }
+      } else if constexpr (PROXY) {
+        product(__builtin_shufflevector(chi, clo, 0, 1, 2, 3, 4, 5, 6, 7), bc, bc);
+      }
+    }
+
+    // ---- per-wave partials, then the unit's combine ---------------------------
+    // Accumulator element i of lane (n, group sub): row 4*sub + i, dim
+    // 16*nb + n. The partials are stored dim-major, [dim][row] with NR4 rows
+    // per dim, so that a lane writes each accumulator as one 16-byte store.
+    constexpr int NR = HLR ? 2 * G : G;  // rows kept
+    constexpr int NR4 = NR < 4 ? 4 : NR;
+    static_assert(kD * NR4 * 4 <= kVTile, "partials must fit a tile");
+    float* red = reinterpret_cast<float*>(&s_vt[w][0][0]);
+    if (4 * sub < NR) {
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+        *reinterpret_cast<floatx4_t*>(red + (16 * nb + r16) * NR4 + 4 * sub) = oacc[nb];
+    }
+    // normaliser of the wave: its keys (key layout, head 4j + sub) and its
+    // proxies (head r16)
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int h = 4 * j + sub;
+      const float tot = sum16(lsr[j]);
+      if (r16 == 0 && h < G) s_l[h][w] = tot;
+    }
+    if constexpr (PROXY) {
+      lsum = sum_rowgroups(lsum);
+      if (sub == 0 && r16 < G) s_lp[r16][w] = lsum;
+    }
+    __syncthreads();
+
+    for (int ei = tid; ei < G * kD; ei += 512) {
+      const int dim = ei / G, h = ei - dim * G;
+      float a = 0.f, L = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < W; ++ww) {
+        const float* rw = reinterpret_cast<const float*>(&s_vt[ww][0][0]) + dim * NR4 + h;
+        a += HLR ? rw[0] + rw[G] : rw[0];
+      }
+#pragma unroll
+      for (int ww = 0; ww < W; ww += 4) {
+        const float4 l4 = *reinterpret_cast<const float4*>(&s_l[h][ww]);
+        L += (l4.x + l4.y) + (l4.z + l4.w);
+        if constexpr (PROXY) {
+          const float4 p4 = *reinterpret_cast<const float4*>(&s_lp[h][ww]);
+          L += (p4.x + p4.y) + (p4.z + p4.w);
+        }
+      }
+      const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
+      // (hardware reciprocal and logarithm, ~1 ulp)
+      p.out[qh * kD + dim] = (L > 0.f) ? a * __builtin_amdgcn_rcpf(L) : 0.f;
+      if (dim == 0 && p.lse) p.lse[qh] = (L > 0.f) ? (s_M[h] + __builtin_amdgcn_logf(L)) * kLn2 : kNegInf;
+    }
   }
 }
 
