@@ -28,10 +28,11 @@ def _grouped(w, G, Hkv):
 
 
 # list length -> tiles of 16 entries per wave in the unit kernel (8 waves)
-@pytest.mark.parametrize("G,n_top", [(1, 40), (2, 200), (4, 430), (8, 100), (8, 310)])
+@pytest.mark.parametrize("G,n_top", [(1, 40), (2, 40), (2, 200), (4, 140), (4, 430), (8, 100), (8, 310)])
 def test_proxy_unit_kernel_group_sizes(orc, G, n_top):
     """Proxy decode through the one-workgroup-per-unit kernel: G = 1..8 and
-    1..4 tiles per wave (m = 108 .. 498; at most 3 tiles for G = 8)."""
+    1..4 tiles per wave (m = 108 .. 498; at most 3 tiles for G = 8), so the
+    cluster-sum tile both shares a pair with a key tile and stands alone."""
     w = _grouped(synth.WORKLOADS["proxy_bf16_b1_n32k"], G, 2).replace(B=2, n=4096, n_top=n_top, C=37)
     c = synth.make_case(w)
     d = case_to_dev(c)
@@ -43,14 +44,15 @@ def test_proxy_unit_kernel_group_sizes(orc, G, n_top):
     assert lse_err(lse, ref_lse) <= LSE_TOL
 
 
-@pytest.mark.parametrize("G", [1, 2, 8])
-def test_none_unit_kernel_group_sizes(orc, G):
+# list length -> tiles per wave: 200 -> 2, 328 -> 3 (a lone last tile), 100 -> 1
+@pytest.mark.parametrize("G,m", [(1, 200), (2, 200), (8, 200), (4, 328), (1, 328), (8, 100), (2, 100)])
+def test_none_unit_kernel_group_sizes(orc, G, m):
     """No tail with 128 units (one workgroup per unit): random lists with
-    duplicates and log-weights."""
+    duplicates and log-weights, 1..3 tiles of 16 keys per wave."""
     w = _grouped(synth.WORKLOADS["proxy_bf16_b1_n32k"], G, 2).replace(B=64, n=1024, n_top=40, C=0)
     c = synth.make_case(w)
-    rng = np.random.default_rng(G)
-    idx = rng.integers(0, w.n, size=(w.B, w.Hkv, 200)).astype(np.int32)
+    rng = np.random.default_rng(G * 1000 + m)
+    idx = rng.integers(0, w.n, size=(w.B, w.Hkv, m)).astype(np.int32)
     logw = rng.normal(0, 1, size=idx.shape).astype(np.float32)
     d = case_to_dev(c)
     out, lse = sda.sparse_decode_attn(d["q"], d["K"], d["V"], to_dev(idx), logw=to_dev(logw))
