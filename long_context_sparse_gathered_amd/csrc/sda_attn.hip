@@ -450,8 +450,9 @@ __global__ __launch_bounds__(512) void sparse_unit_kernel(const AttnParams p) {
 // 4w + qg + 32 and computes their mean logits; the unit maximum comes from the
 // per-wave maxima of the read logits and of the proxy logits.
 //
-// Weighted values: one v_mfma_f32_16x16x32_bf16 per 16 keys and 16 dims (see
-// the value phase below).
+// From the logits to the weights each (head, key) pair sits in one lane (the
+// key layout); the weighted values take one v_mfma_f32_16x16x32_bf16 per two
+// tiles of 16 keys and 16 dims (see the value phase below).
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
