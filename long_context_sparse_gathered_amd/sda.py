@@ -157,20 +157,66 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]):
     return torch.empty(nbytes, dtype=torch.uint8, device=device), nbytes
 
 
-def _i32(t: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
-    if t is None:
-        return None
-    if t.dtype != torch.int32 or not t.is_contiguous():
-        raise TypeError("index-like tensors must be contiguous int32")
+# ---------------------------------------------------------------------------
+# argument checks: everything the kernels assume about a tensor (element type,
+# shape, strides, device) is checked here, before the library is called, so a
+# mismatch raises instead of reading or writing past a caller's buffer
+
+def _need(t, name: str, dtype=None, shape=None, contiguous: bool = True, device=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     return t
 
 
-def _f32c(t: Optional[torch.Tensor], name: str) -> Optional[torch.Tensor]:
-    if t is None:
-        return None
-    if t.dtype != torch.float32 or not t.is_contiguous():
-        raise TypeError(f"{name} must be a contiguous float32 tensor")
-    return t
+def _opt(t, name: str, **kw):
+    return None if t is None else _need(t, name, **kw)
+
+
+def _check_kv(K: torch.Tensor, V: torch.Tensor):
+    """K and V: [B, Hkv, n, d] views with the same shape, strides, element
+    type and device; unit stride along d."""
+    _need(K, "K", contiguous=False)
+    _need(V, "V", contiguous=False)
+    if K.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError(f"K must be bfloat16 or float32, got {K.dtype}")
+    if K.dim() != 4 or K.stride(-1) != 1:
+        raise ValueError("K must be a [B, Hkv, n, d] view with unit stride along d")
+    if V.dtype != K.dtype:
+        raise TypeError(f"V must have K's element type {K.dtype}, got {V.dtype}")
+    if tuple(V.shape) != tuple(K.shape):
+        raise ValueError(f"V must have K's shape {tuple(K.shape)}, got {tuple(V.shape)}")
+    if tuple(V.stride()) != tuple(K.stride()):
+        raise ValueError(f"V must have K's strides {tuple(K.stride())}, got {tuple(V.stride())}")
+    if V.device != K.device:
+        raise ValueError(f"V is on {V.device}, K on {K.device}")
+
+
+def _check_q(q: torch.Tensor, K: torch.Tensor, dtype=None) -> int:
+    """q: contiguous [B, Hq, d] in K's element type (or `dtype`), Hq a
+    multiple of Hkv; returns Hq."""
+    B, Hkv, _, d = K.shape
+    _need(q, "q", dtype=K.dtype if dtype is None else dtype, device=K.device)
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != d or q.shape[1] % Hkv != 0:
+        raise ValueError(f"q must be [B={B}, Hq (a multiple of {Hkv}), d={d}], got {tuple(q.shape)}")
+    return q.shape[1]
+
+
+def _on_gpu(t: torch.Tensor, name: str):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU, got {t.device}")
+
+
+def _check_ws(ws, device):
+    if ws is not None:
+        _need(ws, "ws", dtype=torch.uint8, device=device)
 
 
 # ---------------------------------------------------------------------------
@@ -216,26 +262,35 @@ class SampledTail:
         return NormalDist().inv_cdf(1.0 - self.delta / 2.0)
 
 
-def _tail_struct(tail, idx_cluster, cluster_id, lam, keep) -> Tail:
+def _tail_struct(tail, idx_cluster, cluster_id, lam, keep, B, Hq, Hkv, n, d, m, device) -> Tail:
+    """The tail block, after checking every tensor it points at against the
+    step's shapes."""
     t = Tail()
     if tail is None:
         t.kind = TAIL_NONE
     elif isinstance(tail, ProxyState):
+        C = int(tail.C)
         t.kind = TAIL_PROXY
-        t.C = tail.C
-        t.idx_cluster = _ptr(_i32(idx_cluster))
-        t.cluster_id = _ptr(_i32(cluster_id))
-        t.count = _ptr(_i32(tail.count))
-        t.sumK = _ptr(_f32c(tail.sumK, "sumK"))
-        t.sumV = _ptr(_f32c(tail.sumV, "sumV"))
+        t.C = C
+        t.idx_cluster = _ptr(_opt(idx_cluster, "idx_cluster", dtype=torch.int32, shape=(B, Hkv, m), device=device))
+        t.cluster_id = _ptr(_opt(cluster_id, "cluster_id", dtype=torch.int32, shape=(B, Hkv, n), device=device))
+        t.count = _ptr(_need(tail.count, "count", dtype=torch.int32, shape=(B, Hkv, C), device=device))
+        t.sumK = _ptr(_need(tail.sumK, "sumK", dtype=torch.float32, shape=(B, Hkv, C, d), device=device))
+        t.sumV = _ptr(_need(tail.sumV, "sumV", dtype=torch.float32, shape=(B, Hkv, C, d), device=device))
     elif isinstance(tail, PriorState):
         t.kind = TAIL_PRIOR
-        for name in ("mu_Q", "mu_K", "O_est", "maxP", "sumP"):
-            setattr(t, name, _ptr(_f32c(getattr(tail, name), name)))
+        shapes = {"mu_Q": (B, Hq, d), "mu_K": (B, Hkv, d), "O_est": (B, Hq, d), "maxP": (B, Hq), "sumP": (B, Hq)}
+        for name, shp in shapes.items():
+            setattr(t, name, _ptr(_need(getattr(tail, name), name, dtype=torch.float32, shape=shp, device=device)))
         t.lam = float(lam)
         t.prior_n = int(tail.n_covered)
     elif isinstance(tail, SampledTail):
         t.kind = TAIL_SAMPLED
+        _need(tail.b, "b", dtype=torch.int32, shape=(B, Hkv), device=device)
+        _need(tail.bstar, "bstar", dtype=torch.float64, shape=(B, Hkv), device=device)
+        if tail.b_cap < 0:
+            raise ValueError("b_cap must be >= 0")
+        _opt(tail.samples, "samples", dtype=torch.int32, shape=(B, Hkv, tail.b_cap), device=device)
         t.eps, t.z, t.b0, t.seed, t.b_cap = tail.eps, tail.z, tail.b0, tail.seed & (2**64 - 1), tail.b_cap
         t.b_out, t.bstar_out, t.samples_out = _ptr(tail.b), _ptr(tail.bstar), _ptr(tail.samples)
     else:
@@ -244,22 +299,35 @@ def _tail_struct(tail, idx_cluster, cluster_id, lam, keep) -> Tail:
     return t
 
 
+def _outputs(out, lse, B, Hq, d, device):
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=device) if out is None else \
+        _need(out, "out", dtype=torch.float32, shape=(B, Hq, d), device=device)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=device) if lse is None else \
+        _need(lse, "lse", dtype=torch.float32, shape=(B, Hq), device=device)
+    return out, lse
+
+
 # ---------------------------------------------------------------------------
 # entry points
 
 def build_tail_proxies(K: torch.Tensor, V: torch.Tensor, cluster_id: torch.Tensor, C: int,
                        flags: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
                        stream=None, with_sumK2: bool = False) -> ProxyState:
-    dims = make_dims(K, 1)
-    dims.Hq = dims.Hkv
+    _check_kv(K, V)
     B, Hkv, n, d = K.shape
     dev = K.device
+    _need(cluster_id, "cluster_id", dtype=torch.int32, shape=(B, Hkv, n), device=dev)
+    _opt(flags, "flags", dtype=torch.int32, shape=(B, Hkv), device=dev)
+    _check_ws(ws, dev)
+    _on_gpu(K, "K")
+    dims = make_dims(K, 1)
+    dims.Hq = dims.Hkv
     count = torch.empty((B, Hkv, C), dtype=torch.int32, device=dev)
     sumK = torch.empty((B, Hkv, C, d), dtype=torch.float32, device=dev)
     sumV = torch.empty((B, Hkv, C, d), dtype=torch.float32, device=dev)
     sumK2 = torch.empty((B, Hkv, C, d), dtype=torch.float32, device=dev) if with_sumK2 else None
     ws, wsb = _workspace(workspace_bytes(dims, OP_BUILD_PROXIES, C=C), dev, ws)
-    rc = lib().sda_build_tail_proxies(ctypes.byref(dims), _ptr(K), _ptr(V), _ptr(_i32(cluster_id)), int(C),
+    rc = lib().sda_build_tail_proxies(ctypes.byref(dims), _ptr(K), _ptr(V), _ptr(cluster_id), int(C),
                                       _ptr(count), _ptr(sumK), _ptr(sumV), _ptr(sumK2), _ptr(flags), _ptr(ws),
                                       wsb, _stream(stream))
     _check(rc, "sda_build_tail_proxies")
@@ -268,11 +336,13 @@ def build_tail_proxies(K: torch.Tensor, V: torch.Tensor, cluster_id: torch.Tenso
 
 def build_prior(K: torch.Tensor, V: torch.Tensor, mu_Q: torch.Tensor, scale: Optional[float] = None,
                 ws: Optional[torch.Tensor] = None, stream=None) -> PriorState:
-    Hq = mu_Q.shape[1]
-    dims = make_dims(K, Hq, scale)
+    _check_kv(K, V)
     B, Hkv, n, d = K.shape
     dev = K.device
-    mu_Q = _f32c(mu_Q, "mu_Q")
+    Hq = _check_q(mu_Q, K, dtype=torch.float32)
+    _check_ws(ws, dev)
+    _on_gpu(K, "K")
+    dims = make_dims(K, Hq, scale)
     mu_K = torch.empty((B, Hkv, d), dtype=torch.float32, device=dev)
     O_est = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     maxP = torch.empty((B, Hq), dtype=torch.float32, device=dev)
@@ -287,11 +357,14 @@ def build_prior(K: torch.Tensor, V: torch.Tensor, mu_Q: torch.Tensor, scale: Opt
 def dense_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, scale: Optional[float] = None,
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       ws: Optional[torch.Tensor] = None, stream=None):
-    B, Hq, d = q.shape
+    _check_kv(K, V)
+    Hq = _check_q(q, K)
+    B, _, _, d = K.shape
+    dev = K.device
+    out, lse = _outputs(out, lse, B, Hq, d, dev)
+    _check_ws(ws, dev)
+    _on_gpu(K, "K")
     dims = make_dims(K, Hq, scale)
-    dev = q.device
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev) if out is None else out
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse is None else lse
     ws, wsb = _workspace(workspace_bytes(dims, OP_DENSE), dev, ws)
     rc = lib().sda_dense_decode_attn(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse),
                                      _ptr(ws), wsb, _stream(stream))
@@ -306,14 +379,28 @@ def sparse_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: O
                        scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
                        lse: Optional[torch.Tensor] = None, flags: Optional[torch.Tensor] = None,
                        ws: Optional[torch.Tensor] = None, m: Optional[int] = None, stream=None):
-    """One decode step; returns (out [B,Hq,d] fp32, lse [B,Hq] fp32)."""
-    B, Hq, d = q.shape
-    dims = make_dims(K, Hq, scale)
-    dev = q.device
-    if m is None:
-        m = 0 if idx is None else idx.shape[-1]
+    """One decode step; returns (out [B,Hq,d] fp32, lse [B,Hq] fp32).
+    idx is [B, Hkv, m] (m = idx.shape[-1]; `m`, if given, must agree), or None
+    for an empty list."""
+    _check_kv(K, V)
+    Hq = _check_q(q, K)
+    B, Hkv, n, d = K.shape
+    dev = K.device
+    if idx is None:
+        if m not in (None, 0):
+            raise ValueError("m must be 0 when idx is None")
+        m = 0
+    else:
+        _need(idx, "idx", dtype=torch.int32, device=dev)
+        if idx.dim() != 3 or tuple(idx.shape[:2]) != (B, Hkv):
+            raise ValueError(f"idx must be [B={B}, Hkv={Hkv}, m], got {tuple(idx.shape)}")
+        if m is not None and m != idx.shape[-1]:
+            raise ValueError(f"m = {m} does not match idx's last dimension {idx.shape[-1]}")
+        m = idx.shape[-1]
+    _opt(idx_len, "idx_len", dtype=torch.int32, shape=(B, Hkv), device=dev)
+    _opt(logw, "logw", dtype=torch.float32, shape=(B, Hkv, m), device=dev)
+    _opt(flags, "flags", dtype=torch.int32, shape=(B, Hkv), device=dev)
     if isinstance(tail, SampledTail):
-        Hkv = K.shape[1]
         if tail.b is None:
             tail.b = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
         if tail.bstar is None:
@@ -321,12 +408,14 @@ def sparse_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: O
         if tail.samples is None and tail.b_cap > 0:
             tail.samples = torch.full((B, Hkv, tail.b_cap), -1, dtype=torch.int32, device=dev)
     keep = []
-    t = _tail_struct(tail, idx_cluster, cluster_id, lam, keep)
-    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev) if out is None else out
-    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if lse is None else lse
+    t = _tail_struct(tail, idx_cluster, cluster_id, lam, keep, B, Hq, Hkv, n, d, m, dev)
+    out, lse = _outputs(out, lse, B, Hq, d, dev)
+    _check_ws(ws, dev)
+    _on_gpu(K, "K")
+    dims = make_dims(K, Hq, scale)
     ws, wsb = _workspace(workspace_bytes(dims, OP_SPARSE, t.kind, m, getattr(tail, "C", 0)), dev, ws)
-    rc = lib().sda_sparse_decode_attn(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V), _ptr(_i32(idx)),
-                                      _ptr(_i32(idx_len)), _ptr(_f32c(logw, "logw")), int(m), ctypes.byref(t),
+    rc = lib().sda_sparse_decode_attn(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V), _ptr(idx),
+                                      _ptr(idx_len), _ptr(logw), int(m), ctypes.byref(t),
                                       _ptr(out), _ptr(lse), _ptr(flags), _ptr(ws), wsb, _stream(stream))
     _check(rc, "sda_sparse_decode_attn")
     return out, lse
@@ -342,13 +431,16 @@ class QgsCodes:
 
 def build_qgs_codes(K: torch.Tensor, U: torch.Tensor, ws: Optional[torch.Tensor] = None,
                     stream=None) -> QgsCodes:
-    dims = make_dims(K, 1)
-    dims.Hq = dims.Hkv
+    _need(K, "K", contiguous=False)
+    if K.dim() != 4:
+        raise ValueError("K must be a [B, Hkv, n, d] view")
     B, Hkv, n, d = K.shape
     dev = K.device
-    U = _f32c(U, "U")
-    if tuple(U.shape) != (B, Hkv, d, QGS_RANK):
-        raise ValueError(f"U must be [B, Hkv, d, {QGS_RANK}]")
+    _need(U, "U", dtype=torch.float32, shape=(B, Hkv, d, QGS_RANK), device=dev)
+    _check_ws(ws, dev)
+    _on_gpu(K, "K")
+    dims = make_dims(K, 1)
+    dims.Hq = dims.Hkv
     codes = torch.empty((B, Hkv, n, QGS_RANK), dtype=torch.int8, device=dev)
     kmax = torch.empty((B, Hkv, QGS_RANK), dtype=torch.float64, device=dev)
     ws, wsb = _workspace(workspace_bytes(dims, OP_BUILD_QGS), dev, ws)
@@ -364,12 +456,22 @@ def select_qgs(q: torch.Tensor, K: torch.Tensor, cluster_id: torch.Tensor, proxi
                flags: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None, stream=None):
     """The selector: returns (idx [B,Hkv,m], idx_len [B,Hkv], idx_cluster [B,Hkv,m]); fills budget
     [B,Hkv,C] when given.  K only supplies the cache's shape and strides."""
-    B, Hq, d = q.shape
-    dims = make_dims(K, Hq, scale)
-    n, Hkv = K.shape[2], K.shape[1]
-    dev = q.device
+    _need(K, "K", contiguous=False)
+    if K.dim() != 4:
+        raise ValueError("K must be a [B, Hkv, n, d] view")
+    Hq = _check_q(q, K)
+    B, Hkv, n, d = K.shape
+    dev = K.device
+    C = int(proxies.C)
     if proxies.sumK2 is None:
         raise ValueError("the selector needs the proxies built with with_sumK2=True")
+    _need(cluster_id, "cluster_id", dtype=torch.int32, shape=(B, Hkv, n), device=dev)
+    _need(proxies.count, "count", dtype=torch.int32, shape=(B, Hkv, C), device=dev)
+    for name in ("sumK", "sumK2"):
+        _need(getattr(proxies, name), name, dtype=torch.float32, shape=(B, Hkv, C, d), device=dev)
+    _need(qc.U, "U", dtype=torch.float32, shape=(B, Hkv, d, QGS_RANK), device=dev)
+    _need(qc.codes, "codes", dtype=torch.int8, shape=(B, Hkv, n, QGS_RANK), device=dev)
+    _need(qc.kmax, "kmax", dtype=torch.float64, shape=(B, Hkv, QGS_RANK), device=dev)
     if m is None:
         m = min(n, n_sink + n_local + E)
     if out is None:
@@ -377,10 +479,17 @@ def select_qgs(q: torch.Tensor, K: torch.Tensor, cluster_id: torch.Tensor, proxi
                torch.empty((B, Hkv), dtype=torch.int32, device=dev),
                torch.empty((B, Hkv, m), dtype=torch.int32, device=dev))
     idx, idx_len, idx_cluster = out
-    sel = Selector(int(n_sink), int(n_local), int(E), int(proxies.C), _ptr(_i32(cluster_id)),
-                   _ptr(_i32(proxies.count)), _ptr(_f32c(proxies.sumK, "sumK")),
-                   _ptr(_f32c(proxies.sumK2, "sumK2")), _ptr(_f32c(qc.U, "U")), _ptr(qc.codes), _ptr(qc.kmax))
-    ws, wsb = _workspace(workspace_bytes(dims, OP_SELECT_QGS, C=proxies.C), dev, ws)
+    _need(idx, "idx", dtype=torch.int32, shape=(B, Hkv, m), device=dev)
+    _need(idx_len, "idx_len", dtype=torch.int32, shape=(B, Hkv), device=dev)
+    _need(idx_cluster, "idx_cluster", dtype=torch.int32, shape=(B, Hkv, m), device=dev)
+    _opt(budget, "budget", dtype=torch.int32, shape=(B, Hkv, C), device=dev)
+    _opt(flags, "flags", dtype=torch.int32, shape=(B, Hkv), device=dev)
+    _check_ws(ws, dev)
+    _on_gpu(K, "K")
+    dims = make_dims(K, Hq, scale)
+    sel = Selector(int(n_sink), int(n_local), int(E), C, _ptr(cluster_id), _ptr(proxies.count), _ptr(proxies.sumK),
+                   _ptr(proxies.sumK2), _ptr(qc.U), _ptr(qc.codes), _ptr(qc.kmax))
+    ws, wsb = _workspace(workspace_bytes(dims, OP_SELECT_QGS, C=C), dev, ws)
     rc = lib().sda_select_qgs(ctypes.byref(dims), _ptr(q), ctypes.byref(sel), int(m), _ptr(idx), _ptr(idx_len),
                               _ptr(idx_cluster), _ptr(budget), _ptr(flags), _ptr(ws), wsb, _stream(stream))
     _check(rc, "sda_select_qgs")
@@ -392,14 +501,19 @@ def build_qgc_clusters(K: torch.Tensor, V: torch.Tensor, C: int, T: int = 10,
                        stream=None) -> torch.Tensor:
     """Query-geometry clustering of the keys: cluster ids [B, Hkv, n] int32
     from the basis V [B, Hkv, d, 16] (k-means with T passes)."""
+    _need(K, "K", contiguous=False)
+    if K.dim() != 4:
+        raise ValueError("K must be a [B, Hkv, n, d] view")
+    B, Hkv, n, d = K.shape
+    dev = K.device
+    _need(V, "V", dtype=torch.float32, shape=(B, Hkv, d, QGC_RANK), device=dev)
+    _opt(flags, "flags", dtype=torch.int32, shape=(B, Hkv), device=dev)
+    _check_ws(ws, dev)
+    _on_gpu(K, "K")
     dims = make_dims(K, 1)
     dims.Hq = dims.Hkv
-    B, Hkv, n, d = K.shape
-    V = _f32c(V, "V")
-    if tuple(V.shape) != (B, Hkv, d, QGC_RANK):
-        raise ValueError(f"V must be [B, Hkv, d, {QGC_RANK}]")
-    cid = torch.empty((B, Hkv, n), dtype=torch.int32, device=K.device)
-    ws, wsb = _workspace(workspace_bytes(dims, OP_BUILD_QGC, C=C), K.device, ws)
+    cid = torch.empty((B, Hkv, n), dtype=torch.int32, device=dev)
+    ws, wsb = _workspace(workspace_bytes(dims, OP_BUILD_QGC, C=C), dev, ws)
     rc = lib().sda_build_qgc_clusters(ctypes.byref(dims), _ptr(K), _ptr(V), int(C), int(T), _ptr(cid), _ptr(flags),
                                       _ptr(ws), wsb, _stream(stream))
     _check(rc, "sda_build_qgc_clusters")
