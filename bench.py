@@ -226,7 +226,7 @@ def main():
                    "timing": "eager launches" if a.no_graph else "HIP graph replay of the timed steps"},
         "roofline": {"bound": "hbm", "achieved": round(tot_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(tot_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "sparse_unit_mfma_kernel<4, proxy, 3>", "bytes_per_launch": bytes_["total"],
+                     "kernel": "sparse_unit_vt_kernel<4, proxy, 3>", "bytes_per_launch": bytes_["total"],
                      "bytes_breakdown": bytes_},
         "dense_us_per_step": None if dense_ms is None else round(dense_ms * 1e3, 2),
         "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms, 2),

@@ -311,6 +311,22 @@ sda_status sda_select_qgs(const sda_dims* dims, const void* q, const sda_selecto
                           int32_t* budget, int32_t* dev_flags, void* ws, size_t ws_bytes,
                           void* stream);
 
+/* ---- Measurement aid ----------------------------------------------------
+ * Not part of the method: reads the listed K and V rows of every unit (the
+ * first m entries of idx per unit; positions outside [0, n) are skipped)
+ * and, when state_bytes > 0, state_bytes bytes of per-unit state at
+ * state + u * state_bytes, with `parts` workgroups of `waves` waves per unit
+ * (waves in {4, 8, 16}, parts in [1, 16]), and writes the XOR of every
+ * 32-bit word a wave loaded to checksum[(u * parts + part) * waves + wave]
+ * ([B * Hkv * parts * waves] uint32).  It computes nothing else: timing it
+ * beside sda_sparse_decode_attn gives the rate at which the memory system
+ * delivers the same rows in that launch shape.  Returns SDA_EUNSUPPORTED
+ * when a row group would hold more rows than the kernel keeps in registers
+ * (24 at 4 or 8 waves, 12 at 16).  K, V and state 16-byte aligned. */
+sda_status sda_gather_rows(const sda_dims* dims, const void* K, const void* V, const int32_t* idx,
+                           int32_t m, const void* state, int64_t state_bytes, int32_t waves,
+                           int32_t parts, uint32_t* checksum, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -571,3 +571,38 @@ SDA_EXPORT sda_status sda_build_qgc_clusters(const sda_dims* dims, const void* K
   p.flags = dev_flags;
   return hip_status(launch_qgc(p, r.dtype, r.B * r.Hkv, T, reinterpret_cast<hipStream_t>(stream)));
 }
+
+SDA_EXPORT sda_status sda_gather_rows(const sda_dims* dims, const void* K, const void* V, const int32_t* idx,
+                                      int32_t m, const void* state, int64_t state_bytes, int32_t waves,
+                                      int32_t parts, uint32_t* checksum, void* stream) {
+  Resolved r;
+  sda_status st = resolve(dims, &r);
+  if (st != SDA_OK) return st;
+  if (!K || !V || !checksum || (m > 0 && !idx)) return SDA_EINVAL;
+  if (!aligned16(K) || !aligned16(V)) return SDA_EINVAL;
+  if (m < 0 || state_bytes < 0) return SDA_ESHAPE;
+  if (state_bytes > 0 && (!state || !aligned16(state) || state_bytes % 16)) return SDA_EINVAL;
+  if (waves != 4 && waves != 8 && waves != 16) return SDA_EUNSUPPORTED;
+  if (parts < 1 || parts > 16) return SDA_EUNSUPPORTED;
+  const int rows = gather_rows_per_group(m, waves, parts);
+  if (rows > (waves == 16 ? 12 : 24)) return SDA_EUNSUPPORTED;
+  GatherParams p;
+  memset(&p, 0, sizeof(p));
+  p.K = K;
+  p.V = V;
+  // with an empty list the kernel still reads one (discarded) word
+  p.idx = idx ? idx : reinterpret_cast<const int32_t*>(checksum);
+  p.state = state;
+  p.state_bytes = state_bytes;
+  p.sb = r.sb;
+  p.sh = r.sh;
+  p.sn = r.sn;
+  p.esize = (int)r.esize;
+  p.row_bytes = (int)(r.sn * (int64_t)r.esize);
+  p.Hkv = r.Hkv;
+  p.n = r.n;
+  p.m = m;
+  p.parts = parts;
+  p.checksum = checksum;
+  return hip_status(launch_gather_rows(p, waves, r.B * r.Hkv, reinterpret_cast<hipStream_t>(stream)));
+}

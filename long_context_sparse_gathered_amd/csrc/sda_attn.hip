@@ -1,18 +1,23 @@
 // sda_attn.hip -- decode-attention kernels for gfx950.
 //
-//  sparse_unit_kernel   one 512-thread workgroup per (sequence, KV head):
-//                       gathers every listed K and V row at once, two-pass
-//                       softmax with an exact unit maximum, optional
-//                       count-aware mean proxies ("OpenAttention", method
-//                       stages 04-05: exact rows and proxies share one
-//                       softmax).
-//  stream_kernel        split-K streaming kernel with a per-row-group online
-//                       softmax; serves plain sparse lists, the rank-1 prior
-//                       ("RESA", Online Aggregator), dense decode and the
-//                       prior build ("RESA", Prior Estimator: one extra query
-//                       over the whole cache).
-//  merge_kernel         log-sum-exp merge of split partials + the prior's
-//                       delta merge.
+//  sparse_unit_kernel      one 512-thread workgroup per (sequence, KV head),
+//                          fp32 rows: gathers every listed K and V row at
+//                          once, two-pass softmax with an exact unit maximum,
+//                          optional count-aware mean proxies
+//                          ("OpenAttention", method stages 04-05: exact rows
+//                          and proxies share one softmax).
+//  sparse_unit_vt_kernel   the same for bf16 rows with up to four query heads
+//                          per KV head: logits and weighted values on the
+//                          matrix cores, value rows in registers.
+//  sparse_unit_mfma_kernel the same for bf16 rows with eight query heads per
+//                          KV head: value tiles staged in LDS.
+//  stream_kernel,          split-K streaming kernels with an online softmax;
+//  stream_mfma_kernel      they serve plain sparse lists, the rank-1 prior
+//                          ("RESA", Online Aggregator), dense decode and the
+//                          prior build ("RESA", Prior Estimator: one extra
+//                          query over the whole cache).
+//  merge_kernel            log-sum-exp merge of split partials + the prior's
+//                          delta merge.
 #include "sda_device.hpp"
 #include "sda_kernels.hpp"
 
@@ -1228,6 +1233,542 @@ __global__ __launch_bounds__(512) void sparse_unit_mfma_kernel(const AttnParams 
 }
 
 // ---------------------------------------------------------------------------
+// bf16 one-workgroup-per-unit kernel, value rows in registers (G <= 4).
+//
+// The logits run on the matrix cores as in sparse_unit_mfma_kernel (keys
+// fetched in the MFMA operand layout, 16 keys x 64 bytes per load).  The
+// value rows go to registers in the row layout: row group `sub` of wave w
+// takes value slot k = list entry 16t + 4kq + sub (k = 4t + kq) of the wave's
+// run, lane r16 holding dims 8*r16 .. +8 (one 16-byte load per slot, four
+// whole rows per instruction).  The weighted values then run on the matrix
+// cores with no LDS staging: for a block of eight slots the B operand of
+// v_mfma_f32_16x16x32_bf16 for dim offset i is built with byte permutes from
+// the eight slot registers (K index 8*sub + j = key 32*kb + 4j + sub, column
+// r16 = dim 8*r16 + i), so a block is multiplied as soon as its rows land.
+//
+// The A operand holds each weight as three bf16 parts (rows h, 4 + h and
+// 8 + h: high part, middle part and remainder, together exact to fp32), so
+// the products carry the fp32 weights.  The weight of a read member of
+// cluster b is e^{s - M} - e^{mu_b - M}; the cluster term e^{mu_b - M} sumV_b
+// is added in fp32 on the vector units by the lanes that hold cluster b's
+// sums, so the read members' share of sumV_b cancels at fp32 accuracy.
+template <int G, bool PROXY, int NT>
+__global__ __launch_bounds__(512) void sparse_unit_vt_kernel(const AttnParams p) {
+  constexpr int W = kUnitWaves;
+  constexpr int NS = 4 * NT;   // value slots per row group
+  constexpr int PC = PROXY ? kCmax : 1;
+  constexpr int PW = PROXY ? W : 1;
+  const int u = blockIdx.x;
+  const int s = u / p.Hkv;
+  const int g = u - s * p.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, sub = lane >> 4;
+  const int CH = p.chunk;      // entries of this wave: [w*CH, (w+1)*CH), CH <= 16*NT
+  const int hr = r16 < G ? r16 : 0;  // head of this lane in the [head][..] layouts (clamped)
+
+  constexpr int NV = G < 4 ? 1 : G / 4;  // heads per lane in the key layout
+  static_assert(W % 4 == 0, "per-wave results are read four at a time");
+  __shared__ __attribute__((aligned(16))) float s_wmax[G][W];
+  __shared__ __attribute__((aligned(16))) float s_pmax[G][PW];
+  __shared__ float s_M[G];
+  __shared__ __attribute__((aligned(16))) float s_l[G][W];   // normaliser: the wave's keys
+  __shared__ __attribute__((aligned(16))) float s_lp[G][PW]; // and its proxies
+  __shared__ __attribute__((aligned(16))) float s_csum[PC][G][PW];
+  __shared__ __attribute__((aligned(16))) int s_ccnt[PC][PW];
+  // mean logit of a cluster's unread members (-inf if none), per head; entry
+  // PC is a -inf sentinel for keys outside every cluster
+  __shared__ __attribute__((aligned(16))) float s_mu[G][PC + 4];
+  // list entries of the value slots, handed from the key loads' lanes
+  __shared__ __attribute__((aligned(16))) int s_jv[W][NT][4][4];
+  static_assert(G <= 4, "three weight parts per head fill at most 12 operand rows");
+  constexpr int KB = (NT + 1) / 2;   // blocks of 32 keys (8 slots per row group)
+  // weights as the value products' A operand: per wave, block kb, operand row
+  // m (head m & 3, part m >> 2), key group kg and j: key 32kb + 4j + kg
+  __shared__ __attribute__((aligned(16))) __bf16 s_wa[W][KB][16][4][8];
+  // the waves' output partials, [wave][head][dim]
+  __shared__ __attribute__((aligned(16))) float s_red[W][G][kD];
+
+  // ---- prologue ------------------------------------------------------------
+  // Every load that does not depend on the list is issued before the first
+  // use of any loaded value: the query, the list entries and the cluster sums
+  // share one memory round trip.  (With no list, and for absent optional
+  // arrays, the loads read a valid dummy address and the values are
+  // discarded.)
+  const int64_t lbase = (int64_t)u * p.m;
+  const int e = w * CH + lane;
+  const bool in_list = (lane < CH) && (e < p.m);
+  const int32_t* lst = p.m > 0 ? p.idx : reinterpret_cast<const int32_t*>(p.q);
+  const int64_t ea = lbase + (in_list ? e : 0);
+  int li = lst[ea];
+  int lp = -1, lc = -1;
+  if constexpr (PROXY) {
+    lp = lst[lbase + ((in_list && e > 0) ? e - 1 : 0)];
+    lc = (p.idx_cluster ? p.idx_cluster : lst)[ea];
+  }
+  const float lwv = (p.logw ? p.logw : reinterpret_cast<const float*>(lst))[ea];
+  auto entry = [&](int pos) { return w * CH + pos; };
+  auto listed = [&](int pos) { return pos < CH && entry(pos) < p.m; };
+  int jk[NT];  // key rows of this lane: entry 16t + r16 of tile t
+#pragma unroll
+  for (int t = 0; t < NT; ++t) jk[t] = lst[lbase + (listed(16 * t + r16) ? entry(16 * t + r16) : 0)];
+
+  const int64_t qrow0 = (int64_t)s * p.Hq + (int64_t)g * G;
+  uint4 qa[4];  // MFMA A operand: head r16 (zero past G), dims 32*st + 8*sub
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+    qa[st] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(p.q) + (qrow0 + hr) * kD + 32 * st +
+                                             8 * sub);
+  float qf[PROXY ? G : 1][8];  // row-layout query for the cluster-sum logits
+  if constexpr (PROXY) load_query<bf16_t, G>(p.q, qrow0, r16, p.qscale, qf);
+
+  // cluster sums and counts of the two clusters this lane owns: b0 = 4w + sub
+  // and b1 = b0 + 32 (dims 8*r16 .. +8 of the sums); with C <= 32 there is no
+  // b1 and its loads are skipped (a uniform branch)
+  const int b0 = 4 * w + sub, b1 = b0 + 4 * W;
+  const bool has0 = PROXY && b0 < p.C, has1 = PROXY && b1 < p.C;
+  const bool two = PROXY && p.C > 4 * W;
+  float skf[8], svf[8], sk1[8], sv1[8];
+  int cnt0 = 0, cnt1 = 0;
+  if constexpr (PROXY) {
+    const int64_t c0 = (int64_t)u * p.C + (has0 ? b0 : 0);
+    load8f(p.sumK + c0 * kD + 8 * r16, skf);
+    load8f(p.sumV + c0 * kD + 8 * r16, svf);
+    cnt0 = p.count[c0];
+    if (two) {
+      const int64_t c1 = (int64_t)u * p.C + (has1 ? b1 : 0);
+      load8f(p.sumK + c1 * kD + 8 * r16, sk1);
+      load8f(p.sumV + c1 * kD + 8 * r16, sv1);
+      cnt1 = p.count[c1];
+    }
+  }
+
+  int len = p.m;
+  if (p.idx_len) {
+    int L = p.idx_len[u];
+    if (L < 0 || L > p.m) {
+      if (tid == 0) flag_unit(p.flags, u, SDA_FLAG_LEN);
+      L = L < 0 ? 0 : p.m;
+    }
+    len = L;
+  }
+
+  // ---- addresses ------------------------------------------------------------
+  // The unit's rows span less than 2^31 bytes (checked on the host), so byte
+  // offsets are 32-bit; an absent row reads past the resource and returns
+  // zeros.
+  const bool live = in_list && e < len;
+  const bool in_range = (unsigned)li < (unsigned)p.n;
+  const bool valid = live && in_range;
+  const int rs = 2 * (int)p.sn;
+  auto row_byte = [&](int pos, int j, int c) {
+    const bool ok = (pos < CH) & (entry(pos) < len) & ((unsigned)j < (unsigned)p.n);
+    return __builtin_unpredictable(ok) ? j * rs + c : kOOB;
+  };
+  int koff[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) koff[t] = row_byte(16 * t + r16, jk[t], 16 * sub);
+  // value slot k = 4t + kq is entry 16t + 4kq + sub: its list entry comes
+  // from the key lanes through LDS
+  if (sub == 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) s_jv[w][t][r16 & 3][r16 >> 2] = jk[t];
+  }
+  wave_lds_sync();
+  int voff[NS];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int4 j4 = *reinterpret_cast<const int4*>(&s_jv[w][t][sub][0]);
+    const int jv[4] = {j4.x, j4.y, j4.z, j4.w};
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) voff[4 * t + kq] = row_byte(16 * t + 4 * kq + sub, jv[kq], 16 * r16);
+  }
+
+  // cluster of this lane's entry from the per-row ids when the list carries
+  // none: issued ahead of the row loads (loads complete in issue order)
+  if constexpr (PROXY) {
+    if (!p.idx_cluster) lc = valid ? p.cluster_id[(int64_t)u * p.n + li] : -1;
+  }
+
+  // ---- row loads (streaming: read once) -------------------------------------
+  // Keys first (MFMA layout); the work below that needs no row runs while they
+  // are in flight (the memory queues are full by then), then the values (row
+  // layout, to registers).
+  const int64_t kvoff = (int64_t)s * p.sb + (int64_t)g * p.sh;
+  const rsrc_t rk = make_rsrc<bf16_t>(reinterpret_cast<const bf16_t*>(p.K) + kvoff, p.n, p.sn);
+  const rsrc_t rv = make_rsrc<bf16_t>(reinterpret_cast<const bf16_t*>(p.V) + kvoff, p.n, p.sn);
+  uint4 kt[NT][4];
+  uint4 vt[NS];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[t] + 64 * st, 0, kLoadNT);
+      kt[t][st] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+    if (r16 >= G) qa[st] = make_uint4(0, 0, 0, 0);
+
+  // ---- checks and cluster lookups, behind the key loads ---------------------
+  const float lw_own = valid ? (p.logw ? lwv * kLog2e : 0.f) : kNegInf;
+  const bool bad_cluster = PROXY && p.idx_cluster && valid && (lc < -1 || lc >= p.C);
+  if (bad_cluster) lc = -1;
+  {
+    int bad = 0;
+    if (live && !in_range) bad |= SDA_FLAG_IDX_RANGE;
+    if (PROXY && live && e > 0 && lp >= li) bad |= SDA_FLAG_IDX_ORDER;
+    if (bad_cluster) bad |= SDA_FLAG_CLUSTER;
+    if (bad) flag_unit(p.flags, u, bad);
+  }
+  float qk0 = 0.f, qk1 = 0.f;  // q . (sum of keys) of clusters b0, b1 for head r16
+  if constexpr (PROXY) {
+    if (!has0) cnt0 = 0;
+    if (!has1) cnt1 = 0;
+#pragma unroll
+    for (int i = lane; i < PC * G; i += 64) s_csum[i / G][i % G][w] = 0.f;
+    for (int i = lane; i < PC; i += 64) s_ccnt[i][w] = 0;
+    float a[G];
+    dot_heads<G>(qf, skf, a);
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+      if (r16 == h) qk0 = a[h];
+    if (two) {
+      dot_heads<G>(qf, sk1, a);
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+        if (r16 == h) qk1 = a[h];
+    }
+  }
+
+  // ---- per key tile: log-weight and cluster of this lane's key -------------
+  // (key layout, below) and the controls of the segmented sums over runs of
+  // keys with the same cluster (consecutive lanes of a row group). The read
+  // members' counts per cluster are added here; their logit sums follow the
+  // logits.
+  float lwk[NT];
+  int cmr[NT];  // cluster of the key, -1 if none
+  float sf[NT][4];
+  bool run_end[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int kk = 16 * t + r16;  // this lane's key within the wave's entries
+    lwk[t] = shfl_f(lw_own, kk);
+    cmr[t] = -1;
+    run_end[t] = false;
+    if constexpr (PROXY) {
+      const int ck = shfl_i(lc, kk);
+      const int cm = (lwk[t] != kNegInf && ck >= 0 && ck < p.C) ? ck : -1;
+      cmr[t] = cm;
+      const int cprev = dpp_i<0x111>(cm, -2), cnext = dpp_i<0x101>(cm, -2);  // row_shr:1, row_shl:1
+      int start = cprev != cm ? r16 : 0;
+      start = max(start, dpp_i<0x111>(start, 0));
+      start = max(start, dpp_i<0x112>(start, 0));
+      start = max(start, dpp_i<0x114>(start, 0));
+      start = max(start, dpp_i<0x118>(start, 0));
+      sf[t][0] = r16 - 1 >= start ? 1.f : 0.f;
+      sf[t][1] = r16 - 2 >= start ? 1.f : 0.f;
+      sf[t][2] = r16 - 4 >= start ? 1.f : 0.f;
+      sf[t][3] = r16 - 8 >= start ? 1.f : 0.f;
+      run_end[t] = cm >= 0 && cnext != cm;  // last lane of a run
+      if (run_end[t] && sub == 0) lds_add(&s_ccnt[cm][w], r16 - start + 1);
+    }
+  }
+
+  // ---- value rows, to registers -----------------------------------------------
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    auto v = __builtin_amdgcn_raw_buffer_load_b128(rv, voff[k], 0, kLoadNT);
+    vt[k] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- logits on the matrix cores ------------------------------------------
+  // The MFMA leaves lane (key r16, group sub) the logits of heads 4*sub + i;
+  // a 4 x 4 transpose of row groups turns that into the key layout: lane
+  // (sub, r16) holds heads 4j + sub (j < NV) of key 16t + r16 of tile t.
+  float xr[NT][NV];  // logit plus log-weight (log2 units)
+  float mxr[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) mxr[j] = kNegInf;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    floatx4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
+                                                  __builtin_bit_cast(bf16x8_t, kt[t][st]), d, 0, 0, 0);
+    float sv[4], hv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = d[i] * p.qscale;
+    transpose_rows(sv, hv);
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      xr[t][j] = hv[j] + lwk[t];
+      mxr[j] = fmaxf(mxr[j], xr[t][j]);
+    }
+    if constexpr (PROXY) {
+      // read members' logit sums per cluster (this wave's slice): inclusive
+      // sums within runs by 0/1-weighted DPP steps (no branches: a move must
+      // not read a lane that sits out); the last lane of each run adds the
+      // run total
+#pragma unroll
+      for (int j = 0; j < NV; ++j) {
+        float x = hv[j];
+        x = fmaf(sf[t][0], dppz<0x111>(x), x);
+        x = fmaf(sf[t][1], dppz<0x112>(x), x);
+        x = fmaf(sf[t][2], dppz<0x114>(x), x);
+        x = fmaf(sf[t][3], dppz<0x118>(x), x);
+        hv[j] = x;
+      }
+      if (run_end[t]) {
+#pragma unroll
+        for (int j = 0; j < NV; ++j)
+          if (4 * j + sub < G) lds_add(&s_csum[cmr[t]][4 * j + sub][w], hv[j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const float v = max16(mxr[j]);
+    if (r16 == 0 && 4 * j + sub < G) s_wmax[4 * j + sub][w] = v;
+  }
+  lds_barrier();
+
+  // ---- proxy logits of the clusters this wave owns ------------------------
+  // Unread members of cluster b: n_b = count - (read members); their mean
+  // logit mu_b = (q.sumK_b - sum of the read members' logits) / n_b; the
+  // proxy logit is mu_b + log2(n_b).
+  float Mk = kNegInf;  // maximum of the read logits, head hr
+#pragma unroll
+  for (int q = 0; q < W / 4; ++q) {
+    const float4 m4 = *reinterpret_cast<const float4*>(&s_wmax[hr][4 * q]);
+    Mk = fmaxf(Mk, fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w)));
+  }
+  float pi0 = kNegInf, pi1 = kNegInf;
+  if constexpr (PROXY) {
+    float cs0 = 0.f, cs1 = 0.f;
+    int rc0 = 0, rc1 = 0;
+#pragma unroll
+    for (int q = 0; q < W / 4; ++q) {
+      const float4 a0 = *reinterpret_cast<const float4*>(&s_csum[b0][hr][4 * q]);
+      const float4 a1 = *reinterpret_cast<const float4*>(&s_csum[b1][hr][4 * q]);
+      const int4 n0 = *reinterpret_cast<const int4*>(&s_ccnt[b0][4 * q]);
+      const int4 n1 = *reinterpret_cast<const int4*>(&s_ccnt[b1][4 * q]);
+      cs0 += (a0.x + a0.y) + (a0.z + a0.w);
+      cs1 += (a1.x + a1.y) + (a1.z + a1.w);
+      rc0 += n0.x + n0.y + n0.z + n0.w;
+      rc1 += n1.x + n1.y + n1.z + n1.w;
+    }
+    bool neg_count = false;  // more read members than the cluster holds
+    auto mean_logit = [&](int b, bool has, float qk, int cntb, float cs, int rc, float& pi) {
+      const int nb = cntb - rc;
+      neg_count |= has && nb < 0 && r16 == 0;
+      const bool ok = has && nb > 0;
+      const float nbf = (float)(ok ? nb : 1);
+      const float mu = ok ? (qk - cs) * __builtin_amdgcn_rcpf(nbf) : kNegInf;  // (hardware reciprocal, ~1 ulp)
+      pi = (ok && r16 < G) ? mu + __builtin_amdgcn_logf(nbf) : kNegInf;
+      if (r16 < G) s_mu[r16][b] = mu;
+    };
+    mean_logit(b0, has0, qk0, cnt0, cs0, rc0, pi0);
+    mean_logit(b1, has1, qk1, cnt1, cs1, rc1, pi1);
+    if (w == 0 && sub == 0 && r16 < G) s_mu[r16][PC] = kNegInf;
+    const float pm = max_rowgroups(fmaxf(pi0, pi1));
+    if (sub == 0 && r16 < G) s_pmax[r16][w] = pm;
+    lds_barrier();
+    if (neg_count) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
+  }
+
+  // ---- unit maximum (every wave, same value) --------------------------------
+  float Mh = Mk;  // head hr
+  if constexpr (PROXY) {
+#pragma unroll
+    for (int ww = 0; ww < W; ww += 4) {
+      const float4 m4 = *reinterpret_cast<const float4*>(&s_pmax[hr][ww]);
+      Mh = fmaxf(Mh, fmaxf(fmaxf(m4.x, m4.y), fmaxf(m4.z, m4.w)));
+    }
+  }
+  if (Mh == kNegInf) Mh = 0.f;
+  if (w == 0 && sub == 0 && r16 < G) s_M[r16] = Mh;
+  float Mu[G];   // every head's maximum, uniform (lane h computed head h)
+#pragma unroll
+  for (int h = 0; h < G; ++h) Mu[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(Mh), h));
+  float Mr[NV];  // the same in the key layout: head 4j + sub (a select, no lane shuffle)
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    Mr[j] = Mu[0];
+#pragma unroll
+    for (int h = 1; h < G; ++h)
+      if (4 * j + sub == h) Mr[j] = Mu[h];
+  }
+
+  // ---- weights, in the key layout -------------------------------------------
+  // w = exp2(x - M), minus exp2(mu_b - M) for a read member of cluster b
+  // (whose value the cluster term counts in the cluster's sum), split into
+  // three bf16 parts that sum to w exactly (each part takes 8 of w's 24
+  // significant bits)
+  float lsr[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) lsr[j] = 0.f;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int h = 4 * j + sub;
+      const float ev = fast_exp2(xr[t][j] - Mr[j]);
+      lsr[j] += ev;
+      float wv = ev;
+      if constexpr (PROXY) {
+        const float mu = s_mu[h < G ? h : 0][cmr[t] >= 0 ? cmr[t] : PC];
+        wv = ev - fast_exp2(mu - Mr[j]);
+      }
+      const __bf16 w0 = (__bf16)wv;
+      const float r1 = wv - (float)w0;
+      const __bf16 w1 = (__bf16)r1;
+      const __bf16 w2 = (__bf16)(r1 - (float)w1);
+      if (h < G) {
+        const int kk = 16 * t + r16;  // key within the wave's entries
+        __bf16* dst = &s_wa[w][kk >> 5][h][kk & 3][(kk >> 2) & 7];
+        dst[0] = w0;
+        dst[4 * 4 * 8] = w1;   // row h + 4
+        dst[8 * 4 * 8] = w2;   // row h + 8
+      }
+    }
+  }
+  // the proxies' share of the normaliser (lanes of head r16, clusters b0, b1;
+  // exp2(-inf) = 0 for the absent ones)
+  float lsum = 0.f;
+  if constexpr (PROXY) lsum = fast_exp2(pi0 - Mh) + fast_exp2(pi1 - Mh);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int h = 4 * j + sub;
+    const float tot = sum16(lsr[j]);
+    if (r16 == 0 && h < G) s_l[h][w] = tot;
+  }
+  if constexpr (PROXY) {
+    lsum = sum_rowgroups(lsum);
+    if (sub == 0 && r16 < G) s_lp[r16][w] = lsum;
+  }
+
+  // ---- lane swaps that sum over row groups ------------------------------------
+  // v_permlane16_swap(a, b) leaves even rows (a_even, a_odd) and odd rows
+  // (b_even, b_odd): with a = what even rows keep and b = what odd rows keep,
+  // one add per value sums a pair of rows and halves what each lane holds
+  // (permlane32_swap likewise for rows 0-1 against 2-3).
+  auto swap_add16 = [](float a, float b) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  };
+  auto swap_add32 = [](float a, float b) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  };
+
+  // ---- weighted values on the matrix cores -----------------------------------
+  // A (lane: operand row r16, key group sub): the three weight parts of head
+  // r16 & 3 for keys 32kb + 4j + sub (j = 0..7); rows of absent heads and
+  // the fourth part row set are zero, as are keys past the wave's 16*NT.
+  // B for dim offset i (lane: key group sub, column r16): dim 8*r16 + i of
+  // slots 8kb + j, two slots per 32-bit word by a byte permute.
+  //
+  // The accumulators start from the cluster terms of this lane's clusters:
+  // acc[i][r] (head r, dim 8*r16 + i) = e^{mu_b0 - M_r} sumV_b0[8*r16 + i]
+  // (+ the same for b1), fp32; the sum over the row groups below adds them up
+  // with the products' parts.
+  floatx4_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (PROXY) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float c0 = fast_exp2(s_mu[h][has0 ? b0 : PC] - Mu[h]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i][h] = c0 * svf[i];
+    }
+    if (two) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float c1 = fast_exp2(s_mu[h][has1 ? b1 : PC] - Mu[h]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i][h] = fmaf(c1, sv1[i], acc[i][h]);
+      }
+    }
+  }
+  wave_lds_sync();  // the weights, written by other lanes of this wave
+  const bool arow = (r16 & 3) < G && r16 < 12;
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    uint4 a4 = *reinterpret_cast<const uint4*>(&s_wa[w][kb][r16][sub][0]);
+    if (!arow) a4 = make_uint4(0, 0, 0, 0);
+    if (8 * kb + 8 > NS) a4.z = a4.w = 0;  // slots past the wave's keys
+    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, a4);
+    uint32_t vw[8][4];  // [slot j][word]
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int k = 8 * kb + j;
+      if (k < NS) {
+        vw[j][0] = vt[k].x; vw[j][1] = vt[k].y; vw[j][2] = vt[k].z; vw[j][3] = vt[k].w;
+      } else {
+        vw[j][0] = vw[j][1] = vw[j][2] = vw[j][3] = 0u;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;  // high or low bf16 of each word
+      uint4 b4;
+      b4.x = __builtin_amdgcn_perm(vw[1][i >> 1], vw[0][i >> 1], sel);
+      b4.y = __builtin_amdgcn_perm(vw[3][i >> 1], vw[2][i >> 1], sel);
+      b4.z = __builtin_amdgcn_perm(vw[5][i >> 1], vw[4][i >> 1], sel);
+      b4.w = __builtin_amdgcn_perm(vw[7][i >> 1], vw[6][i >> 1], sel);
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8_t, b4), acc[i], 0, 0, 0);
+    }
+  }
+
+  // ---- sum of the parts and row groups, then over the waves ------------------
+  // acc[i][r] of lane (r16, sub): part sub of head r at dim 8*r16 + i plus
+  // the cluster terms of row group sub.  Two swap steps leave lane (r16, sub)
+  // heads 2*(sub >> 1) + r' (r' < 2) at dims 8*r16 + 4*(sub & 1) + i'
+  // (i' < 4), summed over the row groups.
+  float x[4][4], y[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[i][r] = swap_add16(acc[i][r], acc[i + 4][r]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 2; ++r) y[i][r] = swap_add32(x[i][r], x[i][r + 2]);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int h = 2 * (sub >> 1) + r;
+    if (h < G)
+      *reinterpret_cast<float4*>(&s_red[w][h][8 * r16 + 4 * (sub & 1)]) = make_float4(y[0][r], y[1][r], y[2][r], y[3][r]);
+  }
+  lds_barrier();
+
+  // ---- outputs: one (head, dim) per thread, waves summed in order ----------
+  for (int ei = tid; ei < G * kD; ei += 512) {
+    const int h = ei / kD, dim = ei - h * kD;
+    float a = 0.f, L = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < W; ww += 2) a += s_red[ww][h][dim] + s_red[ww + 1][h][dim];
+#pragma unroll
+    for (int ww = 0; ww < W; ww += 4) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&s_l[h][ww]);
+      L += (l4.x + l4.y) + (l4.z + l4.w);
+      if constexpr (PROXY) {
+        const float4 p4 = *reinterpret_cast<const float4*>(&s_lp[h][ww]);
+        L += (p4.x + p4.y) + (p4.z + p4.w);
+      }
+    }
+    // (hardware reciprocal and logarithm, ~1 ulp)
+    p.out[(qrow0 + h) * kD + dim] = (L > 0.f) ? a * __builtin_amdgcn_rcpf(L) : 0.f;
+    if (dim == 0 && p.lse) p.lse[qrow0 + h] = (L > 0.f) ? (s_M[h] + __builtin_amdgcn_logf(L)) * kLn2 : kNegInf;
+  }
+}
+
 // Final value of one (head, dim) output from the merged sums.
 //   M, L, a : the exact part (log2-unit max, denominator, numerator)
 //   prior   : c (log2 bias shift), mP (log2 maxP), zP (sumP), oe (O_est[dim]),
@@ -2052,9 +2593,25 @@ static hipError_t launch_mfma_nt(const AttnParams& p, int nt, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int G, bool PROXY>
+static hipError_t launch_vt_nt(const AttnParams& p, int nt, hipStream_t st) {
+  const dim3 grid(p.B * p.Hkv), block(512);
+  switch (nt) {
+    case 1: hipLaunchKernelGGL((sparse_unit_vt_kernel<G, PROXY, 1>), grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL((sparse_unit_vt_kernel<G, PROXY, 2>), grid, block, 0, st, p); break;
+    case 3: hipLaunchKernelGGL((sparse_unit_vt_kernel<G, PROXY, 3>), grid, block, 0, st, p); break;
+    case 4: hipLaunchKernelGGL((sparse_unit_vt_kernel<G, PROXY, 4>), grid, block, 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// bf16: value rows in registers for G <= 4 (three weight parts fit one
+// operand's 16 rows), value tiles in LDS for G = 8
 template <int G>
 static hipError_t launch_mfma_g(const AttnParams& p, bool proxy, int nt, hipStream_t st) {
-  return proxy ? launch_mfma_nt<G, true>(p, nt, st) : launch_mfma_nt<G, false>(p, nt, st);
+  if constexpr (G <= 4) return proxy ? launch_vt_nt<G, true>(p, nt, st) : launch_vt_nt<G, false>(p, nt, st);
+  else return proxy ? launch_mfma_nt<G, true>(p, nt, st) : launch_mfma_nt<G, false>(p, nt, st);
 }
 
 hipError_t launch_sparse_unit(const AttnParams& p, int dtype, int G, bool proxy, int ns, hipStream_t st) {

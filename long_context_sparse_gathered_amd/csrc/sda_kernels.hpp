@@ -140,6 +140,21 @@ inline void proxy_build_shape(int units, int n, int C, int* chunks, int* rows) {
   *chunks = (n + r - 1) / r;
 }
 
+// Row-gather measurement kernel (sda_gather.hip).
+struct GatherParams {
+  const void* K;
+  const void* V;
+  const int32_t* idx;        // [units, m]
+  const void* state;         // [units, state_bytes] or null
+  int64_t state_bytes;
+  int64_t sb, sh, sn;        // element strides
+  int32_t esize, row_bytes;  // element size, row stride in bytes
+  int32_t Hkv, n, m, parts;
+  uint32_t* checksum;        // [units * parts * waves]
+};
+int gather_rows_per_group(int m, int waves, int parts);
+hipError_t launch_gather_rows(const GatherParams& p, int waves, int units, hipStream_t st);
+
 // Largest slot count the one-workgroup-per-unit kernel is built for.
 constexpr int kUnitWaves = 8;
 // Tiles of 16 list entries per wave in the bf16 unit kernel (LDS-bound).

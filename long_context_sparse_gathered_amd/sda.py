@@ -29,7 +29,7 @@ FLAG_IDX_RANGE, FLAG_IDX_ORDER, FLAG_SAMPLE_CAP, FLAG_CLUSTER, FLAG_LEN = 1, 2, 
 
 EXPORTED = ["sda_workspace_bytes", "sda_build_tail_proxies", "sda_build_prior", "sda_sparse_decode_attn",
             "sda_dense_decode_attn", "sda_build_qgs_codes", "sda_select_qgs", "sda_build_qgc_clusters",
-            "sda_status_str", "sda_version"]
+            "sda_gather_rows", "sda_status_str", "sda_version"]
 
 
 class SdaError(RuntimeError):
@@ -94,6 +94,8 @@ def lib() -> ctypes.CDLL:
     L.sda_sparse_decode_attn.argtypes = [D, _vp, _vp, _vp, _vp, _vp, _vp, i32, T, _vp, _vp, _vp, _vp, sz, _vp]
     L.sda_dense_decode_attn.restype = i32
     L.sda_dense_decode_attn.argtypes = [D, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp]
+    L.sda_gather_rows.restype = i32
+    L.sda_gather_rows.argtypes = [D, _vp, _vp, _vp, i32, _vp, ctypes.c_int64, i32, i32, _vp, _vp]
     L.sda_status_str.restype = ctypes.c_char_p
     L.sda_status_str.argtypes = [i32]
     L.sda_version.restype = ctypes.c_char_p
@@ -518,6 +520,38 @@ def build_qgc_clusters(K: torch.Tensor, V: torch.Tensor, C: int, T: int = 10,
                                       _ptr(ws), wsb, _stream(stream))
     _check(rc, "sda_build_qgc_clusters")
     return cid
+
+
+def gather_rows(K: torch.Tensor, V: torch.Tensor, idx: torch.Tensor, waves: int = 8, parts: int = 1,
+                state: Optional[torch.Tensor] = None, checksum: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """Measurement aid: read the listed K/V rows (and each unit's slice of
+    `state`, a [B*Hkv, ...] tensor) in the given launch shape; returns the
+    per-wave XOR checksums [B*Hkv*parts*waves] (uint32 bits in an int32
+    tensor)."""
+    _check_kv(K, V)
+    B, Hkv, n, d = K.shape
+    dev = K.device
+    _need(idx, "idx", dtype=torch.int32, device=dev)
+    if idx.dim() != 3 or tuple(idx.shape[:2]) != (B, Hkv):
+        raise ValueError(f"idx must be [B={B}, Hkv={Hkv}, m], got {tuple(idx.shape)}")
+    state_bytes = 0
+    if state is not None:
+        _need(state, "state", device=dev)
+        if state.shape[0] != B * Hkv:
+            raise ValueError("state must be [B*Hkv, ...]")
+        state_bytes = state[0].numel() * state.element_size()
+    words = B * Hkv * int(parts) * int(waves)
+    if checksum is None:
+        checksum = torch.zeros(words, dtype=torch.int32, device=dev)
+    else:
+        _need(checksum, "checksum", dtype=torch.int32, shape=(words,), device=dev)
+    _on_gpu(K, "K")
+    dims = make_dims(K, Hkv)
+    rc = lib().sda_gather_rows(ctypes.byref(dims), _ptr(K), _ptr(V), _ptr(idx), int(idx.shape[-1]), _ptr(state),
+                               int(state_bytes), int(waves), int(parts), _ptr(checksum), _stream(stream))
+    _check(rc, "sda_gather_rows")
+    return checksum
 
 
 def default_scale(d: int) -> float:
