@@ -214,6 +214,25 @@ sda_status sda_sparse_decode_attn(const sda_dims* dims, const void* q,
                                   int32_t* dev_flags, void* ws, size_t ws_bytes,
                                   void* stream);
 
+/* The same decode step for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument; the scratch it needs comes from one array of
+ * SDA_NOALLOC_SCRATCH_BYTES that the library keeps per GPU until the process
+ * ends.  Calls that need more than that (sda_workspace_bytes with
+ * SDA_OP_SPARSE) return SDA_EWORKSPACE before any launch.  The call itself
+ * allocates nothing.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap in time on one GPU (other streams, other threads) race: order
+ * them on one stream.  The array keeps the last call's contents; the decode
+ * initialises what it reads.  A failure to look up the array's device
+ * address returns SDA_EHIP. */
+#define SDA_NOALLOC_SCRATCH_BYTES (64u << 20)
+sda_status sda_sparse_decode_attn_noalloc(const sda_dims* dims, const void* q,
+                                          const void* K, const void* V,
+                                          const int32_t* idx, const int32_t* idx_len,
+                                          const float* logw, int32_t m,
+                                          const sda_tail* tail, float* out, float* lse,
+                                          int32_t* dev_flags, void* stream);
+
 /* Dense decode attention over all n rows (the speedup reference):
  * out = softmax(scale * q K^T) V per query head, lse = ln denominator. */
 sda_status sda_dense_decode_attn(const sda_dims* dims, const void* q,

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include <hip/hip_runtime.h>
 
@@ -364,10 +365,13 @@ SDA_EXPORT sda_status sda_dense_decode_attn(const sda_dims* dims, const void* q,
   return hip_status(e);
 }
 
-SDA_EXPORT sda_status sda_sparse_decode_attn(const sda_dims* dims, const void* q, const void* K, const void* V,
-                                             const int32_t* idx, const int32_t* idx_len, const float* logw,
-                                             int32_t m, const sda_tail* tail, float* out, float* lse,
-                                             int32_t* dev_flags, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+// The decode step behind both decode entry points: ws/ws_bytes is the
+// caller's workspace or the library's static scratch.
+sda_status sparse_decode(const sda_dims* dims, const void* q, const void* K, const void* V, const int32_t* idx,
+                         const int32_t* idx_len, const float* logw, int32_t m, const sda_tail* tail, float* out,
+                         float* lse, int32_t* dev_flags, void* ws, size_t ws_bytes, void* stream) {
   Resolved r;
   sda_status st = resolve(dims, &r);
   if (st != SDA_OK) return st;
@@ -461,6 +465,61 @@ SDA_EXPORT sda_status sda_sparse_decode_attn(const sda_dims* dims, const void* q
   hipError_t e = launch_stream_any(p, r, mode, hs);
   if (e == hipSuccess && p.splits > 1) e = launch_merge(p, r.G, mode, hs);
   return hip_status(e);
+}
+
+// Scratch for the entry point that allocates nothing: one array per GPU the
+// library runs on, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is a stand-in, not a device
+// address); it uses the address hipGetSymbolAddress returns for the current
+// device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[SDA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+sda_status scratch_for_current_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SDA_EHIP;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SDA_EHIP;
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);  // the same value from any racing thread
+  }
+  *out = ptr;
+  return SDA_OK;
+}
+
+}  // namespace
+
+SDA_EXPORT sda_status sda_sparse_decode_attn(const sda_dims* dims, const void* q, const void* K, const void* V,
+                                             const int32_t* idx, const int32_t* idx_len, const float* logw,
+                                             int32_t m, const sda_tail* tail, float* out, float* lse,
+                                             int32_t* dev_flags, void* ws, size_t ws_bytes, void* stream) {
+  return sparse_decode(dims, q, K, V, idx, idx_len, logw, m, tail, out, lse, dev_flags, ws, ws_bytes, stream);
+}
+
+SDA_EXPORT sda_status sda_sparse_decode_attn_noalloc(const sda_dims* dims, const void* q, const void* K,
+                                                     const void* V, const int32_t* idx, const int32_t* idx_len,
+                                                     const float* logw, int32_t m, const sda_tail* tail, float* out,
+                                                     float* lse, int32_t* dev_flags, void* stream) {
+  // the size check first, so that a call too large for the scratch fails
+  // before anything touches the device
+  Resolved r;
+  sda_status st = resolve(dims, &r);
+  if (st != SDA_OK) return st;
+  const int kind = tail ? tail->kind : SDA_TAIL_NONE;
+  if (kind < SDA_TAIL_NONE || kind > SDA_TAIL_SAMPLED || m < 0) return SDA_EINVAL;
+  SparsePlan pl;
+  st = plan_sparse(r, kind, m, &pl);
+  if (st != SDA_OK) return st;
+  if (pl.ws > (size_t)SDA_NOALLOC_SCRATCH_BYTES) return SDA_EWORKSPACE;
+  void* ws = nullptr;
+  if (pl.ws > 0) {
+    st = scratch_for_current_device(&ws);
+    if (st != SDA_OK) return st;
+  }
+  return sparse_decode(dims, q, K, V, idx, idx_len, logw, m, tail, out, lse, dev_flags, ws,
+                       pl.ws > 0 ? (size_t)SDA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 SDA_EXPORT sda_status sda_build_qgs_codes(const sda_dims* dims, const void* K, const float* U, int8_t* codes,

@@ -29,7 +29,7 @@ FLAG_IDX_RANGE, FLAG_IDX_ORDER, FLAG_SAMPLE_CAP, FLAG_CLUSTER, FLAG_LEN = 1, 2, 
 
 EXPORTED = ["sda_workspace_bytes", "sda_build_tail_proxies", "sda_build_prior", "sda_sparse_decode_attn",
             "sda_dense_decode_attn", "sda_build_qgs_codes", "sda_select_qgs", "sda_build_qgc_clusters",
-            "sda_gather_rows", "sda_status_str", "sda_version"]
+            "sda_sparse_decode_attn_noalloc", "sda_gather_rows", "sda_status_str", "sda_version"]
 
 
 class SdaError(RuntimeError):
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
     L.sda_build_prior.argtypes = [D, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp]
     L.sda_sparse_decode_attn.restype = i32
     L.sda_sparse_decode_attn.argtypes = [D, _vp, _vp, _vp, _vp, _vp, _vp, i32, T, _vp, _vp, _vp, _vp, sz, _vp]
+    L.sda_sparse_decode_attn_noalloc.restype = i32
+    L.sda_sparse_decode_attn_noalloc.argtypes = [D, _vp, _vp, _vp, _vp, _vp, _vp, i32, T, _vp, _vp, _vp, _vp]
     L.sda_dense_decode_attn.restype = i32
     L.sda_dense_decode_attn.argtypes = [D, _vp, _vp, _vp, _vp, _vp, _vp, sz, _vp]
     L.sda_gather_rows.restype = i32
@@ -374,16 +376,8 @@ def dense_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, scale: 
     return out, lse
 
 
-def sparse_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: Optional[torch.Tensor],
-                       idx_len: Optional[torch.Tensor] = None, logw: Optional[torch.Tensor] = None,
-                       tail=None, idx_cluster: Optional[torch.Tensor] = None,
-                       cluster_id: Optional[torch.Tensor] = None, lam: float = 1.0,
-                       scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-                       lse: Optional[torch.Tensor] = None, flags: Optional[torch.Tensor] = None,
-                       ws: Optional[torch.Tensor] = None, m: Optional[int] = None, stream=None):
-    """One decode step; returns (out [B,Hq,d] fp32, lse [B,Hq] fp32).
-    idx is [B, Hkv, m] (m = idx.shape[-1]; `m`, if given, must agree), or None
-    for an empty list."""
+def _decode_args(q, K, V, idx, idx_len, logw, tail, idx_cluster, cluster_id, lam, out, lse, flags, m):
+    """Checks shared by the decode entry points; returns (m, tail block, keep-alive list, out, lse)."""
     _check_kv(K, V)
     Hq = _check_q(q, K)
     B, Hkv, n, d = K.shape
@@ -402,24 +396,67 @@ def sparse_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: O
     _opt(idx_len, "idx_len", dtype=torch.int32, shape=(B, Hkv), device=dev)
     _opt(logw, "logw", dtype=torch.float32, shape=(B, Hkv, m), device=dev)
     _opt(flags, "flags", dtype=torch.int32, shape=(B, Hkv), device=dev)
-    if isinstance(tail, SampledTail):
-        if tail.b is None:
-            tail.b = torch.empty((B, Hkv), dtype=torch.int32, device=dev)
-        if tail.bstar is None:
-            tail.bstar = torch.empty((B, Hkv), dtype=torch.float64, device=dev)
-        if tail.samples is None and tail.b_cap > 0:
-            tail.samples = torch.full((B, Hkv, tail.b_cap), -1, dtype=torch.int32, device=dev)
     keep = []
     t = _tail_struct(tail, idx_cluster, cluster_id, lam, keep, B, Hq, Hkv, n, d, m, dev)
     out, lse = _outputs(out, lse, B, Hq, d, dev)
-    _check_ws(ws, dev)
+    return m, t, keep, out, lse
+
+
+def sparse_decode_attn(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: Optional[torch.Tensor],
+                       idx_len: Optional[torch.Tensor] = None, logw: Optional[torch.Tensor] = None,
+                       tail=None, idx_cluster: Optional[torch.Tensor] = None,
+                       cluster_id: Optional[torch.Tensor] = None, lam: float = 1.0,
+                       scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                       lse: Optional[torch.Tensor] = None, flags: Optional[torch.Tensor] = None,
+                       ws: Optional[torch.Tensor] = None, m: Optional[int] = None, stream=None):
+    """One decode step; returns (out [B,Hq,d] fp32, lse [B,Hq] fp32).
+    idx is [B, Hkv, m] (m = idx.shape[-1]; `m`, if given, must agree), or None
+    for an empty list."""
+    if isinstance(tail, SampledTail):
+        B, Hkv = K.shape[0], K.shape[1]
+        if tail.b is None:
+            tail.b = torch.empty((B, Hkv), dtype=torch.int32, device=K.device)
+        if tail.bstar is None:
+            tail.bstar = torch.empty((B, Hkv), dtype=torch.float64, device=K.device)
+        if tail.samples is None and tail.b_cap > 0:
+            tail.samples = torch.full((B, Hkv, tail.b_cap), -1, dtype=torch.int32, device=K.device)
+    m, t, keep, out, lse = _decode_args(q, K, V, idx, idx_len, logw, tail, idx_cluster, cluster_id, lam, out, lse,
+                                        flags, m)
+    _check_ws(ws, K.device)
     _on_gpu(K, "K")
-    dims = make_dims(K, Hq, scale)
-    ws, wsb = _workspace(workspace_bytes(dims, OP_SPARSE, t.kind, m, getattr(tail, "C", 0)), dev, ws)
+    dims = make_dims(K, q.shape[1], scale)
+    ws, wsb = _workspace(workspace_bytes(dims, OP_SPARSE, t.kind, m, getattr(tail, "C", 0)), K.device, ws)
     rc = lib().sda_sparse_decode_attn(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V), _ptr(idx),
                                       _ptr(idx_len), _ptr(logw), int(m), ctypes.byref(t),
                                       _ptr(out), _ptr(lse), _ptr(flags), _ptr(ws), wsb, _stream(stream))
     _check(rc, "sda_sparse_decode_attn")
+    return out, lse
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def sparse_decode_attn_noalloc(q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, idx: Optional[torch.Tensor],
+                               out: torch.Tensor, lse: torch.Tensor, idx_len: Optional[torch.Tensor] = None,
+                               logw: Optional[torch.Tensor] = None, tail=None,
+                               idx_cluster: Optional[torch.Tensor] = None, cluster_id: Optional[torch.Tensor] = None,
+                               lam: float = 1.0, scale: Optional[float] = None, flags: Optional[torch.Tensor] = None,
+                               m: Optional[int] = None, stream=None):
+    """The decode step through the entry point that allocates nothing (its
+    scratch is the library's per-GPU static array).  Every output, including
+    a sampled tail's b and bstar, must be given; nothing is allocated here."""
+    if out is None or lse is None:
+        raise ValueError("out and lse must be given (this entry point allocates nothing)")
+    if isinstance(tail, SampledTail) and (tail.b is None or tail.bstar is None):
+        raise ValueError("a sampled tail's b and bstar must be given (this entry point allocates nothing)")
+    m, t, keep, out, lse = _decode_args(q, K, V, idx, idx_len, logw, tail, idx_cluster, cluster_id, lam, out, lse,
+                                        flags, m)
+    _on_gpu(K, "K")
+    dims = make_dims(K, q.shape[1], scale)
+    rc = lib().sda_sparse_decode_attn_noalloc(ctypes.byref(dims), _ptr(q), _ptr(K), _ptr(V), _ptr(idx),
+                                              _ptr(idx_len), _ptr(logw), int(m), ctypes.byref(t), _ptr(out),
+                                              _ptr(lse), _ptr(flags), _stream(stream))
+    _check(rc, "sda_sparse_decode_attn_noalloc")
     return out, lse
 
 

@@ -206,3 +206,17 @@ def test_clustering_validation(L):
     assert call(cid=None) == sda.SDA_EINVAL
     assert call(K=MISALIGNED) == sda.SDA_EINVAL
     assert call(ws_bytes=need - 1) == sda.SDA_EWORKSPACE
+
+
+def test_noalloc_entry_rejects_calls_beyond_its_scratch(L):
+    """The allocation-free decode refuses, before touching the device, a call
+    whose scratch would exceed the static array (sampled tail at batch 64,
+    128K rows needs far more than 64 MiB of draw records)."""
+    dims = sda.Dims(64, 256, 32, 131072, 128, sda.SDA_BF16, 0, 0, 0, 0.0)
+    need = L.sda_workspace_bytes(ctypes.byref(dims), sda.OP_SPARSE, sda.TAIL_SAMPLED, 1000, 0)
+    assert need > sda.NOALLOC_SCRATCH_BYTES
+    t = sda.Tail()
+    t.kind, t.eps, t.z, t.b0 = sda.TAIL_SAMPLED, 0.05, 1.96, 64
+    rc = L.sda_sparse_decode_attn_noalloc(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE2, None, None, 1000,
+                                          ctypes.byref(t), FAKE, None, None, None)
+    assert rc == sda.SDA_EWORKSPACE
