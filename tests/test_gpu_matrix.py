@@ -200,3 +200,76 @@ def test_proxy_without_listed_rows(orc, G):
     ref, ref_lse = orc.sparse_proxy_def(c.q, c.K, c.V, idx, c.cid, w.C)
     assert rel_err(out, ref) <= TOL
     assert lse_err(lse, ref_lse) <= LSE_TOL
+
+
+def test_dense_full_size_b32_n32k(orc):
+    """Dense decode in the launch bench.py times (batch 32, 32K: 256 units,
+    8 splits of 4096 rows each plus the merge), checked on 4 sampled units
+    against the oracle's textbook softmax."""
+    w = synth.WORKLOADS["proxy_bf16_b32_n32k"]
+    c = synth.make_case(w)
+    d = case_to_dev(c)
+    out, lse = sda.dense_decode_attn(d["q"], d["K"], d["V"])
+    _sync()
+    got, got_lse = out.cpu().double().numpy(), lse.cpu().double().numpy()
+    for s, g in _sample_units(w, 4, 7):
+        uc = synth.unit_case(w, s, g)
+        ref, ref_lse = orc.dense(uc.q, uc.K, uc.V)
+        rows = slice(g * w.G, (g + 1) * w.G)
+        assert rel_err(got[s, rows], ref[0]) <= TOL, (s, g)
+        assert np.abs(got_lse[s, rows] - ref_lse[0]).max() <= LSE_TOL, (s, g)
+
+
+def _mostly_read_clusters(G, seed):
+    """Units where several clusters are listed but for two members each, and
+    those unread members hold logits near the unit's largest (held by a listed
+    row, so that the proxy weight e^{mu_b - M} is no round number) while the
+    listed members sit low; within such a cluster the values are nearly
+    equal, so the cluster's value sum and its listed members' share cancel to
+    1/64 of their size (OpenAttention, method stage 04: the proxy folds only a
+    cluster's unread tokens)."""
+    rng = np.random.default_rng(seed)
+    B, Hkv, n, d, C, size, m = 2, 8, 4096, 128, 32, 128, 328
+    Hq = G * Hkv
+    q = synth.round_bf16_bits(rng.standard_normal((B, Hq, d)).astype(np.float32))
+    qf = synth.bf16_bits_to_f32(q).astype(np.float64)
+    K = (0.5 * rng.standard_normal((B, Hkv, n, d))).astype(np.float32)
+    V = rng.standard_normal((B, Hkv, n, d)).astype(np.float32)
+    cid = np.broadcast_to((np.arange(n) // size).astype(np.int32), (B, Hkv, n)).copy()
+    idx = np.empty((B, Hkv, m), np.int32)
+    for s in range(B):
+        for g in range(Hkv):
+            qb = qf[s, g * G:(g + 1) * G].mean(axis=0)
+            aligned = np.sqrt(d) * qb / (qb @ qb)   # key of scaled logit 1 against the mean query
+            listed = set(range(4)) | set(range(n - 64, n))
+            K[s, g, n - 1] = (14.5 * aligned).astype(np.float32)   # a listed row holds the unit maximum
+            for b in rng.choice(np.arange(1, C - 1), size=2, replace=False):
+                members = np.arange(b * size, (b + 1) * size)
+                unread = rng.choice(members, size=2, replace=False)
+                # two different keys, so the unread mean's weight is no bf16 number
+                K[s, g, unread[0]] = (14.0 * aligned).astype(np.float32)
+                K[s, g, unread[1]] = (13.6 * aligned + 0.3 * rng.standard_normal(d)).astype(np.float32)
+                V[s, g, members] = (3.0 * rng.standard_normal(d) + 0.01 * rng.standard_normal((size, d)))
+                listed |= set(members.tolist()) - set(unread.tolist())
+            rest = np.setdiff1d(np.arange(n), np.fromiter(listed, int))
+            listed |= set(rng.choice(rest, size=m - len(listed), replace=False).tolist())
+            idx[s, g] = np.sort(np.fromiter(listed, np.int32))
+    return q, synth.round_bf16_bits(K), synth.round_bf16_bits(V), idx, cid, C
+
+
+@pytest.mark.parametrize("G", [4, 8, 2])
+def test_proxy_mostly_read_clusters(orc, G):
+    """The cancellation case at the headline kernel's shape (m = 328, three
+    tiles of 16 keys per wave): the listed members' correction and the
+    cluster's value sum must cancel to the unread members' share within the
+    bf16 tolerance; the margin is printed."""
+    q, K, V, idx, cid, C = _mostly_read_clusters(G, 11 + G)
+    st = sda.build_tail_proxies(to_dev(K), to_dev(V), to_dev(cid), C)
+    icl = np.take_along_axis(cid, idx.astype(np.int64), axis=2).astype(np.int32)
+    out, lse = sda.sparse_decode_attn(to_dev(q), to_dev(K), to_dev(V), to_dev(idx), tail=st, idx_cluster=to_dev(icl))
+    _sync()
+    ref, ref_lse = orc.sparse_proxy_def(q, K, V, idx, cid, C)
+    err = rel_err(out, ref)
+    print(f"mostly-read clusters, G={G}: max rel err {err:.3e} (tolerance {TOL:.0e}, margin {TOL / max(err, 1e-30):.0f}x)")
+    assert err <= TOL
+    assert lse_err(lse, ref_lse) <= LSE_TOL
