@@ -253,18 +253,21 @@ const char* sda_version(void);
  * sda_select_qgs.  Per unit:
  *   - V [B,Hkv,d,16] fp32: the projection basis (orthonormal columns; the
  *     leading 16 columns of the selector's basis);
- *   - fixed-point coordinates zq_j = rint(4096 * V^T k_j), the projection
- *     summed over d in order in fp64 (exact products), clamped to
- *     |zq| <= 2^23 - 1 (a clamp sets SDA_FLAG_CLUSTER);
- *   - k-means with C centroids on the same integer grid: start at the points
- *     of rows floor((2k + 1) n / (2C)); T passes of "each row to its nearest
- *     centroid (squared distance, ties to the lower k), each centroid to its
- *     rows' mean rounded half to even (an empty one stays)";
+ *   - coordinates z_j = V^T k_j, the projection summed over d in order in
+ *     fp64 (exact products), clamped to |z| <= 2048 (a clamp sets
+ *     SDA_FLAG_CLUSTER);
+ *   - Lloyd's k-means with C centroids: start at the points of rows
+ *     floor((2k + 1) n / (2C)); T passes of "each row to its nearest
+ *     centroid (squared distance, its 16 terms added in coordinate order in
+ *     fp64, ties to the lower k), each centroid to its rows' mean (an empty
+ *     one stays)"; the mean is formed from an exact integer sum of the
+ *     coordinates rounded to 2^-32, so it is within 2^-33 of the exact mean
+ *     and the same in any order of the rows;
  *   - cluster_id [B,Hkv,n] int32 = the centroid of each row after pass T.
- * Distances and sums are exact integers, so the result does not depend on
- * the order of the arithmetic.  C in [1, 64] (else SDA_EUNSUPPORTED),
- * T in [1, 1000] (else SDA_EINVAL); K and V 16-byte aligned.  Workspace:
- * SDA_OP_BUILD_QGC with this C (64 B per row of fixed-point coordinates). */
+ * The result is reproducible bit for bit.  C in [1, 64] (else
+ * SDA_EUNSUPPORTED), T in [1, 1000] (else SDA_EINVAL), n <= 2^20 (else
+ * SDA_EUNSUPPORTED); K and V 16-byte aligned.  Workspace: SDA_OP_BUILD_QGC
+ * with this C (128 B per row of coordinates). */
 sda_status sda_build_qgc_clusters(const sda_dims* dims, const void* K, const float* V, int32_t C,
                                   int32_t T, int32_t* cluster_id, int32_t* dev_flags, void* ws,
                                   size_t ws_bytes, void* stream);

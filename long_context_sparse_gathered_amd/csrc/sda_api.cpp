@@ -207,14 +207,14 @@ QgsSelectWs qgs_select_ws(const Resolved& r, int C) {
 }
 
 struct QgcWs {
-  size_t zq, cent, sums, cnt, total;
+  size_t z, cent, sums, cnt, total;
 };
 
 QgcWs qgc_ws(const Resolved& r, int C) {
   const size_t units = (size_t)r.B * r.Hkv;
   QgcWs w;
-  w.zq = 0;
-  w.cent = align256(units * r.n * kQgcRank * sizeof(int32_t));
+  w.z = 0;
+  w.cent = align256(units * r.n * kQgcRank * sizeof(double));
   w.sums = w.cent + align256(units * C * kQgcRank * sizeof(double));
   w.cnt = w.sums + align256(units * C * kQgcRank * sizeof(uint64_t));
   w.total = w.cnt + align256(units * C * sizeof(int32_t));
@@ -609,6 +609,7 @@ SDA_EXPORT sda_status sda_build_qgc_clusters(const sda_dims* dims, const void* K
   if (!aligned16(K) || !aligned16(V)) return SDA_EINVAL;
   if (C < 1 || C > kCmax) return SDA_EUNSUPPORTED;
   if (T < 1 || T > 1000) return SDA_EINVAL;
+  if (r.n > kQgcMaxN) return SDA_EUNSUPPORTED;
   const QgcWs w = qgc_ws(r, C);
   if (!ws || ws_bytes < w.total) return SDA_EWORKSPACE;
   char* base = reinterpret_cast<char*>(ws);
@@ -622,7 +623,7 @@ SDA_EXPORT sda_status sda_build_qgc_clusters(const sda_dims* dims, const void* K
   p.Hkv = r.Hkv;
   p.n = r.n;
   p.C = C;
-  p.zq = reinterpret_cast<int32_t*>(base + w.zq);
+  p.z = reinterpret_cast<double*>(base + w.z);
   p.cent = reinterpret_cast<double*>(base + w.cent);
   p.sums = reinterpret_cast<unsigned long long*>(base + w.sums);
   p.cnt = reinterpret_cast<int32_t*>(base + w.cnt);

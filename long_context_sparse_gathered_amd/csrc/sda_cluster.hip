@@ -3,13 +3,13 @@
 // method list and the settings list: keys projected on the top 16 query
 // eigenvectors are clustered with k-means, C = 64).
 //
-// Coordinates are fixed point: zq = rint(4096 * V^T k), the projection summed
-// over d in order in fp64 (exact products), clamped to |zq| < 2^23.  Centroids
-// live on the same integer grid (each is its rows' mean rounded half to
-// even), so every squared distance is an integer below 2^52 -- exact in fp64
-// whatever the order of the terms -- and the centroid sums are exact 64-bit
-// integer sums (atomics in any order give the same bits).  The k-means
-// trajectory is therefore reproducible bit for bit.
+// Coordinates are fp64: z = V^T k, the projection summed over d in order
+// (exact products), clamped to |z| <= 2048.  A squared distance adds its 16
+// terms in coordinate order with no fused multiply-add, so it is the same
+// fp64 number wherever it is computed.  A centroid is its rows' mean, formed
+// from an exact 64-bit integer sum of the coordinates rounded to 2^-32
+// (atomics in any order give the same bits), within 2^-33 of the plain mean.
+// The k-means trajectory is therefore reproducible bit for bit.
 #include <math.h>
 
 #include "sda_device.hpp"
@@ -72,17 +72,19 @@ __global__ __launch_bounds__(256) void qgc_project_kernel(const QgcParams p) {
   for (int r = 0; r < 4; ++r) {
     const int j = row0 + 4 * rg + r;
     if (j >= p.n) break;
-    int zi[4];
+    double zc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      double x = rint(acc[r][i] * kQgcScale);
-      if (fabs(x) > (double)kQgcMax) {
-        x = x > 0.0 ? (double)kQgcMax : -(double)kQgcMax;
+      double x = acc[r][i];
+      if (fabs(x) > kQgcZMax) {
+        x = x > 0.0 ? kQgcZMax : -kQgcZMax;
         bad = true;
       }
-      zi[i] = (int)x;
+      zc[i] = x;
     }
-    *reinterpret_cast<int4*>(p.zq + ((int64_t)u * p.n + j) * kQgcRank + 4 * cg) = make_int4(zi[0], zi[1], zi[2], zi[3]);
+    double* dst = p.z + ((int64_t)u * p.n + j) * kQgcRank + 4 * cg;
+    *reinterpret_cast<double2*>(dst) = make_double2(zc[0], zc[1]);
+    *reinterpret_cast<double2*>(dst + 2) = make_double2(zc[2], zc[3]);
   }
   if (bad) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
 }
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(256) void qgc_init_kernel(const QgcParams p) {
   for (int t = threadIdx.x; t < C * kQgcRank; t += 256) {
     const int k = t / kQgcRank, i = t - k * kQgcRank;
     const int row = (int)(((int64_t)(2 * k + 1) * p.n) / (2 * C));
-    p.cent[(int64_t)u * C * kQgcRank + t] = (double)p.zq[((int64_t)u * p.n + row) * kQgcRank + i];
+    p.cent[(int64_t)u * C * kQgcRank + t] = p.z[((int64_t)u * p.n + row) * kQgcRank + i];
     p.sums[(int64_t)u * C * kQgcRank + t] = 0ull;
   }
   for (int k = threadIdx.x; k < C; k += 256) p.cnt[(int64_t)u * C + k] = 0;
@@ -104,6 +106,7 @@ __global__ __launch_bounds__(256) void qgc_init_kernel(const QgcParams p) {
 // k), its coordinates added to that centroid's sums.  Two rows per thread
 // share each centroid read.
 __global__ __launch_bounds__(256) void qgc_assign_kernel(const QgcParams p) {
+#pragma clang fp contract(off)  // distances: rounded products and sums, as in a plain loop
   __shared__ double s_c[kCmax * kQgcRank];
   __shared__ unsigned long long s_sum[kCmax * kQgcRank];
   __shared__ int s_cnt[kCmax];
@@ -120,23 +123,18 @@ __global__ __launch_bounds__(256) void qgc_assign_kernel(const QgcParams p) {
 
   constexpr int RW = 2;
   int jr[RW];
-  int zi[RW][kQgcRank];
   double z[RW][kQgcRank];
 #pragma unroll
   for (int r = 0; r < RW; ++r) {
     jr[r] = ch * kQgcAssignRows + r * 256 + tid;
     const int j = min(jr[r], p.n - 1);
-    const int4* src = reinterpret_cast<const int4*>(p.zq + ((int64_t)u * p.n + j) * kQgcRank);
+    const double2* src = reinterpret_cast<const double2*>(p.z + ((int64_t)u * p.n + j) * kQgcRank);
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int4 v = src[q4];
-      zi[r][4 * q4] = v.x;
-      zi[r][4 * q4 + 1] = v.y;
-      zi[r][4 * q4 + 2] = v.z;
-      zi[r][4 * q4 + 3] = v.w;
+    for (int q2 = 0; q2 < kQgcRank / 2; ++q2) {
+      const double2 v = src[q2];
+      z[r][2 * q2] = v.x;
+      z[r][2 * q2 + 1] = v.y;
     }
-#pragma unroll
-    for (int i = 0; i < kQgcRank; ++i) z[r][i] = (double)zi[r][i];
   }
   double best[RW];
   int bk[RW];
@@ -155,7 +153,7 @@ __global__ __launch_bounds__(256) void qgc_assign_kernel(const QgcParams p) {
 #pragma unroll
       for (int i = 0; i < kQgcRank; ++i) {
         const double diff = z[r][i] - c[i];
-        d = fma(diff, diff, d);   // integers below 2^52: exact
+        d = d + diff * diff;
       }
       if (d < best[r]) {
         best[r] = d;
@@ -169,8 +167,8 @@ __global__ __launch_bounds__(256) void qgc_assign_kernel(const QgcParams p) {
     p.cluster_id[(int64_t)u * p.n + jr[r]] = bk[r];
     atomicAdd(&s_cnt[bk[r]], 1);
 #pragma unroll
-    for (int i = 0; i < kQgcRank; ++i)
-      atomicAdd(&s_sum[bk[r] * kQgcRank + i], (unsigned long long)(long long)zi[r][i]);
+    for (int i = 0; i < kQgcRank; ++i)  // |z| * 2^32 <= 2^43: rint is exact in fp64 and in int64
+      atomicAdd(&s_sum[bk[r] * kQgcRank + i], (unsigned long long)(long long)rint(z[r][i] * kQgcSumScale));
   }
   __syncthreads();
   for (int t = tid; t < C * kQgcRank; t += 256)
@@ -179,16 +177,16 @@ __global__ __launch_bounds__(256) void qgc_assign_kernel(const QgcParams p) {
     if (s_cnt[k]) atomicAdd(&p.cnt[(int64_t)u * C + k], s_cnt[k]);
 }
 
-// Centroids = rint(sum / count) (fp64 quotient of two exact integers rounds
-// to the same integer as the exact quotient); empty centroids stay; sums and
-// counts cleared for the next pass.
+// Centroids = (sum / count) * 2^-32 in fp64 (the integer sum converted with
+// one rounding, a correctly rounded division, an exact scaling); empty
+// centroids stay; sums and counts cleared for the next pass.
 __global__ __launch_bounds__(256) void qgc_update_kernel(const QgcParams p) {
   const int u = blockIdx.x, C = p.C;
   for (int t = threadIdx.x; t < C * kQgcRank; t += 256) {
     const int k = t / kQgcRank;
     const int N = p.cnt[(int64_t)u * C + k];
     const int64_t idx = (int64_t)u * C * kQgcRank + t;
-    if (N > 0) p.cent[idx] = rint((double)(long long)p.sums[idx] / (double)N);
+    if (N > 0) p.cent[idx] = ((double)(long long)p.sums[idx] / (double)N) * (1.0 / kQgcSumScale);
     p.sums[idx] = 0ull;
   }
   __syncthreads();

@@ -31,7 +31,13 @@ list them with the reasons):
       code scale moved onto the query), one scale per KV group
       wmax = max_{h,i} |w_hi| and wq_hi = rint(127 * w_hi / wmax).  Score of
       row j: S_j = max over the group's heads of sum_i wq_hi * code_ji, an
-      exact integer (|S_j| <= 32 * 127 * 127).
+      exact integer (|S_j| <= 32 * 127 * 127).  The page codes the keys in
+      int8 and says nothing of the query; the plain reading keeps the query
+      in fp64: S_j = max_h sum_i qt_hi * (kmax_i / 127) * code_ji
+      (scores_plain, select_unit_plain).  Rounding the query too makes the
+      scores exact integers, so the GPU's ranking is bit-exact; on the
+      selector workload it moves 1-2.5% of the listed rows against the plain
+      reading (the tests measure it).
   Q5  ErrorGate weight error.  Per head h and cluster b: mean logit
       zbar = scale <q_h, mu_b>, diagonal logit variance
       s2 = scale^2 sum_d q_hd^2 nu_bd, with mu_b = sumK_b / N_b and
@@ -109,6 +115,14 @@ def scores(code, wq) -> np.ndarray:
     """Q4: S_j = max_h sum_i wq_hi code_ji as exact int64."""
     dots = np.asarray(code, np.int64) @ np.asarray(wq, np.int64).T     # [n, G]
     return dots.max(axis=1)
+
+
+def scores_plain(code, q, U, kmax) -> np.ndarray:
+    """Q4, plain reading: S_j = max_h <U^T q_h, code_j * kmax / 127> in fp64
+    (the key's coded projection against the unrounded query projection)."""
+    qt = project(q, U)                                                  # [G, r]
+    yhat = np.asarray(code, np.float64) * (np.asarray(kmax, np.float64) / float(CODE_MAX))[None, :]
+    return (yhat @ qt.T).max(axis=1)
 
 
 def cluster_stats(K, cid, C):
@@ -246,3 +260,17 @@ def select_unit(q, K, cid, C, U, n_sink, n_local, E, scale, stats=None):
     qb, margin = allocate(eps, avail, E)
     idx = select(S, cid, qb, n_sink, n_local)
     return dict(idx=idx, budget=qb, eps=eps, margin=margin, scores=S, codes=code, kmax=kmax, wq=wq, avail=avail)
+
+
+def select_unit_plain(q, K, cid, C, U, n_sink, n_local, E, scale, stats=None):
+    """The selector for one unit with the plain scores (query unrounded);
+    budgets as in select_unit."""
+    code, kmax = codes(K, U)
+    S = scores_plain(code, q, U, kmax)
+    N, S1, S2 = cluster_stats(K, cid, C) if stats is None else stats
+    eps = weight_errors(q, N, S1, S2, scale)
+    el = eligible(cid, n_sink, n_local)
+    avail = np.array([int((el & (np.asarray(cid) == b)).sum()) for b in range(C)], np.int64)
+    qb, margin = allocate(eps, avail, E)
+    idx = select(S, cid, qb, n_sink, n_local)
+    return dict(idx=idx, budget=qb, eps=eps, margin=margin, scores=S)

@@ -1,7 +1,9 @@
 """GPU parity of the query-geometry clustering ("OpenAttention" stage 01 and
 the settings list; readings G1-G4 in oracle/qgc.py): the cluster id of every
-row is bit-exact against the oracle (fixed-point coordinates and integer
-centroids make the whole k-means trajectory exact arithmetic).  Then the ids
+row is bit-exact against the oracle (fp64 coordinates, distances added in
+coordinate order with no fused multiply-add, centroid sums exact on a 2^-32
+grid: the same arithmetic on both sides), and the same as the plain k-means
+with exactly rounded means on the sampled full-size units.  Then the ids
 drive the proxy builder, the selector and the proxy decode end to end."""
 import numpy as np
 import pytest
@@ -50,14 +52,14 @@ def test_clusters_fp32_keys_and_fixed_point():
     cid = sda.build_qgc_clusters(to_dev(c.K), to_dev(V), 12, T=30)
     _sync()
     for g in range(w.Hkv):
-        zq = qgc.project_fixed(c.K[0, g], V[0, g])
-        a, _, it = qgc.kmeans(zq, 12, T=30)
+        z = qgc.project(c.K[0, g], V[0, g])
+        a, _, it = qgc.kmeans(z, 12, T=30)
         np.testing.assert_array_equal(cid[0, g].cpu().numpy(), a)
 
 
 def test_clamped_coordinates_flagged():
-    """Keys whose projection leaves the fixed-point range are clamped (as in
-    the oracle) and flagged."""
+    """Keys whose projection exceeds 2048 are clamped there (as in the
+    oracle) and flagged."""
     w = _w(B=1, Hkv=1, Hq=4, n=600, n_top=20, C=4, dtype="f32")
     c = synth.make_case(w)
     K = c.K.copy()
@@ -72,7 +74,8 @@ def test_clamped_coordinates_flagged():
 
 def test_clusters_full_size_b32_n32k():
     """The timed shape (batch 32, 32K rows, C = 64, 10 passes): 4 sampled
-    units bit-exact; every id in range."""
+    units bit-exact against the oracle, and the same as the plain k-means
+    (exactly rounded means) on 2 of them; every id in range."""
     w = _w(C=64)
     c = synth.make_case(w)
     V = _v16(c)
@@ -81,9 +84,11 @@ def test_clusters_full_size_b32_n32k():
     got = cid.cpu().numpy()
     assert got.min() >= 0 and got.max() < 64
     rng = np.random.default_rng(7)
-    for u in rng.choice(w.B * w.Hkv, size=4, replace=False):
+    for i, u in enumerate(rng.choice(w.B * w.Hkv, size=4, replace=False)):
         s, g = divmod(int(u), w.Hkv)
         np.testing.assert_array_equal(got[s, g], qgc.cluster_unit(c.K[s, g], V[s, g], 64, T=10))
+        if i < 2:
+            np.testing.assert_array_equal(got[s, g], qgc.cluster_unit_plain(c.K[s, g], V[s, g], 64, T=10))
 
 
 def test_clusters_feed_selector_and_decode(orc):

@@ -2,14 +2,15 @@
 per-cluster top-q; "OpenAttention", method stages 01-03) against the oracle
 in oracle/qgs.py.
 
-Bit-exact: the int8 codes, the fp64 coordinate maxima and every listed row,
-for units whose budget decision is not fragile.  The budgets come from fp64
-arithmetic on fp32 cluster sums (the GPU's builder) against the oracle's fp64
-sums, so a quota within MARGIN of a rounding boundary may move one row
-between clusters; such units are counted and checked for validity instead:
-the budget is spent in full, no cluster exceeds its eligible rows, the
-budgets differ from the oracle's by at most two rows in all, and every
-cluster lists exactly its top-q_b rows by the oracle's exact scores.
+Bit-exact: the int8 codes, the fp64 coordinate maxima, the budgets and every
+listed row, with the oracle's ErrorGate fed the GPU builder's own cluster
+count and fp32 sums (so both sides start from the same numbers); only a unit
+whose budget decision lies within a few fp64 roundings of a tie (margin below
+EXACT_MARGIN) is checked for validity instead.  Separately, against the
+oracle's fp64 cluster sums: units whose decision is clear by MARGIN match bit
+for bit, the others must be valid -- the budget spent in full, no cluster
+above its eligible rows, at most two rows moved between clusters, and every
+cluster listing exactly its top-q_b rows by the oracle's exact scores.
 """
 import numpy as np
 import pytest
@@ -21,7 +22,8 @@ from tests.gpu_util import dev, rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
-MARGIN = 1e-3
+MARGIN = 1e-3         # against the oracle's fp64 cluster sums
+EXACT_MARGIN = 1e-9   # against the GPU builder's sums: a few fp64 roundings
 
 
 def _sync():
@@ -50,8 +52,9 @@ def _gpu_select(c, w, E=None, n_sink=None, n_local=None, cid=None):
 
 def _check_unit(r, s, g, q, K, cid, U, w, E, n_sink, n_local):
     """Compares unit (s, g) with the oracle; returns True if its budget
-    decision was fragile (then only validity is checked)."""
-    o = qgs.select_unit(q, K, cid, w.C, U, n_sink, n_local, E, np.float32(1.0 / np.sqrt(w.d)))
+    decision was fragile against the oracle's own fp64 sums (then only
+    validity is checked there)."""
+    sc = np.float32(1.0 / np.sqrt(w.d))
     gb = r["budget"][s, g].cpu().numpy()
     L = int(r["idx_len"][s, g])
     gidx = r["idx"][s, g, :L].cpu().numpy()
@@ -62,6 +65,16 @@ def _check_unit(r, s, g, q, K, cid, U, w, E, n_sink, n_local):
     own = np.where((cid[gidx] >= 0) & (cid[gidx] < w.C), cid[gidx], -1)
     np.testing.assert_array_equal(gicl, own)
     assert L <= m and (np.diff(gidx) > 0).all()
+    # 1. the same inputs on both sides: the GPU builder's count and sums
+    st = r["st"]
+    stats = (st.count[s, g].cpu().numpy().astype(np.int64), st.sumK[s, g].cpu().double().numpy(),
+             st.sumK2[s, g].cpu().double().numpy())
+    og = qgs.select_unit(q, K, cid, w.C, U, n_sink, n_local, E, sc, stats=stats)
+    if og["margin"] >= EXACT_MARGIN:
+        np.testing.assert_array_equal(gb, og["budget"])
+        np.testing.assert_array_equal(gidx, og["idx"])
+    # 2. the oracle's own fp64 sums
+    o = qgs.select_unit(q, K, cid, w.C, U, n_sink, n_local, E, sc)
     if o["margin"] >= MARGIN:
         np.testing.assert_array_equal(gb, o["budget"])
         np.testing.assert_array_equal(gidx, o["idx"])

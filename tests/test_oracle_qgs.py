@@ -238,3 +238,84 @@ def test_select_unit_shapes_and_budget():
     mid = idx[(idx >= 4) & (idx < n - 64)]
     for b in range(C):
         assert ((cid[mid] == b).sum()) == r["budget"][b]
+
+
+def test_plain_scores_rank_like_the_logits_for_lossless_codes():
+    """Q4 plain reading: keys inside span(U) whose projections sit on the code
+    grid are coded without loss, so the plain score of a row is its largest
+    logit over the group up to one positive factor: the top-k by plain score
+    is the exact top-k by max_h <q_h, k_j> (lexsort reference, ties to the
+    lower position)."""
+    rng = np.random.default_rng(11)
+    d, r, n, G = 64, 32, 300, 4
+    U, _ = np.linalg.qr(rng.standard_normal((d, r)))
+    U = U.astype(np.float32)
+    cgrid = rng.integers(-127, 128, size=(n, r))
+    cgrid[0, :] = 127                                  # every column reaches the code maximum
+    K = (cgrid.astype(np.float64) / 127.0) @ U.astype(np.float64).T     # projections = code / 127
+    code, kmax = qgs.codes(K.astype(np.float64), U)
+    np.testing.assert_array_equal(code.astype(np.int64), cgrid)
+    q = rng.standard_normal((G, d)).astype(np.float32)
+    S = qgs.scores_plain(code, q, U, kmax)
+    logits = (K @ q.astype(np.float64).T).max(axis=1)
+    order = np.lexsort((np.arange(n), -logits))
+    top = np.sort(order[:40])
+    order_s = np.lexsort((np.arange(n), -S))
+    np.testing.assert_array_equal(np.sort(order_s[:40]), top)
+
+
+def test_plain_and_integer_scores_agree_when_the_query_weights_are_integral():
+    """When 127 * w / max|w| is already integral the integer weights are the
+    plain weights up to one factor, so both readings list the same rows."""
+    rng = np.random.default_rng(12)
+    d, r, n = 64, 32, 400
+    U, _ = np.linalg.qr(rng.standard_normal((d, r)))
+    U = U.astype(np.float32)
+    K = rng.standard_normal((n, d)).astype(np.float32)
+    code, kmax = qgs.codes(K, U)
+    # a query whose projection is chosen so that w = qt * kmax is a multiple of wmax / 127
+    target = rng.integers(-127, 128, size=(1, r)).astype(np.float64)
+    target[0, 0] = 127
+    qt = target / kmax[None, :]
+    q = (qt @ U.astype(np.float64).T).astype(np.float32)
+    wq = qgs.query_weights(q, U, kmax)
+    S_int = qgs.scores(code, wq)
+    S_pl = qgs.scores_plain(code, q, U, kmax)
+    top_int = np.lexsort((np.arange(n), -S_int))[:50]
+    top_pl = np.lexsort((np.arange(n), -S_pl))[:50]
+    # the float query is within rounding of the target, so compare the sets away from near-ties
+    gap = np.sort(S_pl)[::-1]
+    if abs(gap[49] - gap[50]) > 1e-6 * abs(gap[0]):
+        np.testing.assert_array_equal(np.sort(top_int), np.sort(top_pl))
+
+
+def test_plain_scores_invariant_to_query_scale():
+    rng = np.random.default_rng(13)
+    d, r, n = 64, 32, 200
+    U, _ = np.linalg.qr(rng.standard_normal((d, r)))
+    U = U.astype(np.float32)
+    K = rng.standard_normal((n, d)).astype(np.float32)
+    code, kmax = qgs.codes(K, U)
+    q = rng.standard_normal((2, d)).astype(np.float32)
+    a = np.lexsort((np.arange(n), -qgs.scores_plain(code, q, U, kmax)))[:30]
+    b = np.lexsort((np.arange(n), -qgs.scores_plain(code, q * np.float32(4.0), U, kmax)))[:30]
+    np.testing.assert_array_equal(a, b)
+
+
+def test_integer_query_weights_move_few_listed_rows_on_the_selector_workload():
+    """The measured effect of rounding the query weights (reading Q4) on units
+    of the selector workload (n = 8192 rows here, 260 rows picked): the rows
+    listed by the integer scores against the plain fp64 scores, same budgets.
+    The selector notes record the numbers (2-4 of 260 on full 32K units)."""
+    from long_context_sparse_gathered_amd import synth
+    w = synth.WORKLOADS["qgs_bf16_b32_n32k"].replace(n=8192)
+    sc = np.float32(1.0 / np.sqrt(w.d))
+    moved = []
+    for s, g in [(0, 0), (3, 5), (9, 1), (17, 6)]:
+        ud = synth.make_unit(w, s, g)
+        a = qgs.select_unit(ud.q, ud.K, ud.cid, w.C, ud.U, w.n_sink, w.n_local, w.n_top, sc)
+        b = qgs.select_unit_plain(ud.q, ud.K, ud.cid, w.C, ud.U, w.n_sink, w.n_local, w.n_top, sc)
+        np.testing.assert_array_equal(a["budget"], b["budget"])
+        moved.append(len(np.setdiff1d(b["idx"], a["idx"])))
+    print(f"listed rows that the integer query weights move: {moved} of {w.n_top} per unit")
+    assert max(moved) <= 0.03 * w.n_top
