@@ -114,7 +114,12 @@ typedef struct {
    * rows in b) > 0 adds one entry with key sumK_b' / n_b, value
    * sumV_b' / n_b and logit scale*<q, key> + ln n_b, where the primes
    * denote the sums without the listed rows.  The list must hold distinct
-   * positions in increasing order. */
+   * positions in increasing order.  Lists of up to 512 entries per unit
+   * (384 when 8 query heads share a KV head) run in one workgroup per unit
+   * with no workspace; longer bf16 lists are split across workgroups, each
+   * split writing per-cluster listed counts, logit sums and value sums to
+   * the workspace (sda_workspace_bytes gives the size); longer fp32 lists
+   * return SDA_EUNSUPPORTED. */
   int32_t C;                     /* clusters per unit, 1 <= C <= 64         */
   const int32_t* idx_cluster;    /* [B,Hkv,m] cluster of each listed row (as
                                     a per-cluster selector emits it), or

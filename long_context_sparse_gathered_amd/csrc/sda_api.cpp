@@ -95,7 +95,7 @@ struct SparsePlan {
   size_t ws;
 };
 
-sda_status plan_sparse(const Resolved& r, int kind, int m, SparsePlan* pl) {
+sda_status plan_sparse(const Resolved& r, int kind, int m, int C, SparsePlan* pl) {
   const int units = r.B * r.Hkv;
   pl->unit = false;
   pl->ns = 0;
@@ -121,10 +121,18 @@ sda_status plan_sparse(const Resolved& r, int kind, int m, SparsePlan* pl) {
     unit_chunk = 4 * ceil_div(ceil_div(m, kUnitWaves), 4);
   }
   if (kind == SDA_TAIL_PROXY) {
-    if (ns == 0) return SDA_EUNSUPPORTED;
-    pl->unit = true;
-    pl->ns = ns;
-    pl->chunk = unit_chunk;
+    if (ns != 0) {
+      pl->unit = true;
+      pl->ns = ns;
+      pl->chunk = unit_chunk;
+      return SDA_OK;
+    }
+    // a list longer than one workgroup holds: split-K on the matrix cores,
+    // each split keeping per-cluster listed counts, logit sums and value
+    // sums for the merge that forms the proxies (bf16 rows only)
+    if (r.dtype != SDA_BF16 || C < 1 || C > kCmax) return SDA_EUNSUPPORTED;
+    stream_shape(units, m, 256, 512, &pl->splits, &pl->chunk);
+    pl->ws = (size_t)units * pl->splits * ((size_t)r.G * kPartStride + (size_t)C * kClusterRec) * sizeof(float);
     return SDA_OK;
   }
   if (kind == SDA_TAIL_NONE) {
@@ -262,7 +270,7 @@ SDA_EXPORT size_t sda_workspace_bytes(const sda_dims* dims, int32_t op, int32_t 
     case SDA_OP_SPARSE: {
       if (m < 0) return 0;
       SparsePlan pl;
-      if (plan_sparse(r, tail_kind, m, &pl) != SDA_OK) return 0;
+      if (plan_sparse(r, tail_kind, m, C, &pl) != SDA_OK) return 0;
       return pl.ws;
     }
     case SDA_OP_DENSE: return dense_ws(r, false);
@@ -435,7 +443,7 @@ sda_status sparse_decode(const sda_dims* dims, const void* q, const void* K, con
   }
 
   SparsePlan pl;
-  st = plan_sparse(r, kind, m, &pl);
+  st = plan_sparse(r, kind, m, kind == SDA_TAIL_PROXY ? tail->C : 0, &pl);
   if (st != SDA_OK) return st;
   if (pl.ws && (!ws || ws_bytes < pl.ws)) return SDA_EWORKSPACE;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
@@ -457,6 +465,15 @@ sda_status sparse_decode(const sda_dims* dims, const void* q, const void* K, con
   if (pl.unit) {
     p.chunk = pl.chunk;
     return hip_status(launch_sparse_unit(p, r.dtype, r.G, kind == SDA_TAIL_PROXY, pl.ns, hs));
+  }
+  if (kind == SDA_TAIL_PROXY) {
+    p.splits = pl.splits;
+    p.chunk = pl.chunk;
+    p.part = reinterpret_cast<float*>(ws);
+    p.cpart = p.part + (size_t)r.B * r.Hkv * pl.splits * r.G * kPartStride;
+    hipError_t e = launch_stream_mfma(p, r.G, kModeProxy, hs);
+    if (e == hipSuccess) e = launch_merge(p, r.G, kModeProxy, hs);
+    return hip_status(e);
   }
   p.splits = pl.splits;
   p.chunk = pl.chunk;
@@ -510,7 +527,7 @@ SDA_EXPORT sda_status sda_sparse_decode_attn_noalloc(const sda_dims* dims, const
   const int kind = tail ? tail->kind : SDA_TAIL_NONE;
   if (kind < SDA_TAIL_NONE || kind > SDA_TAIL_SAMPLED || m < 0) return SDA_EINVAL;
   SparsePlan pl;
-  st = plan_sparse(r, kind, m, &pl);
+  st = plan_sparse(r, kind, m, (kind == SDA_TAIL_PROXY && tail) ? tail->C : 0, &pl);
   if (st != SDA_OK) return st;
   if (pl.ws > (size_t)SDA_NOALLOC_SCRATCH_BYTES) return SDA_EWORKSPACE;
   void* ws = nullptr;

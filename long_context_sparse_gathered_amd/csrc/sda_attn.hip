@@ -2177,6 +2177,8 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
   constexpr int W = 4;
   constexpr bool DENSE = (MODE == kModeDense);
   constexpr bool PRIOR = (MODE == kModePrior);
+  constexpr bool PROXY = (MODE == kModeProxy);
+  constexpr int CBX = PROXY ? kCmax / 16 : 1;  // blocks of 16 clusters (value sums)
   constexpr int RA = PRIOR ? 3 * G : G;  // A rows of the logits
   constexpr int RP = PRIOR ? 2 * G : G;  // A rows of the weighted values
   static_assert(RA <= 16, "the logit rows fit one 16-row block");
@@ -2199,6 +2201,11 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
   __shared__ float s_bm[W][G];
   __shared__ float s_m[W][G], s_l[W][G], s_sp[W][G];
   __shared__ float s_c[G];
+  // proxy mode: the split's listed rows per cluster (count over all waves),
+  // their logit sums per wave, and the cluster of each entry of the batch
+  __shared__ int s_pcn[PROXY ? kCmax : 1];
+  __shared__ float s_pcs[PROXY ? W : 1][PROXY ? kCmax : 1][G];
+  __shared__ __attribute__((aligned(16))) int s_cl[PROXY ? W : 1][KB];
   __shared__ __attribute__((aligned(16))) unsigned char s_pool[W * kWaveLds];
 
   // ---- A operand: row r16, dims 32*st + 8*sub .. +8 ---------------------------
@@ -2244,17 +2251,29 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
   const rsrc_t rv = make_rsrc<bf16_t>(reinterpret_cast<const bf16_t*>(p.V) + kvoff, p.n, p.sn);
 
   // list entry of this lane for the batch at tb: tb + w*KB + lane (lane < KB)
-  int li = -1, lp = -1;
+  int li = -1, lp = -1, lc = -1;
   float lwv = 0.f;
-  auto load_list = [&](int tb, int& vi, int& vp, float& vw) {
+  auto load_list = [&](int tb, int& vi, int& vp, float& vw, int& vc) {
     const int t = tb + w * KB + lane;
     const bool in = lane < KB && t < t1;
     const int64_t a = lbase + (in ? t : 0);
     vi = p.idx[a];
-    if (PRIOR) vp = p.idx[lbase + ((in && t > 0) ? t - 1 : 0)];
+    if (PRIOR || PROXY) vp = p.idx[lbase + ((in && t > 0) ? t - 1 : 0)];
+    if (PROXY && p.idx_cluster) vc = p.idx_cluster[a];
     if (p.logw) vw = p.logw[a];
   };
-  if (!DENSE && t0 < t1) load_list(t0, li, lp, lwv);
+  if (!DENSE && t0 < t1) load_list(t0, li, lp, lwv, lc);
+  if constexpr (PROXY) {
+    for (int i = tid; i < kCmax; i += 256) s_pcn[i] = 0;
+    for (int i = lane; i < kCmax * G; i += 64) (&s_pcs[w][0][0])[i] = 0.f;
+    __syncthreads();
+  }
+  const int CB = PROXY ? (p.C + 15) / 16 : 0;
+  floatx4_t racc[CBX][8];  // proxy mode: listed value sums, 16 clusters x 16 dims per accumulator
+#pragma unroll
+  for (int cb = 0; cb < CBX; ++cb)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) racc[cb][nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
   floatx4_t oacc[8];
 #pragma unroll
@@ -2270,6 +2289,7 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
     int row;
     float lw_own;
     bool cov_own = false;  // the prior covers this lane's row
+    int cm_own = -1;       // proxy mode: cluster of this lane's row, -1 if none
     if constexpr (DENSE) {
       valid = lane < KB && e < t1;
       row = valid ? e : 0;
@@ -2282,7 +2302,15 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
       if constexpr (PRIOR) cov_own = valid && li < p.prior_n;
       int bad = 0;
       if (live && (unsigned)li >= (unsigned)p.n) bad |= SDA_FLAG_IDX_RANGE;
-      if (PRIOR && live && e > 0 && lp >= li) bad |= SDA_FLAG_IDX_ORDER;
+      if ((PRIOR || PROXY) && live && e > 0 && lp >= li) bad |= SDA_FLAG_IDX_ORDER;
+      if constexpr (PROXY) {
+        int c = -1;
+        if (valid) c = p.idx_cluster ? lc : p.cluster_id[(int64_t)u * p.n + li];
+        if (valid && p.idx_cluster && (c < -1 || c >= p.C)) bad |= SDA_FLAG_CLUSTER;
+        cm_own = (valid && c >= 0 && c < p.C) ? c : -1;
+        if (lane < KB) s_cl[w][lane] = cm_own;
+        if (cm_own >= 0) atomicAdd(&s_pcn[cm_own], 1);
+      }
       if (bad) flag_unit(p.flags, u, bad);
     }
     int koff[NT];
@@ -2313,7 +2341,7 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
 #pragma unroll
     for (int k = 0; k < NS; ++k) buf_load(vc[k], rv, voff[k]);
     if constexpr (!DENSE) {
-      if (tb + STEP < t1) load_list(tb + STEP, li, lp, lwv);
+      if (tb + STEP < t1) load_list(tb + STEP, li, lp, lwv, lc);
     }
 
     // ---- logits ---------------------------------------------------------------
@@ -2328,6 +2356,16 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
       const int kk = 16 * t + r16;
       const float lwk = shfl_f(lw_own, kk);
       const bool cvk = PRIOR && shfl_i(cov_own ? 1 : 0, kk) != 0;   // the prior covers this key
+      if constexpr (PROXY) {
+        // the listed rows' logits per cluster (log2 units, no log-weight),
+        // this wave's slots: one LDS add per (key, head)
+        const int ck = shfl_i(cm_own, kk);
+        if (ck >= 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (4 * sub + i < G) lds_add(&s_pcs[w][ck][4 * sub + i], d[i] * p.qscale);
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 4 * sub + i;
@@ -2375,6 +2413,21 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
       float4 y4 = make_float4(0.f, 0.f, 0.f, 0.f);
       if constexpr (PRIOR) y4 = *reinterpret_cast<const float4*>(&s_x[w][r16 >= G && r16 < 2 * G ? r16 + G : 0][16 * t + 4 * sub]);
       const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+      // proxy mode: one-hot cluster rows (row r16 of block cb is cluster
+      // 16cb + r16) for the keys of this lane's operand half, so that the
+      // same B operand also sums the listed values per cluster
+      bf16x8_t a1[CBX];
+      if constexpr (PROXY) {
+        const int4 c4 = *reinterpret_cast<const int4*>(&s_cl[w][16 * t + 4 * sub]);
+        const int cl4[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+        for (int cb = 0; cb < CBX; ++cb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            a1[cb][j] = (__bf16)(cl4[j] == 16 * cb + r16 ? 1.f : 0.f);
+            a1[cb][4 + j] = (__bf16)0.f;
+          }
+      }
       const float ys[4] = {y4.x, y4.y, y4.z, y4.w};
       bf16x8_t a;
 #pragma unroll
@@ -2401,6 +2454,11 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
         const bf16x4_t b4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(src);
         const bf16x8_t b = {b4[0], b4[1], b4[2], b4[3], b4[0], b4[1], b4[2], b4[3]};
         oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, oacc[nb], 0, 0, 0);
+        if constexpr (PROXY) {
+#pragma unroll
+          for (int cb = 0; cb < CBX; ++cb)
+            if (cb < CB) racc[cb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1[cb], b, racc[cb][nb], 0, 0, 0);
+        }
       }
     }
   }
@@ -2454,7 +2512,7 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
       }
     }
     const int64_t qh = qrow0 + h;
-    if (p.splits > 1) {
+    if (PROXY || p.splits > 1) {
       float* rec = p.part + (((int64_t)u * p.splits + split) * G + h) * kPartStride;
       if (dim == 0) {
         rec[0] = M;
@@ -2475,9 +2533,54 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
       if (dim == 0 && p.lse) p.lse[qh] = f.lse;
     }
   }
+  if constexpr (PROXY) {
+    // the split's per-cluster records: counts and logit sums of every
+    // cluster (the merge reads them unconditionally), value sums of the
+    // clusters it touched, the waves' accumulators added through LDS 16
+    // clusters at a time
+    float* cbase = p.cpart + ((int64_t)u * p.splits + split) * p.C * kClusterRec;
+    for (int b = tid; b < p.C; b += 256) {
+      float* rec = cbase + (int64_t)b * kClusterRec;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float sh = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < W; ++ww) sh += s_pcs[ww][b][h];
+        rec[128 + h] = sh;
+      }
+      reinterpret_cast<int*>(rec)[136] = s_pcn[b];
+    }
+    // a wave's pool slice holds 8 cluster rows of fp32 sums: two halves per
+    // block of 16 clusters (rows 8hf .. 8hf+7 come from lanes with sub >> 1 == hf)
+    static_assert(8 * kD * 4 <= kWaveLds, "half a cluster block fits a wave's slice");
+#pragma unroll
+    for (int cb = 0; cb < CBX; ++cb) {
+      if (cb >= CB) break;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        __syncthreads();  // the pool is free
+        float* mine = reinterpret_cast<float*>(s_pool + w * kWaveLds);
+        if ((sub >> 1) == hf) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) mine[(4 * (sub & 1) + i) * kD + 16 * nb + r16] = racc[cb][nb][i];
+        }
+        __syncthreads();
+        for (int e2 = tid; e2 < 8 * kD; e2 += 256) {
+          const int row = e2 / kD, dim = e2 - row * kD;
+          const int b = 16 * cb + 8 * hf + row;
+          if (b < p.C && s_pcn[b] > 0) {
+            float a = 0.f;
+#pragma unroll
+            for (int ww = 0; ww < W; ++ww) a += reinterpret_cast<const float*>(s_pool + ww * kWaveLds)[row * kD + dim];
+            cbase[(int64_t)b * kClusterRec + dim] = a;
+          }
+        }
+      }
+    }
+  }
 }
-
-// ---------------------------------------------------------------------------
 // Merge of split partials: one workgroup per unit, fixed split order.
 template <int G, int MODE>
 __global__ __launch_bounds__(512) void merge_kernel(const AttnParams p) {
@@ -2540,6 +2643,95 @@ __global__ __launch_bounds__(512) void merge_kernel(const AttnParams p) {
       for (int sp = 0; sp < p.splits; ++sp) a += p.ksum[((int64_t)u * p.splits + sp) * kD + dim];
       p.aux2[(int64_t)u * kD + dim] = a / (float)p.n;
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the split-K proxy decode, one workgroup per unit.  The splits'
+// per-cluster listed counts, logit sums and value sums are added in split
+// order; every cluster b with n_b = count_b - (listed rows) > 0 then enters
+// the softmax as its proxy ("OpenAttention", method stage 04): mean logit
+// mu_b = (scale <q, sumK_b> - listed logits) / n_b, weight n_b e^{mu_b - M}
+// in the normaliser and e^{mu_b - M} (sumV_b - listed values) in the
+// numerator, the difference formed in fp32.
+template <int G>
+__global__ __launch_bounds__(512) void merge_proxy_kernel(const AttnParams p) {
+  const int u = blockIdx.x;
+  const int s = u / p.Hkv;
+  const int g = u - s * p.Hkv;
+  const int tid = threadIdx.x;
+  const int C = p.C;
+  __shared__ float s_mu[kCmax][G];   // mean logit of the unread members (log2), -inf if none
+  __shared__ float s_pi[kCmax][G];   // proxy logit mu_b + log2 n_b
+  __shared__ float s_D[kCmax][kD];   // sumV_b minus the listed values
+  const int64_t qrow0 = (int64_t)s * p.Hq + (int64_t)g * G;
+  const float* cb0 = p.cpart + (int64_t)u * p.splits * C * kClusterRec;
+  const int64_t sstride = (int64_t)C * kClusterRec;
+
+  for (int t = tid; t < C * G; t += 512) {
+    const int b = t / G, h = t - b * G;
+    float S = 0.f;
+    int cnt = 0;
+    for (int sp = 0; sp < p.splits; ++sp) {
+      const float* rec = cb0 + sp * sstride + (int64_t)b * kClusterRec;
+      S += rec[128 + h];
+      cnt += reinterpret_cast<const int*>(rec)[136];
+    }
+    const bf16_t* qh = reinterpret_cast<const bf16_t*>(p.q) + (qrow0 + h) * kD;
+    const float* sk = p.sumK + ((int64_t)u * C + b) * kD;
+    float qk = 0.f;
+#pragma unroll 4
+    for (int d0 = 0; d0 < kD; d0 += 8) {
+      RowChunk<bf16_t> c;
+      c.load_cached(qh + d0);
+      float f[8], kf[8];
+      c.unpack(f);
+      load8f(sk + d0, kf);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qk = fmaf(f[i], kf[i], qk);
+    }
+    qk *= p.qscale;
+    const int nb = p.count[(int64_t)u * C + b] - cnt;
+    if (nb < 0 && h == 0) flag_unit(p.flags, u, SDA_FLAG_CLUSTER);
+    const bool ok = nb > 0;
+    const float mu = ok ? (qk - S) / (float)nb : kNegInf;
+    s_mu[b][h] = mu;
+    s_pi[b][h] = ok ? mu + __builtin_amdgcn_logf((float)nb) : kNegInf;
+  }
+  for (int t = tid; t < C * kD; t += 512) {
+    const int b = t / kD, dim = t - b * kD;
+    float r = 0.f;
+    for (int sp = 0; sp < p.splits; ++sp) {
+      const float* rec = cb0 + sp * sstride + (int64_t)b * kClusterRec;
+      if (reinterpret_cast<const int*>(rec)[136] > 0) r += rec[dim];
+    }
+    s_D[b][dim] = p.sumV[((int64_t)u * C + b) * kD + dim] - r;
+  }
+  __syncthreads();
+
+  for (int ei = tid; ei < G * kD; ei += 512) {
+    const int h = ei / kD, dim = ei - h * kD;
+    const float* base = p.part + ((int64_t)u * p.splits * G + h) * kPartStride;
+    const int64_t stride = (int64_t)G * kPartStride;
+    float M = kNegInf;
+    for (int sp = 0; sp < p.splits; ++sp) M = fmaxf(M, base[sp * stride]);
+    for (int b = 0; b < C; ++b) M = fmaxf(M, s_pi[b][h]);
+    float a = 0.f, L = 0.f;
+    if (M != kNegInf) {
+      for (int sp = 0; sp < p.splits; ++sp) {
+        const float* rec = base + sp * stride;
+        const float f = rescale(rec[0], M);
+        a = fmaf(rec[4 + dim], f, a);
+        L = fmaf(rec[1], f, L);
+      }
+      for (int b = 0; b < C; ++b) {
+        a = fmaf(fast_exp2(s_mu[b][h] - M), s_D[b][dim], a);   // exp2(-inf) = 0: no unread member
+        L += fast_exp2(s_pi[b][h] - M);
+      }
+    }
+    const int64_t qh = qrow0 + h;
+    p.out[qh * kD + dim] = (L > 0.f) ? a / L : 0.f;
+    if (dim == 0 && p.lse) p.lse[qh] = (L > 0.f) ? (M + __builtin_amdgcn_logf(L)) * kLn2 : kNegInf;
   }
 }
 
@@ -2669,6 +2861,7 @@ static hipError_t launch_stream_mfma_g(const AttnParams& p, int mode, hipStream_
         break;
       }
       return hipErrorInvalidValue;
+    case kModeProxy: hipLaunchKernelGGL((stream_mfma_kernel<G, kModeProxy, kStreamMfmaTiles>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -2696,6 +2889,7 @@ static hipError_t launch_merge_g(const AttnParams& p, int mode, hipStream_t st) 
     case kModeDense: hipLaunchKernelGGL((merge_kernel<G, kModeSparse>), grid, block, 0, st, p); break;
     case kModePrior: hipLaunchKernelGGL((merge_kernel<G, kModePrior>), grid, block, 0, st, p); break;
     case kModeBuildPrior: hipLaunchKernelGGL((merge_kernel<G, kModeBuildPrior>), grid, block, 0, st, p); break;
+    case kModeProxy: hipLaunchKernelGGL((merge_proxy_kernel<G>), grid, block, 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

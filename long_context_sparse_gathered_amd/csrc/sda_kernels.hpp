@@ -64,6 +64,7 @@ struct AttnParams {
   int32_t splits;              // WGs per unit
   int32_t chunk;               // entries (rows) per split
   float* part;                 // [units, splits, G, kPartStride]
+  float* cpart;                // [units, splits, C, kClusterRec] (split-K proxy decode)
   float* ksum;                 // [units, splits, d] (prior build)
 
   // outputs
@@ -75,7 +76,12 @@ struct AttnParams {
 };
 
 // Stream-kernel modes.
-enum StreamMode { kModeSparse = 0, kModePrior = 1, kModeDense = 2, kModeBuildPrior = 3 };
+enum StreamMode { kModeSparse = 0, kModePrior = 1, kModeDense = 2, kModeBuildPrior = 3, kModeProxy = 4 };
+
+// Per (unit, split, cluster) record of the split-K proxy decode: the listed
+// rows' value sum [0, 128), logit sums per head (log2 units) [128, 136), and
+// the listed-row count (int32 bits) at 136.
+constexpr int kClusterRec = 144;
 
 struct ProxyBuildParams {
   const void* K;

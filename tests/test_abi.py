@@ -101,7 +101,16 @@ def test_proxy_tail_validation(L):
     t.count, t.sumK, t.sumV = FAKE, FAKE, FAKE
     assert _sparse(L, dims, tail=t) == sda.SDA_EINVAL                 # no cluster lookup
     t.cluster_id = FAKE2
-    assert _sparse(L, dims, tail=t, m=600) == sda.SDA_EUNSUPPORTED    # list longer than one workgroup holds
+    # a list longer than one workgroup holds: split-K with per-cluster
+    # records, which needs a workspace (bf16); fp32 rows take only the
+    # one-workgroup kernel
+    need = L.sda_workspace_bytes(ctypes.byref(dims), sda.OP_SPARSE, sda.TAIL_PROXY, 600, 32)
+    assert need > 0
+    assert _sparse(L, dims, tail=t, m=600) == sda.SDA_EWORKSPACE
+    assert _sparse(L, dims, tail=t, m=600, ws=FAKE2, ws_bytes=need - 1) == sda.SDA_EWORKSPACE
+    d32 = _dims()
+    d32.dtype = sda.SDA_F32
+    assert _sparse(L, d32, tail=t, m=600) == sda.SDA_EUNSUPPORTED
 
 
 def test_prior_tail_validation(L):
