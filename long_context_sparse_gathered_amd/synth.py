@@ -273,6 +273,28 @@ def make_case(w: Workload, threads: int | None = None) -> Case:
     return Case(w=w, q=q, K=K, V=V, idx=idx, cid=cid, mu_Q=mu_Q, U=U)
 
 
+def index_sets(c: Case, n_top: int, threads: int | None = None) -> np.ndarray:
+    """The index sets [B, Hkv, n_sink + n_local + n_top] of case c for another
+    top-k count.  K, V, q and the clusters of a unit do not depend on n_top,
+    so these are the lists make_case would give for w.replace(n_top=n_top)."""
+    w = c.w
+    m = w.n_sink + w.n_local + n_top
+    idx = np.empty((w.B, w.Hkv, m), np.int32)
+    scale = np.float32(1.0 / np.sqrt(w.d))
+
+    def fill(u):
+        s, g = divmod(u, w.Hkv)
+        Kf = bf16_bits_to_f32(c.K[s, g]) if c.K.dtype == np.uint16 else c.K[s, g]
+        qs = c.q[s, g * w.G:(g + 1) * w.G]
+        qf = bf16_bits_to_f32(qs) if qs.dtype == np.uint16 else qs
+        idx[s, g] = select_index_set(Kf, qf, w.n_sink, w.n_local, n_top, scale)
+
+    nthreads = threads or min(16, os.cpu_count() or 1)
+    with ThreadPoolExecutor(nthreads) as ex:
+        list(ex.map(fill, range(w.B * w.Hkv)))
+    return idx
+
+
 def unit_case(w: Workload, s: int, g: int) -> Case:
     """One unit as a B=1, Hkv=1 case (same values as in the full workload)."""
     ud = make_unit(w, s, g)

@@ -68,3 +68,16 @@ def test_prior_workload_mean_query():
     assert u.mu_Q.shape == (w.G, w.d) and u.mu_Q.dtype == np.float32
     # the prefill mean sits near a norm-3 vector
     assert np.all(np.abs(np.linalg.norm(u.mu_Q, axis=1) - 3.0) < 0.5)
+
+
+def test_index_sets_for_another_read_fraction():
+    """index_sets(c, n_top) gives the lists make_case gives for that n_top on
+    the same keys and queries."""
+    w = synth.WORKLOADS["proxy_bf16_b1_n32k"].replace(n=4096, n_top=40)
+    c = synth.make_case(w, threads=4)
+    w3 = w.replace(n_top=120)
+    c3 = synth.make_case(w3, threads=4)
+    np.testing.assert_array_equal(c.K, c3.K)
+    got = synth.index_sets(c, 120, threads=4)
+    np.testing.assert_array_equal(got, c3.idx)
+    np.testing.assert_array_equal(synth.index_sets(c, 40, threads=4), c.idx)
