@@ -139,13 +139,15 @@ __device__ __forceinline__ rsrc_t rsrc_of(const void* base, int64_t n, int64_t s
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
+// rows are read once per step: streaming (non-temporal) cache policy
+constexpr int kRowNT = 2;
 __device__ __forceinline__ void gather(RowChunk<bf16_t>& c, rsrc_t r, int off) {
-  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kRowNT);
   c.raw = make_uint4(v[0], v[1], v[2], v[3]);
 }
 __device__ __forceinline__ void gather(RowChunk<float>& c, rsrc_t r, int off) {
-  auto a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-  auto b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+  auto a = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kRowNT);
+  auto b = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, kRowNT);
   c.a = make_float4(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3]));
   c.b = make_float4(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3]));
 }
