@@ -15,9 +15,15 @@
 //  stream_mfma_kernel      they serve plain sparse lists, the rank-1 prior
 //                          ("RESA", Online Aggregator), dense decode and the
 //                          prior build ("RESA", Prior Estimator: one extra
-//                          query over the whole cache).
+//                          query over the whole cache); the matrix-core one
+//                          also takes proxy-tail lists longer than one
+//                          workgroup holds, each split keeping per-cluster
+//                          listed counts, logit sums and value sums.
 //  merge_kernel            log-sum-exp merge of split partials + the prior's
 //                          delta merge.
+//  merge_proxy_kernel      merge of proxy-mode splits: adds the per-cluster
+//                          records across splits, forms the proxy entries
+//                          and finishes the softmax.
 #include "sda_device.hpp"
 #include "sda_kernels.hpp"
 
