@@ -19,7 +19,7 @@ context, 1% read (32 query / 8 KV heads, d = 128, bf16; 328 listed rows and
   and at one thread.
 * `configs` holds one line per measured workload: the single-head fp32
   correctness case, batch 1, the headline shape at 3% read (lists longer
-  than one workgroup holds), the sampled tail (batch 8, 64K), the rank-1
+  than the one-pass kernel holds), the sampled tail (batch 8, 64K), the rank-1
   prior (batch 16, 128K) and the selector (batch 32, 32K), each with
   µs/step, gathered and total GB/s, the dense speedup, the max relative
   error against the oracle and, where the path computes integers, bit-exact
@@ -405,7 +405,8 @@ def gather_ceiling(a, copies, gstate, idx, w, waves, parts):
 
 def measure_three_percent(a, dev, w, c, q, copies, out, lse, dense_ms):
     """The headline shape at 3% read (984 listed rows per KV head): the proxy
-    tail on the split-K path, over the same KV-cache copies."""
+    tail on the long-list path (keys and weights, then values), over the same
+    KV-cache copies."""
     import numpy as np
     import torch
 
@@ -435,7 +436,7 @@ def measure_three_percent(a, dev, w, c, q, copies, out, lse, dense_ms):
         ref, _ = oracle.sparse_proxy_def(uc.q, uc.K, uc.V, uc.idx, uc.cid, w.C)
         errs.append(rel_err(got[s, g * w.G:(g + 1) * w.G], ref[0]))
     by = step_bytes(w3)
-    return line(ms, by["gathered"], by["total"], dense_ms, m=w3.m, path="split-K proxy + merge (2 launches)",
+    return line(ms, by["gathered"], by["total"], dense_ms, m=w3.m, path="two launches of one workgroup per unit: keys and weights, then values",
                 repeats_us=[round(x * 1e3, 3) for x in per], max_rel_err=max(errs), units_checked=len(errs))
 
 

@@ -20,7 +20,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsda.so")
 ARCH = os.environ.get("SDA_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["sda_attn.hip", "sda_build.hip", "sda_sampled.hip", "sda_select.hip", "sda_cluster.hip", "sda_gather.hip", "sda_api.cpp"]
+SOURCES = ["sda_attn.hip", "sda_proxy_long.hip", "sda_build.hip", "sda_sampled.hip", "sda_select.hip", "sda_cluster.hip",
+           "sda_gather.hip", "sda_api.cpp"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden", f"--offload-arch={ARCH}",
           "-I", INCLUDE, "-I", CSRC,

@@ -12,6 +12,7 @@
 
 #include "sda.h"
 #include "sda_kernels.hpp"
+#include "sda_proxy_long.hpp"
 #include "sda_select.hpp"
 #include "sda_cluster.hpp"
 
@@ -90,6 +91,7 @@ void stream_shape(int units, int len, int min_chunk, int target_wgs, int* splits
 
 struct SparsePlan {
   bool unit;      // one workgroup per unit
+  bool two;       // proxy tail in two launches (logits, then values), one workgroup per unit
   int ns;         // slots per wave (unit kernel)
   int splits, chunk;
   size_t ws;
@@ -98,6 +100,7 @@ struct SparsePlan {
 sda_status plan_sparse(const Resolved& r, int kind, int m, int C, SparsePlan* pl) {
   const int units = r.B * r.Hkv;
   pl->unit = false;
+  pl->two = false;
   pl->ns = 0;
   pl->splits = 1;
   pl->chunk = m;
@@ -127,10 +130,19 @@ sda_status plan_sparse(const Resolved& r, int kind, int m, int C, SparsePlan* pl
       pl->chunk = unit_chunk;
       return SDA_OK;
     }
-    // a list longer than one workgroup holds: split-K on the matrix cores,
-    // each split keeping per-cluster listed counts, logit sums and value
-    // sums for the merge that forms the proxies (bf16 rows only)
     if (r.dtype != SDA_BF16 || C < 1 || C > kCmax) return SDA_EUNSUPPORTED;
+    // up to 1024 entries: two launches of one workgroup per unit (keys, then
+    // values), the row weights and cluster coefficients in the workspace
+    if (m <= kLongMaxList) {
+      pl->two = true;
+      pl->chunk = long_chunk(m);
+      pl->ws = ((size_t)units * long_weights_floats(r.G, m) * sizeof(float) + 255) / 256 * 256 +
+               (size_t)units * long_coef_floats(r.G, C) * sizeof(float);
+      return SDA_OK;
+    }
+    // longer: split-K on the matrix cores, each split keeping per-cluster
+    // listed counts, logit sums and value sums for the merge that forms the
+    // proxies
     stream_shape(units, m, 256, 512, &pl->splits, &pl->chunk);
     pl->ws = (size_t)units * pl->splits * ((size_t)r.G * kPartStride + (size_t)C * kClusterRec) * sizeof(float);
     return SDA_OK;
@@ -465,6 +477,13 @@ sda_status sparse_decode(const sda_dims* dims, const void* q, const void* K, con
   if (pl.unit) {
     p.chunk = pl.chunk;
     return hip_status(launch_sparse_unit(p, r.dtype, r.G, kind == SDA_TAIL_PROXY, pl.ns, hs));
+  }
+  if (pl.two) {
+    p.chunk = pl.chunk;
+    p.part = reinterpret_cast<float*>(ws);
+    const size_t wbytes = (size_t)r.B * r.Hkv * long_weights_floats(r.G, m) * sizeof(float);
+    p.cpart = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (wbytes + 255) / 256 * 256);
+    return hip_status(launch_proxy_long(p, r.G, hs));
   }
   if (kind == SDA_TAIL_PROXY) {
     p.splits = pl.splits;

@@ -1,10 +1,12 @@
-"""GPU parity of the proxy tail with lists longer than one workgroup holds:
-split-K on the matrix cores, each split keeping per-cluster listed counts,
-logit sums and value sums that the merge adds before it forms the proxy
-entries ("OpenAttention: One Percent Is Enough with Tail Proxies", method
-stage 04: each cluster's unread tokens fold into one virtual token; key
-points: 3% read, 96K context).  Against the oracle's O(n) definition, max
-rel err <= 2e-3 (bf16 inputs)."""
+"""GPU parity of the proxy tail with lists longer than the one-pass kernel
+holds ("OpenAttention: One Percent Is Enough with Tail Proxies", method stage
+04: each cluster's unread tokens fold into one virtual token; key points: 3%
+read, 96K context).  Up to 1024 entries the library runs two launches per
+unit (keys, proxies and row weights; then values); beyond that split-K on the
+matrix cores, each split keeping per-cluster listed counts, logit sums and
+value sums that a merge adds before it forms the proxies (the log-weight and
+ragged case, 1268 entries).  Against the oracle's O(n) definition, max rel
+err <= 2e-3 (bf16 inputs)."""
 import numpy as np
 import pytest
 import torch
@@ -98,8 +100,8 @@ def test_proxy_long_general_clusters_c64(orc):
 
 
 def test_proxy_long_mostly_read_clusters(orc):
-    """The cancellation case on the split-K path: clusters of 256 rows with
-    254 listed (low logits) and 2 unread near the unit's largest logit."""
+    """The cancellation case on the long-list path: clusters of 256 rows
+    with 254 listed (low logits) and 2 unread near the unit's largest logit."""
     rng = np.random.default_rng(5)
     B, Hkv, G, n, d_, C, size, m = 1, 4, 4, 8192, 128, 32, 256, 900
     q = synth.round_bf16_bits(rng.standard_normal((B, G * Hkv, d_)).astype(np.float32))
@@ -129,7 +131,7 @@ def test_proxy_long_mostly_read_clusters(orc):
     torch.cuda.synchronize()
     ref, ref_lse = orc.sparse_proxy_def(q, K, V, idx, cid, C)
     err = rel_err(out, ref)
-    print(f"mostly-read clusters, split-K: max rel err {err:.3e} (tolerance {TOL:.0e})")
+    print(f"mostly-read clusters, long list: max rel err {err:.3e} (tolerance {TOL:.0e})")
     assert err <= TOL
     assert lse_err(lse, ref_lse) <= LSE_TOL
 
