@@ -405,8 +405,7 @@ def gather_ceiling(a, copies, gstate, idx, w, waves, parts):
 
 def measure_three_percent(a, dev, w, c, q, copies, out, lse, dense_ms):
     """The headline shape at 3% read (984 listed rows per KV head): the proxy
-    tail on the long-list path (keys and weights, then values), over the same
-    KV-cache copies."""
+    tail on the long-list kernel, over the same KV-cache copies."""
     import numpy as np
     import torch
 
@@ -436,7 +435,7 @@ def measure_three_percent(a, dev, w, c, q, copies, out, lse, dense_ms):
         ref, _ = oracle.sparse_proxy_def(uc.q, uc.K, uc.V, uc.idx, uc.cid, w.C)
         errs.append(rel_err(got[s, g * w.G:(g + 1) * w.G], ref[0]))
     by = step_bytes(w3)
-    return line(ms, by["gathered"], by["total"], dense_ms, m=w3.m, path="two launches of one workgroup per unit: keys and weights, then values",
+    return line(ms, by["gathered"], by["total"], dense_ms, m=w3.m, path="one workgroup per unit, value rows requested as the key tiles are consumed",
                 repeats_us=[round(x * 1e3, 3) for x in per], max_rel_err=max(errs), units_checked=len(errs))
 
 

@@ -116,12 +116,12 @@ typedef struct {
    * denote the sums without the listed rows.  The list must hold distinct
    * positions in increasing order.  Lists of up to 512 entries per unit
    * (384 when 8 query heads share a KV head) run in one workgroup per unit
-   * with no workspace.  Longer bf16 lists need a workspace
-   * (sda_workspace_bytes gives the size): up to 1024 entries, two launches
-   * of one workgroup per unit (keys, proxies and row weights, then values);
-   * beyond that the list is split across workgroups, each split writing
-   * per-cluster listed counts, logit sums and value sums.  Longer fp32 lists
-   * return SDA_EUNSUPPORTED. */
+   * with no workspace, and so do bf16 lists of up to 1024 entries (a
+   * second kernel that streams the value rows behind the key rows).  Longer
+   * bf16 lists are split across workgroups, each split writing per-cluster
+   * listed counts, logit sums and value sums to the workspace
+   * (sda_workspace_bytes gives the size).  Longer fp32 lists return
+   * SDA_EUNSUPPORTED. */
   int32_t C;                     /* clusters per unit, 1 <= C <= 64         */
   const int32_t* idx_cluster;    /* [B,Hkv,m] cluster of each listed row (as
                                     a per-cluster selector emits it), or

@@ -91,7 +91,7 @@ void stream_shape(int units, int len, int min_chunk, int target_wgs, int* splits
 
 struct SparsePlan {
   bool unit;      // one workgroup per unit
-  bool two;       // proxy tail in two launches (logits, then values), one workgroup per unit
+  bool two;       // proxy tail over a long list (keys, then values), one workgroup per unit
   int ns;         // slots per wave (unit kernel)
   int splits, chunk;
   size_t ws;
@@ -131,13 +131,11 @@ sda_status plan_sparse(const Resolved& r, int kind, int m, int C, SparsePlan* pl
       return SDA_OK;
     }
     if (r.dtype != SDA_BF16 || C < 1 || C > kCmax) return SDA_EUNSUPPORTED;
-    // up to 1024 entries: two launches of one workgroup per unit (keys, then
-    // values), the row weights and cluster coefficients in the workspace
+    // up to 1024 entries: one workgroup per unit, value rows requested as
+    // the key tiles are consumed, no workspace
     if (m <= kLongMaxList) {
       pl->two = true;
       pl->chunk = long_chunk(m);
-      pl->ws = ((size_t)units * long_weights_floats(r.G, m) * sizeof(float) + 255) / 256 * 256 +
-               (size_t)units * long_coef_floats(r.G, C) * sizeof(float);
       return SDA_OK;
     }
     // longer: split-K on the matrix cores, each split keeping per-cluster
@@ -480,9 +478,6 @@ sda_status sparse_decode(const sda_dims* dims, const void* q, const void* K, con
   }
   if (pl.two) {
     p.chunk = pl.chunk;
-    p.part = reinterpret_cast<float*>(ws);
-    const size_t wbytes = (size_t)r.B * r.Hkv * long_weights_floats(r.G, m) * sizeof(float);
-    p.cpart = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + (wbytes + 255) / 256 * 256);
     return hip_status(launch_proxy_long(p, r.G, hs));
   }
   if (kind == SDA_TAIL_PROXY) {

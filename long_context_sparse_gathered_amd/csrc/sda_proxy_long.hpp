@@ -1,5 +1,5 @@
-// sda_proxy_long.hpp -- limits and launcher of the two-launch proxy decode
-// for lists longer than the one-pass kernel holds (sda_proxy_long.hip).
+// sda_proxy_long.hpp -- limits and launcher of the proxy decode for lists
+// longer than the one-pass kernel holds (sda_proxy_long.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -18,12 +18,7 @@ inline int long_chunk(int m) {
   return (per + 15) / 16 * 16;
 }
 
-// Workspace floats per unit: the listed rows' weights [G][8 * chunk], then
-// the cluster coefficients [C][G], the maxima [G] and the normalisers [G].
-inline size_t long_weights_floats(int G, int m) { return (size_t)G * kLongWaves * long_chunk(m); }
-inline size_t long_coef_floats(int G, int C) { return (size_t)C * G + 2 * (size_t)G; }
-
-// p.part: weights of all units, p.cpart: coefficient blocks, p.chunk = long_chunk(m).
+// One workgroup per unit and no workspace; p.chunk = long_chunk(p.m).
 hipError_t launch_proxy_long(const AttnParams& p, int G, hipStream_t st);
 
 }  // namespace sda

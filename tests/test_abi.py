@@ -101,13 +101,15 @@ def test_proxy_tail_validation(L):
     t.count, t.sumK, t.sumV = FAKE, FAKE, FAKE
     assert _sparse(L, dims, tail=t) == sda.SDA_EINVAL                 # no cluster lookup
     t.cluster_id = FAKE2
-    # a list longer than one workgroup holds: split-K with per-cluster
-    # records, which needs a workspace (bf16); fp32 rows take only the
-    # one-workgroup kernel
-    need = L.sda_workspace_bytes(ctypes.byref(dims), sda.OP_SPARSE, sda.TAIL_PROXY, 600, 32)
+    # up to 1024 entries (bf16) one workgroup per unit, no workspace; longer
+    # lists split across workgroups with per-cluster records, which need a
+    # workspace; fp32 rows take only the one-pass kernel (m <= 512)
+    assert L.sda_workspace_bytes(ctypes.byref(dims), sda.OP_SPARSE, sda.TAIL_PROXY, 600, 32) == 0
+    assert L.sda_workspace_bytes(ctypes.byref(dims), sda.OP_SPARSE, sda.TAIL_PROXY, 1024, 32) == 0
+    need = L.sda_workspace_bytes(ctypes.byref(dims), sda.OP_SPARSE, sda.TAIL_PROXY, 1025, 32)
     assert need > 0
-    assert _sparse(L, dims, tail=t, m=600) == sda.SDA_EWORKSPACE
-    assert _sparse(L, dims, tail=t, m=600, ws=FAKE2, ws_bytes=need - 1) == sda.SDA_EWORKSPACE
+    assert _sparse(L, dims, tail=t, m=1025) == sda.SDA_EWORKSPACE
+    assert _sparse(L, dims, tail=t, m=1025, ws=FAKE2, ws_bytes=need - 1) == sda.SDA_EWORKSPACE
     d32 = _dims()
     d32.dtype = sda.SDA_F32
     assert _sparse(L, d32, tail=t, m=600) == sda.SDA_EUNSUPPORTED

@@ -1,12 +1,12 @@
 """GPU parity of the proxy tail with lists longer than the one-pass kernel
 holds ("OpenAttention: One Percent Is Enough with Tail Proxies", method stage
 04: each cluster's unread tokens fold into one virtual token; key points: 3%
-read, 96K context).  Up to 1024 entries the library runs two launches per
-unit (keys, proxies and row weights; then values); beyond that split-K on the
-matrix cores, each split keeping per-cluster listed counts, logit sums and
-value sums that a merge adds before it forms the proxies (the log-weight and
-ragged case, 1268 entries).  Against the oracle's O(n) definition, max rel
-err <= 2e-3 (bf16 inputs)."""
+read, 96K context).  Up to 1024 entries the library runs one workgroup per
+unit that streams the value rows behind the key rows; beyond that split-K on
+the matrix cores, each split keeping per-cluster listed counts, logit sums
+and value sums that a merge adds before it forms the proxies (the log-weight
+and ragged case with 1268 entries).  Against the oracle's O(n) definition,
+max rel err <= 2e-3 (bf16 inputs)."""
 import numpy as np
 import pytest
 import torch
@@ -40,9 +40,15 @@ def _check(orc, w, c, d, idx_cluster=True, logw=None, idx_len=None):
     return err
 
 
-def _needs_split_k(d, w, m):
-    """The list is too long for the one-workgroup kernel: the workspace query
-    asks for per-cluster records."""
+def _long_list(w, m):
+    """The list is longer than the one-pass kernel takes (512 entries, 384
+    at eight query heads per KV head)."""
+    return m > (384 if w.G == 8 else 512)
+
+
+def _split_k(d, w, m):
+    """Beyond 1024 entries: split-K, whose per-cluster records need a
+    workspace."""
     return sda.workspace_bytes(sda.make_dims(d["K"], w.Hq), sda.OP_SPARSE, sda.TAIL_PROXY, m, w.C) > 0
 
 
@@ -52,7 +58,7 @@ def test_proxy_32k_three_percent(orc):
     w = synth.WORKLOADS["proxy_bf16_b1_n32k"].replace(B=2, n_top=_pct(32768, 0.03) - 68)
     c = synth.make_case(w)
     d = case_to_dev(c)
-    assert c.idx.shape[-1] == 984 and _needs_split_k(d, w, 984)
+    assert c.idx.shape[-1] == 984 and _long_list(w, 984) and not _split_k(d, w, 984)
     _check(orc, w, c, d)
 
 
@@ -62,7 +68,7 @@ def test_proxy_96k_one_percent(orc):
     w = synth.WORKLOADS["proxy_bf16_b1_n32k"].replace(B=1, n=n, n_top=_pct(n, 0.01) - 68)
     c = synth.make_case(w)
     d = case_to_dev(c)
-    assert _needs_split_k(d, w, c.idx.shape[-1])
+    assert _long_list(w, c.idx.shape[-1])
     _check(orc, w, c, d)
 
 
@@ -71,7 +77,7 @@ def test_proxy_long_group_sizes(orc, G):
     w = synth.WORKLOADS["proxy_bf16_b1_n32k"].replace(B=2, Hq=2 * G, Hkv=2, n=8192, n_top=700, C=37)
     c = synth.make_case(w)
     d = case_to_dev(c)
-    assert _needs_split_k(d, w, c.idx.shape[-1])
+    assert _long_list(w, c.idx.shape[-1])
     _check(orc, w, c, d, idx_cluster=(G != 2))
 
 
@@ -83,6 +89,20 @@ def test_proxy_long_logw_and_ragged(orc):
     logw = rng.normal(0.0, 0.5, size=c.idx.shape).astype(np.float32)
     lens = rng.integers(0, c.idx.shape[-1] + 1, size=(w.B, w.Hkv)).astype(np.int32)
     lens[0, 0], lens[0, 1] = 0, c.idx.shape[-1]
+    assert _split_k(d, w, c.idx.shape[-1])
+    _check(orc, w, c, d, logw=logw, idx_len=lens)
+
+
+def test_proxy_long_list_logw_and_ragged(orc):
+    """The same on the one-workgroup long-list path (1000 entries)."""
+    w = synth.WORKLOADS["proxy_bf16_b1_n32k"].replace(B=2, n=16384, n_top=932, C=20)
+    c = synth.make_case(w)
+    d = case_to_dev(c)
+    rng = np.random.default_rng(6)
+    logw = rng.normal(0.0, 0.5, size=c.idx.shape).astype(np.float32)
+    lens = rng.integers(0, c.idx.shape[-1] + 1, size=(w.B, w.Hkv)).astype(np.int32)
+    lens[0, 0], lens[0, 1], lens[1, 2] = 0, c.idx.shape[-1], 513
+    assert _long_list(w, c.idx.shape[-1]) and not _split_k(d, w, c.idx.shape[-1])
     _check(orc, w, c, d, logw=logw, idx_len=lens)
 
 
