@@ -349,9 +349,16 @@ sda_status sda_select_qgs(const sda_dims* dims, const void* q, const sda_selecto
  * 32-bit word a wave loaded to checksum[(u * parts + part) * waves + wave]
  * ([B * Hkv * parts * waves] uint32).  It computes nothing else: timing it
  * beside sda_sparse_decode_attn gives the rate at which the memory system
- * delivers the same rows in that launch shape.  Returns SDA_EUNSUPPORTED
- * when a row group would hold more rows than the kernel keeps in registers
- * (24 at 4 or 8 waves, 12 at 16).  K, V and state 16-byte aligned. */
+ * delivers the same rows in that launch shape.
+ * Partition: part p takes list entries [p*EP, (p+1)*EP) (EP = ceil(m /
+ * parts)), its wave w the run [w*EW, (w+1)*EW) of those (EW = ceil(EP /
+ * waves)); part p takes the state bytes [p*SP, (p+1)*SP) (SP = ceil(
+ * state_bytes / parts) rounded up to 16), thread t of the part the 16-byte
+ * chunks at offsets p*SP + 16 t + k*16*64*waves that end inside the share,
+ * XOR-ed into the checksum of wave t / 64.
+ * bf16 rows only (else SDA_EUNSUPPORTED); SDA_EUNSUPPORTED also when a row
+ * group would hold more rows than the kernel keeps in registers (24 at 4 or
+ * 8 waves, 12 at 16).  K, V and state 16-byte aligned. */
 sda_status sda_gather_rows(const sda_dims* dims, const void* K, const void* V, const int32_t* idx,
                            int32_t m, const void* state, int64_t state_bytes, int32_t waves,
                            int32_t parts, uint32_t* checksum, void* stream);

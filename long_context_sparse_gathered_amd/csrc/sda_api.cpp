@@ -670,6 +670,7 @@ SDA_EXPORT sda_status sda_gather_rows(const sda_dims* dims, const void* K, const
   sda_status st = resolve(dims, &r);
   if (st != SDA_OK) return st;
   if (!K || !V || !checksum || (m > 0 && !idx)) return SDA_EINVAL;
+  if (r.dtype != SDA_BF16) return SDA_EUNSUPPORTED;  // a lane quarter covers one 256-byte bf16 row
   if (!aligned16(K) || !aligned16(V)) return SDA_EINVAL;
   if (m < 0 || state_bytes < 0) return SDA_ESHAPE;
   if (state_bytes > 0 && (!state || !aligned16(state) || state_bytes % 16)) return SDA_EINVAL;

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(WAVES * 64) void gather_rows_kernel(const GatherPar
   // per-unit state: this part's share, 16 bytes per thread and step
   uint32_t x = 0;
   if (p.state_bytes > 0) {
-    const int64_t sp = (p.state_bytes + p.parts - 1) / p.parts;
+    const int64_t sp = ((p.state_bytes + p.parts - 1) / p.parts + 15) / 16 * 16;  // 16-byte aligned shares
     const int64_t sb0 = part * sp, sb1 = min(p.state_bytes, sb0 + sp);
     const char* base = static_cast<const char*>(p.state) + (int64_t)u * p.state_bytes;
     for (int64_t b = sb0 + 16 * (int64_t)tid; b + 16 <= sb1; b += 16 * WAVES * 64) {

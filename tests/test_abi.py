@@ -231,3 +231,17 @@ def test_noalloc_entry_rejects_calls_beyond_its_scratch(L):
     rc = L.sda_sparse_decode_attn_noalloc(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE2, None, None, 1000,
                                           ctypes.byref(t), FAKE, None, None, None)
     assert rc == sda.SDA_EWORKSPACE
+
+
+def test_gather_rows_validation(L):
+    """The gather measurement aid: bf16 rows only, supported shapes, aligned
+    state whose size is a multiple of 16, rows per group within registers."""
+    def call(dims, m=100, state=None, sbytes=0, waves=8, parts=1):
+        return L.sda_gather_rows(ctypes.byref(dims), FAKE, FAKE2, FAKE, m, state, sbytes, waves, parts, FAKE2, None)
+    assert call(_dims(dtype=sda.SDA_F32)) == sda.SDA_EUNSUPPORTED
+    assert call(_dims(), waves=2) == sda.SDA_EUNSUPPORTED
+    assert call(_dims(), parts=17) == sda.SDA_EUNSUPPORTED
+    assert call(_dims(), m=8 * 4 * 25) == sda.SDA_EUNSUPPORTED        # 25 rows per row group at 8 waves
+    assert call(_dims(), state=FAKE, sbytes=24) == sda.SDA_EINVAL      # not a multiple of 16
+    assert call(_dims(), state=MISALIGNED, sbytes=32) == sda.SDA_EINVAL
+    assert call(_dims(), m=-1) == sda.SDA_ESHAPE
