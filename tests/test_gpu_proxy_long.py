@@ -177,3 +177,50 @@ def test_proxy_long_twice_and_flags():
     torch.cuda.synchronize()
     f = flags.cpu().numpy()
     assert f[0, 1] & sda.FLAG_CLUSTER and f[1, 0] == 0
+
+
+def test_long_list_edges(orc):
+    """The one-workgroup long-list path at its limits: 1024 entries at eight
+    query heads per KV head; an interleaved K|V cache with the cluster looked
+    up per row and a single cluster; every cluster entirely listed (no proxy
+    at all: plain sparse attention over the list); empty and one-entry units."""
+    # 1024 entries, G = 8
+    w = synth.WORKLOADS["proxy_bf16_b1_n32k"].replace(B=1, Hq=16, Hkv=2, n=8192, n_top=956, C=24)
+    c = synth.make_case(w)
+    d = case_to_dev(c)
+    assert c.idx.shape[-1] == 1024 and _long_list(w, 1024) and not _split_k(d, w, 1024)
+    _check(orc, w, c, d)
+    # interleaved K|V, cluster lookup, C = 1
+    w = synth.WORKLOADS["proxy_bf16_b1_n32k"].replace(B=1, n=6000, n_top=700, C=1, seg="equal")
+    c = synth.make_case(w)
+    kv = np.stack([c.K, c.V], axis=3)              # [B, Hkv, n, 2, d]
+    KV = to_dev(kv)
+    K, V = KV[:, :, :, 0, :], KV[:, :, :, 1, :]
+    cid = to_dev(c.cid)
+    st = sda.build_tail_proxies(K, V, cid, w.C)
+    out, lse = sda.sparse_decode_attn(to_dev(c.q), K, V, to_dev(c.idx), tail=st, cluster_id=cid)
+    torch.cuda.synchronize()
+    ref, ref_lse = orc.sparse_proxy_def(c.q, c.K, c.V, c.idx, c.cid, w.C)
+    assert rel_err(out, ref) <= TOL and lse_err(lse, ref_lse) <= LSE_TOL
+    # every cluster entirely listed: the clusters are the listed rows' own, so
+    # n_b = 0 for all and the result is plain sparse attention
+    w = synth.WORKLOADS["proxy_bf16_b1_n32k"].replace(B=1, n=4096, n_top=632, C=8)
+    c = synth.make_case(w)
+    cid = np.full(c.cid.shape, -1, np.int32)
+    for g in range(w.Hkv):
+        cid[0, g, c.idx[0, g]] = np.arange(c.idx.shape[-1]) * 8 // c.idx.shape[-1]
+    c.cid = cid
+    d = case_to_dev(c)
+    st = sda.build_tail_proxies(d["K"], d["V"], d["cid"], w.C)
+    out, lse = sda.sparse_decode_attn(d["q"], d["K"], d["V"], d["idx"], tail=st, idx_cluster=d["idx_cluster"])
+    torch.cuda.synchronize()
+    ref, ref_lse = orc.sparse(c.q, c.K, c.V, c.idx)
+    assert rel_err(out, ref) <= TOL and lse_err(lse, ref_lse) <= LSE_TOL
+    # empty and one-entry units
+    w = synth.WORKLOADS["proxy_bf16_b1_n32k"].replace(B=2, n=8192, n_top=700, C=16)
+    c = synth.make_case(w)
+    d = case_to_dev(c)
+    lens = np.full((w.B, w.Hkv), c.idx.shape[-1], np.int32)
+    lens[0, :4] = 0
+    lens[1, 3] = 1
+    _check(orc, w, c, d, idx_len=lens)
