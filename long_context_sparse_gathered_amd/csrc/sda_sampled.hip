@@ -600,10 +600,12 @@ __global__ __launch_bounds__(512) void sampled_stats_kernel(const AttnParams p) 
       for (int ww = 0; ww < kW; ++ww) a += s_part[ww][h][i];
       s_mN[h][i] = b0 > 0 ? a / (double)b0 : 0.0;
     }
-    if (tid < G) {
+    // wave h sums head h's base weights (lanes strided, then a wave sum)
+    if (w < G) {
       double a = 0.0;
-      for (int k = 0; k < b0; ++k) a += s_wb[k][tid];
-      s_mD[tid] = b0 > 0 ? a / (double)b0 : 0.0;
+      for (int k = lane; k < b0; k += 64) a += s_wb[k][w];
+      a = sum_rowgroups_d(sum16_d(a));
+      if (lane == 0) s_mD[w] = b0 > 0 ? a / (double)b0 : 0.0;
     }
     __syncthreads();
   }
@@ -655,27 +657,32 @@ __global__ __launch_bounds__(512) void sampled_stats_kernel(const AttnParams p) 
     }
     __syncthreads();
   }
-  if (tid < G) {
+  // wave h: head h's weight variance (lanes strided, then a wave sum), then
+  // its budget on lane 0
+  if (w < G) {
 #pragma clang fp contract(off)
-    const int h = tid;
-    double bh = 0.0;
-    if (b0 > 0) {
-      const double mD = s_mD[h];
-      double varD = 0.0;
-      for (int k = 0; k < b0; ++k) {
-        const double dv = s_wb[k][h] - mD;
-        varD += dv * dv;
-      }
-      varD /= (double)(b0 - 1);
-      double trN = 0.0;
-#pragma unroll
-      for (int ww = 0; ww < kW; ++ww) trN += s_pm[ww][h];
-      trN /= (double)(b0 - 1);
-      const double normN = sqrt(s_hs[h][0] + s_hs[h][1]);
-      const double Dhat = s_Df[h] + (double)n_s * mD;
-      bh = budget_of(p.z, p.eps, (double)n_s, varD, Dhat, trN, normN);
+    const int h = w;
+    const double mD = s_mD[h];
+    double varD = 0.0;
+    for (int k = lane; k < b0; k += 64) {
+      const double dv = s_wb[k][h] - mD;
+      varD += dv * dv;
     }
-    s_bh[h] = bh;
+    varD = sum_rowgroups_d(sum16_d(varD));
+    if (lane == 0) {
+      double bh = 0.0;
+      if (b0 > 0) {
+        varD /= (double)(b0 - 1);
+        double trN = 0.0;
+#pragma unroll
+        for (int ww = 0; ww < kW; ++ww) trN += s_pm[ww][h];
+        trN /= (double)(b0 - 1);
+        const double normN = sqrt(s_hs[h][0] + s_hs[h][1]);
+        const double Dhat = s_Df[h] + (double)n_s * mD;
+        bh = budget_of(p.z, p.eps, (double)n_s, varD, Dhat, trN, normN);
+      }
+      s_bh[h] = bh;
+    }
   }
   __syncthreads();
   if (tid == 0) {
