@@ -154,11 +154,13 @@ sda_status plan_sparse(const Resolved& r, int kind, int m, int C, SparsePlan* pl
     }
   }
   if (kind == SDA_TAIL_SAMPLED) {
-    // scratch per unit: the fp64 exact part (M, D_f, N_f), the draw
-    // partials, the budget and the work-item numbering
+    // scratch per unit: the fp64 exact part (M, D_f, N_f) and its split
+    // records, the base draws' moments, the draw partials, the budget and
+    // the work-item numbering
     if (m > kSampMaxList || units > kSampMaxUnits) return SDA_EUNSUPPORTED;
     pl->splits = sampled_exact_splits(units);
     pl->ws = (size_t)units * ((size_t)(1 + pl->splits) * r.G * (2 + kD) * sizeof(double) +
+                              (size_t)r.G * (4 + kD) * sizeof(double) +
                               (size_t)sampled_max_items(r.n) * r.G * kDrawRec * sizeof(float) +
                               2 * sizeof(int32_t)) +
              sizeof(int32_t);
@@ -465,6 +467,8 @@ sda_status sparse_decode(const sda_dims* dims, const void* q, const void* K, con
     p.splits = pl.splits;
     p.wexact = reinterpret_cast<double*>(w);
     w += units * (size_t)pl.splits * r.G * (2 + kD) * sizeof(double);
+    p.wbase = reinterpret_cast<double*>(w);
+    w += units * (size_t)r.G * (4 + kD) * sizeof(double);
     p.part = reinterpret_cast<float*>(w);
     w += units * (size_t)sampled_max_items(r.n) * r.G * kDrawRec * sizeof(float);
     p.wb = reinterpret_cast<int32_t*>(w);

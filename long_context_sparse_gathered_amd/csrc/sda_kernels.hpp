@@ -57,6 +57,7 @@ struct AttnParams {
   int32_t* samples_out;        // [B,Hkv,b_cap] or null
   double* wstat;               // workspace: [units, G*(2 + d)] fp64 M, D_f, N_f of the exact part
   double* wexact;              // workspace: [units, splits, G*(2 + d)] fp64 records of the I_f shares
+  double* wbase;               // workspace: [units, G*(4 + d)] fp64 moments of the base draws
   int32_t* wb;                 // workspace: [units] sample budget b
   int32_t* wsched;             // workspace: [units + 1] first draw work item of each unit
 
@@ -122,10 +123,11 @@ constexpr int kDrawRec = 4 + 128;        // floats per (work item, head) partial
 constexpr int kSampMaxUnits = 4096;
 constexpr int kDrawGrid = 768;           // draw workgroups (upper bound): three per CU
 __host__ __device__ inline int sampled_max_items(int n) { return (n + kDrawChunk - 1) / kDrawChunk; }
-// Workgroups per unit that share the exact pass over I_f (about 256 in all).
+// Workgroups per unit that share the exact pass over I_f: with the unit's
+// base-draw workgroup, about 256 in all (the kernel holds one per CU).
 constexpr int kSampMaxSplits = 8;  // exact-part workgroups per unit (at most)
 inline int sampled_exact_splits(int units) {
-  const int s = 256 / units;
+  const int s = 256 / units - 1;
   return s < 1 ? 1 : (s > kSampMaxSplits ? kSampMaxSplits : s);
 }
 hipError_t launch_proxy_build(const ProxyBuildParams& p, int dtype, int units, hipStream_t st);

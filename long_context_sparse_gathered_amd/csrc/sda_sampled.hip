@@ -6,13 +6,20 @@
 // numerator and the denominator (b = max(b_N, b_D), Lemma 4.2), with the
 // statistics estimated from b0 base draws.
 //
-// Three launches per call:
-//   sampled_stats_kernel  one workgroup per (sequence, KV head): I_f and the
-//                         base draws in fp64, the budget b; leaves M, D_f,
-//                         N_f and b in the workspace.
-//   sampled_draws_kernel  `splits` workgroups per unit share the b fresh
-//                         draws: each generates its draws' positions, gathers
-//                         the rows and keeps an fp32 online softmax.
+// Four launches per call:
+//   sampled_exact_kernel  about 256 workgroups share the exact pass over I_f
+//                         (fp64 records per share); B*Hkv more workgroups,
+//                         one per (sequence, KV head), check the list and
+//                         take the b0 base draws' fp64 moments relative to
+//                         their own maximum.
+//   sampled_budget_kernel one workgroup per unit: the records merged at the
+//                         unit's maximum M, the base moments rescaled to it,
+//                         the budget b; leaves M, D_f, N_f and b in the
+//                         workspace.
+//   sampled_draws_kernel  up to kDrawGrid workgroups share the b fresh draws
+//                         of every unit (work items of kDrawChunk draws):
+//                         each generates its draws' positions, gathers the
+//                         rows and keeps an fp32 online softmax.
 //   sampled_merge_kernel  one workgroup per unit: log-sum-exp merge of the
 //                         draw partials, then num = N_f + (n_s/b) N_dyn and
 //                         den = D_f + (n_s/b) D_dyn in fp64.
@@ -180,22 +187,298 @@ __device__ double budget_of(double z, double eps, double n_s, double varD, doubl
 
 }  // namespace
 
-// Exact part over a share of I_f: rows [c*per, min(mf, (c+1)*per)) of unit u
-// for workgroup (u, c), an fp64 online softmax per row group (keys and values
-// read together), merged into one record (m, D, N) per head relative to m.
+// Base draws of unit u, on one extra workgroup of the exact-part launch (they
+// need nothing from the exact part): the deterministic list's checks and its
+// rank map, the b0 base positions, their fp64 logits, and per head, relative
+// to the base draws' own maximum m_b (w' = e^{s - m_b}): S1 = sum w',
+// VD = sum (w' - S1/b0)^2, N1 = sum w' v, TN = sum_k |w'_k v_k - N1/b0|^2.
+// The budget kernel rescales them to the unit's maximum.  Record per head,
+// in wbase: m_b, S1, VD, TN at [h], [G + h], [2G + h], [3G + h], N1 at
+// [4G + h*d, 4G + (h+1)*d).
 template <typename T, int G>
-__global__ __launch_bounds__(512) void sampled_exact_kernel(const AttnParams p) {
+__device__ void sampled_base_role(const AttnParams& p, int u, double (&s_part)[kW][G][kD]) {
   constexpr int NSB = 2;               // slots (of 4 rows) per wave per batch
   constexpr int STEP = 4 * kW * NSB;   // rows per batch
   constexpr double kInf = __builtin_huge_val();
-  const int u = blockIdx.x / p.splits;
-  const int c = blockIdx.x - u * p.splits;
   const int s = u / p.Hkv;
   const int g = u - s * p.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, sub = lane >> 4;
 
+  __shared__ int s_A[kSampMaxList];
+  __shared__ int s_bj[kSampMaxB0];
+  __shared__ double s_wb[kSampMaxB0][G];  // base draws: logits, then weights e^{s - m_b}
+  __shared__ double s_pm[kW][G];
+  __shared__ double s_mb[G], s_S1[G];
+  __shared__ double s_N1[G][kD];
+
+  // ---- the deterministic set, as A[i] = I_f[i] - i ---------------------------
+  int mf = p.m;
+  if (p.idx_len) {
+    int L = p.idx_len[u];
+    if (L < 0 || L > p.m) {
+      if (tid == 0) flag_unit(p.flags, u, SDA_FLAG_LEN);
+      L = L < 0 ? 0 : p.m;
+    }
+    mf = L;
+  }
+  const int64_t lbase = (int64_t)u * p.m;
+  {
+    int bad = 0;
+    for (int i = tid; i < mf; i += 512) {
+      int j = p.idx[lbase + i];
+      if ((unsigned)j >= (unsigned)p.n) {
+        bad |= SDA_FLAG_IDX_RANGE;
+        j = 0;
+      }
+      if (i > 0 && p.idx[lbase + i - 1] >= j) bad |= SDA_FLAG_IDX_ORDER;
+      s_A[i] = j - i;
+    }
+    if (bad) flag_unit(p.flags, u, bad);
+  }
+  const int64_t n_s = (int64_t)p.n - mf;
+  const int b0 = n_s > 0 ? p.b0 : 0;
+  const uint64_t key = splitmix_at(p.seed, (uint64_t)u);
+  __syncthreads();
+
+  // ---- base draws ---------------------------------------------------------------
+  for (int k = tid; k < b0; k += 512) {
+    const int64_t rank = (int64_t)__umul64hi(splitmix_at(key, (uint64_t)k), (uint64_t)n_s);
+    const int pos = tail_position(s_A, mf, rank);
+    s_bj[k] = pos < p.n ? pos : p.n - 1;  // in range whenever the list is valid
+  }
+
+  const int64_t kvoff = (int64_t)s * p.sb + (int64_t)g * p.sh;
+  const rsrc_t rk = rsrc_of<T>(reinterpret_cast<const T*>(p.K) + kvoff, p.n, p.sn);
+  const rsrc_t rv = rsrc_of<T>(reinterpret_cast<const T*>(p.V) + kvoff, p.n, p.sn);
+  const double scale = (double)p.scale;
+  // query chunk (bf16/fp32 values are exact in fp32 and in fp64)
+  float qr[G][8];
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    load_q8<T>(p.q, ((int64_t)s * p.Hq + (int64_t)g * G + h) * kD + 8 * r16, qr[h]);
+  // fp64 logit of the row chunk in kc for head h (identical on the 16 lanes)
+  auto logit = [&](const RowChunk<T>& kc, double (&x)[G]) {
+    double kd[8];
+    widen8(kc, kd);
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      double a = 0.0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) a = fma((double)qr[h][i], kd[i], a);
+      x[h] = scale * sum16_d(a);
+    }
+  };
+  __syncthreads();  // the draw positions
+
+  // the first batch of base rows (keys and values) in one round trip; the
+  // values stay in registers for the two passes over them
+  RowChunk<T> kc0[NSB], vc0[NSB];
+#pragma unroll
+  for (int k = 0; k < NSB; ++k) {
+    const int r = 4 * (k * kW + w) + sub;
+    const int off = r < b0 ? off_of<T>(s_bj[r], p.sn, r16) : kOOBs;
+    gather(kc0[k], rk, off);
+    gather(vc0[k], rv, off);
+  }
+
+  // ---- fp64 logits and their maximum m_b ----------------------------------------
+  double bmx[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) bmx[h] = -kInf;
+  for (int rb = 0; rb < b0; rb += STEP) {
+    RowChunk<T> kc[NSB];
+#pragma unroll
+    for (int k = 0; k < NSB; ++k) {
+      const int r = rb + 4 * (k * kW + w) + sub;
+      if (rb == 0)
+        kc[k] = kc0[k];
+      else
+        gather(kc[k], rk, r < b0 ? off_of<T>(s_bj[r], p.sn, r16) : kOOBs);
+    }
+#pragma unroll
+    for (int k = 0; k < NSB; ++k) {
+      const int r = rb + 4 * (k * kW + w) + sub;
+      double x[G];
+      logit(kc[k], x);
+      if (r < b0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          bmx[h] = fmax(bmx[h], x[h]);
+          if (r16 == h) s_wb[r][h] = x[h];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const RowPairD a = swap_d<false>(bmx[h]);
+    const double v = fmax(a.even, a.odd);
+    const RowPairD b = swap_d<true>(v);
+    bmx[h] = fmax(b.even, b.odd);
+    if (lane == 0) s_pm[w][h] = bmx[h];
+  }
+  __syncthreads();
+  if (tid < G) {
+    double M = -kInf;
+#pragma unroll
+    for (int ww = 0; ww < kW; ++ww) M = fmax(M, s_pm[ww][tid]);
+    s_mb[tid] = M;
+  }
+  __syncthreads();
+  for (int e = tid; e < b0 * G; e += 512) {
+    const int k = e / G, h = e - k * G;
+    s_wb[k][h] = exp(s_wb[k][h] - s_mb[h]);
+  }
+  __syncthreads();
+
+  // ---- S1 = sum w' and N1 = sum w' v ---------------------------------------------
+  auto base_values = [&](int rb, RowChunk<T> (&vc)[NSB]) {
+#pragma unroll
+    for (int k = 0; k < NSB; ++k) {
+      const int r = rb + 4 * (k * kW + w) + sub;
+      if (rb == 0)
+        vc[k] = vc0[k];
+      else
+        gather(vc[k], rv, r < b0 ? off_of<T>(s_bj[r], p.sn, r16) : kOOBs);
+    }
+  };
+  {
+    double mn[G][8];
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mn[h][i] = 0.0;
+    for (int rb = 0; rb < b0; rb += STEP) {
+      RowChunk<T> vc[NSB];
+      base_values(rb, vc);
+#pragma unroll
+      for (int k = 0; k < NSB; ++k) {
+        const int r = rb + 4 * (k * kW + w) + sub;
+        if (r < b0) {
+          double vd[8];
+          widen8(vc[k], vd);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+#pragma clang fp contract(off)
+            const double e = s_wb[r][h];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) mn[h][i] += e * vd[i];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mn[h][i] = sum_rowgroups_d(mn[h][i]);
+      if (sub == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s_part[w][h][8 * r16 + i] = mn[h][i];
+      }
+    }
+    if (w < G) {  // wave h sums head h's base weights
+      double a = 0.0;
+      for (int k = lane; k < b0; k += 64) a += s_wb[k][w];
+      a = sum_rowgroups_d(sum16_d(a));
+      if (lane == 0) s_S1[w] = a;
+    }
+    __syncthreads();
+    for (int e = tid; e < G * kD; e += 512) {
+      const int h = e / kD, i = e - h * kD;
+      double a = 0.0;
+#pragma unroll
+      for (int ww = 0; ww < kW; ++ww) a += s_part[ww][h][i];
+      s_N1[h][i] = a;
+    }
+    __syncthreads();
+  }
+
+  // ---- centred second moments: TN and VD -------------------------------------------
+  double* rec = p.wbase + (int64_t)u * G * (4 + kD);
+  {
+    double mnr[G][8], sq[G];
+    const double inv = b0 > 0 ? 1.0 / (double)b0 : 0.0;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      sq[h] = 0.0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) mnr[h][i] = s_N1[h][8 * r16 + i] * inv;
+    }
+    for (int rb = 0; rb < b0; rb += STEP) {
+      RowChunk<T> vc[NSB];
+      base_values(rb, vc);
+#pragma unroll
+      for (int k = 0; k < NSB; ++k) {
+        const int r = rb + 4 * (k * kW + w) + sub;
+        if (r < b0) {
+          double vd[8];
+          widen8(vc[k], vd);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+#pragma clang fp contract(off)
+            const double e = s_wb[r][h];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              const double dv = e * vd[i] - mnr[h][i];
+              sq[h] += dv * dv;
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      double v = sum_rowgroups_d(sum16_d(sq[h]));
+      if (lane == 0) s_pm[w][h] = v;
+    }
+    if (w < G) {  // wave h: head h's centred weight sum of squares
+#pragma clang fp contract(off)
+      const double mD = s_S1[w] * inv;
+      double vd2 = 0.0;
+      for (int k = lane; k < b0; k += 64) {
+        const double dv = s_wb[k][w] - mD;
+        vd2 += dv * dv;
+      }
+      vd2 = sum_rowgroups_d(sum16_d(vd2));
+      if (lane == 0) rec[2 * G + w] = vd2;
+    }
+    __syncthreads();
+  }
+  if (tid < G) {
+    double tn = 0.0;
+#pragma unroll
+    for (int ww = 0; ww < kW; ++ww) tn += s_pm[ww][tid];
+    rec[tid] = s_mb[tid];
+    rec[G + tid] = s_S1[tid];
+    rec[3 * G + tid] = tn;
+  }
+  for (int e = tid; e < G * kD; e += 512) rec[4 * G + e] = s_N1[e / kD][e % kD];
+}
+
+// Exact part over a share of I_f: rows [c*per, min(mf, (c+1)*per)) of unit u
+// for workgroup (u, c), an fp64 online softmax per row group (keys and values
+// read together), merged into one record (m, D, N) per head relative to m.
+// The first B*Hkv workgroups of the launch take the base draws instead, one
+// unit each (sampled_base_role).
+template <typename T, int G>
+__global__ __launch_bounds__(512) void sampled_exact_kernel(const AttnParams p) {
+  constexpr int NSB = 2;               // slots (of 4 rows) per wave per batch
+  constexpr int STEP = 4 * kW * NSB;   // rows per batch
+  constexpr double kInf = __builtin_huge_val();
   __shared__ double s_part[kW][G][kD];
+  const int units = p.B * p.Hkv;
+  if ((int)blockIdx.x < units) {
+    sampled_base_role<T, G>(p, blockIdx.x, s_part);
+    return;
+  }
+  const int u = (blockIdx.x - units) / p.splits;
+  const int c = (blockIdx.x - units) - u * p.splits;
+  const int s = u / p.Hkv;
+  const int g = u - s * p.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, sub = lane >> 4;
+
   __shared__ double s_pm[kW][G], s_pd[kW][G];
   __shared__ double s_wf[kW][G], s_wM[G];
 
@@ -231,7 +514,7 @@ __global__ __launch_bounds__(512) void sampled_exact_kernel(const AttnParams p) 
     int j = -1;
     if (lane < 4 * NSB && r < r1) {
       j = p.idx[lbase + r];
-      if ((unsigned)j >= (unsigned)p.n) j = 0;  // flagged by the statistics kernel
+      if ((unsigned)j >= (unsigned)p.n) j = 0;  // flagged by the base-draw workgroup
     }
     return j;
   };
@@ -369,320 +652,75 @@ __global__ __launch_bounds__(512) void sampled_exact_kernel(const AttnParams p) 
   }
 }
 
-template <typename T, int G>
-__global__ __launch_bounds__(512) void sampled_stats_kernel(const AttnParams p) {
-  constexpr int NSB = 2;               // slots (of 4 rows) per wave per batch
-  constexpr int STEP = 4 * kW * NSB;   // rows per batch
+// The budget of each unit (one workgroup per unit): the exact part's
+// records merged at the unit's maximum M = max(M_f, m_b) (fp64 log-sum-exp),
+// the base draws' moments rescaled by e^{m_b - M}, the CLT budget per head
+// (b = max over the group's heads, Lemma 4.2); M, D_f, N_f and b go to the
+// workspace for the draw and merge kernels.
+template <int G>
+__global__ __launch_bounds__(256) void sampled_budget_kernel(const AttnParams p) {
   constexpr double kInf = __builtin_huge_val();
   const int u = blockIdx.x;
-  const int s = u / p.Hkv;
-  const int g = u - s * p.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int r16 = lane & 15, sub = lane >> 4;
-
-  __shared__ int s_A[kSampMaxList];
-  __shared__ int s_bj[kSampMaxB0];
-  __shared__ double s_wb[kSampMaxB0][G];  // base draws: logits, then weights exp(s - M)
-  __shared__ double s_part[kW][G][kD];    // per-wave partial sums
-  __shared__ double s_pm[kW][G];
-  __shared__ double s_M[G], s_Mf[G], s_Df[G], s_mD[G];
-  __shared__ double s_Nf[G][kD], s_mN[G][kD];
-  __shared__ double s_hs[G][4];           // per head: two halves of |Nhat|^2
+  const int tid = threadIdx.x, lane = tid & 63;
+  __shared__ double s_sf[kSampMaxSplits][G];  // the exact-part splits' scale factors to M
+  __shared__ double s_M[G], s_fb[G], s_Df[G];
+  __shared__ double s_hs[G][2];               // per head: two halves of |Nhat|^2
   __shared__ double s_bh[G];
-  __shared__ double s_sf[kSampMaxSplits][G];  // the exact-part splits' scale factors
-  __shared__ int s_b;
 
-  // ---- the deterministic set, as A[i] = I_f[i] - i ---------------------------
   int mf = p.m;
   if (p.idx_len) {
-    int L = p.idx_len[u];
-    if (L < 0 || L > p.m) {
-      if (tid == 0) flag_unit(p.flags, u, SDA_FLAG_LEN);
-      L = L < 0 ? 0 : p.m;
-    }
-    mf = L;
-  }
-  const int64_t lbase = (int64_t)u * p.m;
-  {
-    int bad = 0;
-    for (int i = tid; i < mf; i += 512) {
-      int j = p.idx[lbase + i];
-      if ((unsigned)j >= (unsigned)p.n) {
-        bad |= SDA_FLAG_IDX_RANGE;
-        j = 0;
-      }
-      if (i > 0 && p.idx[lbase + i - 1] >= j) bad |= SDA_FLAG_IDX_ORDER;
-      s_A[i] = j - i;
-    }
-    if (bad) flag_unit(p.flags, u, bad);
+    const int L = p.idx_len[u];
+    mf = L < 0 ? 0 : (L > p.m ? p.m : L);
   }
   const int64_t n_s = (int64_t)p.n - mf;
   const int b0 = n_s > 0 ? p.b0 : 0;
-  const uint64_t key = splitmix_at(p.seed, (uint64_t)u);
-  __syncthreads();
-
-  // ---- base draws ---------------------------------------------------------------
-  for (int k = tid; k < b0; k += 512) {
-    const int64_t rank = (int64_t)__umul64hi(splitmix_at(key, (uint64_t)k), (uint64_t)n_s);
-    const int pos = tail_position(s_A, mf, rank);
-    s_bj[k] = pos < p.n ? pos : p.n - 1;  // in range whenever the list is valid
-  }
-
-  const int64_t kvoff = (int64_t)s * p.sb + (int64_t)g * p.sh;
-  const rsrc_t rk = rsrc_of<T>(reinterpret_cast<const T*>(p.K) + kvoff, p.n, p.sn);
-  const rsrc_t rv = rsrc_of<T>(reinterpret_cast<const T*>(p.V) + kvoff, p.n, p.sn);
-  const double scale = (double)p.scale;
-  // query chunk (bf16/fp32 values are exact in fp32 and in fp64)
-  float qr[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-    load_q8<T>(p.q, ((int64_t)s * p.Hq + (int64_t)g * G + h) * kD + 8 * r16, qr[h]);
-  // fp64 logit of the row chunk in kc for head h (identical on the 16 lanes)
-  auto logit = [&](const RowChunk<T>& kc, double (&x)[G]) {
-    double kd[8];
-    widen8(kc, kd);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      double a = 0.0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) a = fma((double)qr[h][i], kd[i], a);
-      x[h] = scale * sum16_d(a);
-    }
-  };
-
-  // the first batch of base rows (keys and values) goes out now, so that its
-  // latency overlaps the merge of the exact-part records below; the values
-  // stay in registers for the two passes over them
-  __syncthreads();  // the draw positions
-  RowChunk<T> kc0[NSB], vc0[NSB];
-#pragma unroll
-  for (int k = 0; k < NSB; ++k) {
-    const int r = 4 * (k * kW + w) + sub;
-    const int off = r < b0 ? off_of<T>(s_bj[r], p.sn, r16) : kOOBs;
-    gather(kc0[k], rk, off);
-    gather(vc0[k], rv, off);
-  }
-
-  // ---- I_f: merge the exact-part records of the splits (log-sum-exp, fp64) ---
-  {
-    const double* rec = p.wexact + (int64_t)u * p.splits * G * (2 + kD);
-    // the splits' scale factors, once per (split, head)
-    if (tid < G) {
-      double M = -kInf;
-      for (int c = 0; c < p.splits; ++c) M = fmax(M, rec[(int64_t)c * G * (2 + kD) + tid]);
-      s_Mf[tid] = M;
-      for (int c = 0; c < p.splits; ++c) s_sf[c][tid] = rescale_d(rec[(int64_t)c * G * (2 + kD) + tid], M);
-    }
-    __syncthreads();
-    for (int e = tid; e < G * kD; e += 512) {
-      const int h = e / kD, i = e - h * kD;
-      double a = 0.0, d = 0.0;
-      for (int c = 0; c < p.splits; ++c) {
-        const double* rc = rec + (int64_t)c * G * (2 + kD);
-        const double f = s_sf[c][h];
-        a += rc[2 * G + e] * f;
-        d += rc[G + h] * f;
-      }
-      s_Nf[h][i] = a;
-      if (i == 0) s_Df[h] = d;
-    }
+  const double inv = b0 > 0 ? 1.0 / (double)b0 : 0.0;
+  const double* rec = p.wexact + (int64_t)u * p.splits * G * (2 + kD);
+  const double* bs = p.wbase + (int64_t)u * G * (4 + kD);
+  if (tid < G) {
+    double M = bs[tid];
+    for (int c = 0; c < p.splits; ++c) M = fmax(M, rec[(int64_t)c * G * (2 + kD) + tid]);
+    s_M[tid] = M;
+    for (int c = 0; c < p.splits; ++c) s_sf[c][tid] = rescale_d(rec[(int64_t)c * G * (2 + kD) + tid], M);
+    s_fb[tid] = rescale_d(bs[tid], M);
   }
   __syncthreads();
-
-  // ---- base draws: fp64 logits, the shift M, the weights --------------------
-  double bmx[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) bmx[h] = -kInf;
-  for (int rb = 0; rb < b0; rb += STEP) {
-    RowChunk<T> kc[NSB];
-#pragma unroll
-    for (int k = 0; k < NSB; ++k) {
-      const int r = rb + 4 * (k * kW + w) + sub;
-      if (rb == 0)
-        kc[k] = kc0[k];
-      else
-        gather(kc[k], rk, r < b0 ? off_of<T>(s_bj[r], p.sn, r16) : kOOBs);
+  double* st = p.wstat + (int64_t)u * G * (2 + kD);
+  for (int e = tid; e < G * kD; e += 256) {  // a wave covers 64 dims of one head
+#pragma clang fp contract(off)
+    const int h = e / kD, i = e - h * kD;
+    double a = 0.0, d = 0.0;
+    for (int c = 0; c < p.splits; ++c) {
+      const double* rc = rec + (int64_t)c * G * (2 + kD);
+      const double f = s_sf[c][h];
+      a += rc[2 * G + e] * f;
+      d += rc[G + h] * f;
     }
-#pragma unroll
-    for (int k = 0; k < NSB; ++k) {
-      const int r = rb + 4 * (k * kW + w) + sub;
-      double x[G];
-      logit(kc[k], x);
-      if (r < b0) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          bmx[h] = fmax(bmx[h], x[h]);
-          if (r16 == h) s_wb[r][h] = x[h];
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const RowPairD a = swap_d<false>(bmx[h]);
-    const double v = fmax(a.even, a.odd);
-    const RowPairD b = swap_d<true>(v);
-    bmx[h] = fmax(b.even, b.odd);
-    if (lane == 0) s_pm[w][h] = bmx[h];
+    st[2 * G + e] = a;
+    if (i == 0) s_Df[h] = d;
+    const double mN = s_fb[h] * bs[4 * G + e] * inv;
+    const double nh = a + (double)n_s * mN;
+    double nn = nh * nh;
+    nn = sum_rowgroups_d(sum16_d(nn));
+    if (lane == 0) s_hs[h][i >> 6] = nn;
   }
   __syncthreads();
   if (tid < G) {
-    double M = s_Mf[tid];
-#pragma unroll
-    for (int ww = 0; ww < kW; ++ww) M = fmax(M, s_pm[ww][tid]);
-    s_M[tid] = M;
-  }
-  __syncthreads();
-  if (tid < G) s_bh[tid] = rescale_d(s_Mf[tid], s_M[tid]);  // (s_bh reused before the budget)
-  __syncthreads();
-  for (int e = tid; e < G * kD; e += 512) {
-    const int h = e / kD, i = e - h * kD;
-    const double f = s_bh[h];
-    s_Nf[h][i] *= f;
-    if (i == 0) s_Df[h] *= f;
-  }
-  for (int e = tid; e < b0 * G; e += 512) {
-    const int k = e / G, h = e - k * G;
-    s_wb[k][h] = exp(s_wb[k][h] - s_M[h]);
-  }
-  __syncthreads();
-
-  // ---- base draws: means of r^D = w and r^N = w v ------------------------------
-  auto base_values = [&](int rb, RowChunk<T> (&vc)[NSB]) {
-#pragma unroll
-    for (int k = 0; k < NSB; ++k) {
-      const int r = rb + 4 * (k * kW + w) + sub;
-      if (rb == 0)
-        vc[k] = vc0[k];
-      else
-        gather(vc[k], rv, r < b0 ? off_of<T>(s_bj[r], p.sn, r16) : kOOBs);
-    }
-  };
-  {
-    double mn[G][8];
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mn[h][i] = 0.0;
-    for (int rb = 0; rb < b0; rb += STEP) {
-      RowChunk<T> vc[NSB];
-      base_values(rb, vc);
-#pragma unroll
-      for (int k = 0; k < NSB; ++k) {
-        const int r = rb + 4 * (k * kW + w) + sub;
-        if (r < b0) {
-          double vd[8];
-          widen8(vc[k], vd);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
 #pragma clang fp contract(off)
-            const double e = s_wb[r][h];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) mn[h][i] += e * vd[i];
-          }
-        }
-      }
+    const int h = tid;
+    double bh = 0.0;
+    if (b0 > 0) {
+      const double fb = s_fb[h];
+      const double mD = fb * bs[G + h] * inv;
+      const double varD = fb * fb * bs[2 * G + h] / (double)(b0 - 1);
+      const double trN = fb * fb * bs[3 * G + h] / (double)(b0 - 1);
+      const double normN = sqrt(s_hs[h][0] + s_hs[h][1]);
+      const double Dhat = s_Df[h] + (double)n_s * mD;
+      bh = budget_of(p.z, p.eps, (double)n_s, varD, Dhat, trN, normN);
     }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mn[h][i] = sum_rowgroups_d(mn[h][i]);
-      if (sub == 0) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s_part[w][h][8 * r16 + i] = mn[h][i];
-      }
-    }
-    __syncthreads();
-    for (int e = tid; e < G * kD; e += 512) {
-      const int h = e / kD, i = e - h * kD;
-      double a = 0.0;
-#pragma unroll
-      for (int ww = 0; ww < kW; ++ww) a += s_part[ww][h][i];
-      s_mN[h][i] = b0 > 0 ? a / (double)b0 : 0.0;
-    }
-    // wave h sums head h's base weights (lanes strided, then a wave sum)
-    if (w < G) {
-      double a = 0.0;
-      for (int k = lane; k < b0; k += 64) a += s_wb[k][w];
-      a = sum_rowgroups_d(sum16_d(a));
-      if (lane == 0) s_mD[w] = b0 > 0 ? a / (double)b0 : 0.0;
-    }
-    __syncthreads();
-  }
-
-  // ---- base draws: centred second moments --------------------------------------
-  {
-    double mnr[G][8], sq[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      sq[h] = 0.0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) mnr[h][i] = s_mN[h][8 * r16 + i];
-    }
-    for (int rb = 0; rb < b0; rb += STEP) {
-      RowChunk<T> vc[NSB];
-      base_values(rb, vc);
-#pragma unroll
-      for (int k = 0; k < NSB; ++k) {
-        const int r = rb + 4 * (k * kW + w) + sub;
-        if (r < b0) {
-          double vd[8];
-          widen8(vc[k], vd);
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
-#pragma clang fp contract(off)
-            const double e = s_wb[r][h];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              const double dv = e * vd[i] - mnr[h][i];
-              sq[h] += dv * dv;
-            }
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      double v = sum_rowgroups_d(sum16_d(sq[h]));
-      if (lane == 0) s_pm[w][h] = v;
-    }
-    // |N_f + n_s mean(r^N)|^2 per head: 128 dims over two waves' lanes
-    for (int e = tid; e < G * kD; e += 512) {
-#pragma clang fp contract(off)
-      const int h = e / kD, i = e - h * kD;
-      const double nh = s_Nf[h][i] + (double)n_s * s_mN[h][i];
-      double nn = nh * nh;
-      nn = sum_rowgroups_d(sum16_d(nn));
-      if ((tid & 63) == 0) s_hs[h][i >> 6] = nn;
-    }
-    __syncthreads();
-  }
-  // wave h: head h's weight variance (lanes strided, then a wave sum), then
-  // its budget on lane 0
-  if (w < G) {
-#pragma clang fp contract(off)
-    const int h = w;
-    const double mD = s_mD[h];
-    double varD = 0.0;
-    for (int k = lane; k < b0; k += 64) {
-      const double dv = s_wb[k][h] - mD;
-      varD += dv * dv;
-    }
-    varD = sum_rowgroups_d(sum16_d(varD));
-    if (lane == 0) {
-      double bh = 0.0;
-      if (b0 > 0) {
-        varD /= (double)(b0 - 1);
-        double trN = 0.0;
-#pragma unroll
-        for (int ww = 0; ww < kW; ++ww) trN += s_pm[ww][h];
-        trN /= (double)(b0 - 1);
-        const double normN = sqrt(s_hs[h][0] + s_hs[h][1]);
-        const double Dhat = s_Df[h] + (double)n_s * mD;
-        bh = budget_of(p.z, p.eps, (double)n_s, varD, Dhat, trN, normN);
-      }
-      s_bh[h] = bh;
-    }
+    s_bh[h] = bh;
+    st[h] = s_M[h];
+    st[G + h] = s_Df[h];
   }
   __syncthreads();
   if (tid == 0) {
@@ -699,25 +737,16 @@ __global__ __launch_bounds__(512) void sampled_stats_kernel(const AttnParams p) 
         if (b > n_s) b = n_s;
       }
     }
-    s_b = (int)b;
     if (p.b_out) p.b_out[u] = (int32_t)b;
     if (p.bstar_out) p.bstar_out[u] = bstar;
     if (p.samples_out && b > p.b_cap) flag_unit(p.flags, u, SDA_FLAG_SAMPLE_CAP);
+    p.wb[u] = (int32_t)b;
   }
-  __syncthreads();
-
-  // ---- hand the exact part and the budget to the draw workgroups -----------
-  double* st = p.wstat + (int64_t)u * G * (2 + kD);
-  for (int e = tid; e < G * kD; e += 512) st[2 * G + e] = s_Nf[e / kD][e % kD];
-  if (tid < G) {
-    st[tid] = s_M[tid];
-    st[G + tid] = s_Df[tid];
-  }
-  if (tid == 0) p.wb[u] = s_b;
+  (void)kInf;
 }
 
 // the deterministic list as A[i] = I_f[i] - i (entries out of range count as
-// position 0; the statistics kernel flags them)
+// position 0; the base-draw workgroup flags them)
 __device__ __forceinline__ int list_len(const AttnParams& p, int u) {
   int mf = p.m;
   if (p.idx_len) {
@@ -1062,10 +1091,10 @@ __global__ __launch_bounds__(512) void sampled_merge_kernel(const AttnParams p) 
 template <typename T, int G>
 static hipError_t launch_sampled_g(const AttnParams& p, hipStream_t st) {
   const int units = p.B * p.Hkv;
-  hipLaunchKernelGGL((sampled_exact_kernel<T, G>), dim3(units * p.splits), dim3(512), 0, st, p);
+  hipLaunchKernelGGL((sampled_exact_kernel<T, G>), dim3(units * (1 + p.splits)), dim3(512), 0, st, p);
   hipError_t e0 = hipGetLastError();
   if (e0 != hipSuccess) return e0;
-  hipLaunchKernelGGL((sampled_stats_kernel<T, G>), dim3(units), dim3(512), 0, st, p);
+  hipLaunchKernelGGL((sampled_budget_kernel<G>), dim3(units), dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int grid = std::min(kDrawGrid, units * sampled_max_items(p.n));
