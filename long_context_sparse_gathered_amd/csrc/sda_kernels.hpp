@@ -60,6 +60,7 @@ struct AttnParams {
   double* wbase;               // workspace: [units, G*(4 + d)] fp64 moments of the base draws
   int32_t* wb;                 // workspace: [units] sample budget b
   int32_t* wsched;             // workspace: [units + 1] first draw work item of each unit
+  int32_t draw_grid;           // draw workgroups of a full round (set by the launcher)
 
   // split-K
   int32_t splits;              // WGs per unit
@@ -121,7 +122,7 @@ constexpr int kSampMaxB0 = 256;
 constexpr int kDrawChunk = 256;
 constexpr int kDrawRec = 4 + 128;        // floats per (work item, head) partial: m, l, -, -, acc[d]
 constexpr int kSampMaxUnits = 4096;
-constexpr int kDrawGrid = 768;           // draw workgroups (upper bound): three per CU
+constexpr int kDrawGrid = 1024;          // draw workgroups (upper bound); the launch takes one round
 __host__ __device__ inline int sampled_max_items(int n) { return (n + kDrawChunk - 1) / kDrawChunk; }
 // Workgroups per unit that share the exact pass over I_f: with the unit's
 // base-draw workgroup, about 256 in all (the kernel holds one per CU).

@@ -16,10 +16,11 @@
 //                         unit's maximum M, the base moments rescaled to it,
 //                         the budget b; leaves M, D_f, N_f and b in the
 //                         workspace.
-//   sampled_draws_kernel  up to kDrawGrid workgroups share the b fresh draws
-//                         of every unit (work items of kDrawChunk draws):
-//                         each generates its draws' positions, gathers the
-//                         rows and keeps an fp32 online softmax.
+//   sampled_draws_kernel  one round of workgroups (as many as the chip
+//                         holds) shares the b fresh draws of every unit
+//                         (work items of kDrawChunk draws): each generates
+//                         its draws' positions, gathers the rows and keeps
+//                         an fp32 online softmax.
 //   sampled_merge_kernel  one workgroup per unit: log-sum-exp merge of the
 //                         draw partials, then num = N_f + (n_s/b) N_dyn and
 //                         den = D_f + (n_s/b) D_dyn in fp64.
@@ -1000,7 +1001,7 @@ __global__ __launch_bounds__(512) void sampled_merge_kernel(const AttnParams p) 
   const int b = p.wb[u];
   const int maxc = sampled_max_items(p.n);
   const int S = p.wsched[u], nc = p.wsched[u + 1] - S, total = p.wsched[units];
-  const int grid = min(kDrawGrid, units * maxc);
+  const int grid = min(p.draw_grid, units * maxc);
   const int per = (total + grid - 1) / grid;
   const double* st = p.wstat + (int64_t)u * G * (2 + kD);
   const float* rec = p.part + (int64_t)u * maxc * G * kDrawRec;
@@ -1097,11 +1098,23 @@ static hipError_t launch_sampled_g(const AttnParams& p, hipStream_t st) {
   hipLaunchKernelGGL((sampled_budget_kernel<G>), dim3(units), dim3(256), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int grid = std::min(kDrawGrid, units * sampled_max_items(p.n));
-  hipLaunchKernelGGL((sampled_draws_kernel<T, G>), dim3(grid), dim3(256), 0, st, p);
+  // one round of draw workgroups: as many as the chip holds at once
+  static const int resident = [] {
+    int per_cu = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sampled_draws_kernel<T, G>, 256, 0) != hipSuccess ||
+        hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    return per_cu * cus;
+  }();
+  if (resident <= 0) return hipErrorInvalidDeviceFunction;
+  AttnParams q = p;
+  q.draw_grid = std::min(kDrawGrid, resident);
+  const int grid = std::min(q.draw_grid, units * sampled_max_items(p.n));
+  hipLaunchKernelGGL((sampled_draws_kernel<T, G>), dim3(grid), dim3(256), 0, st, q);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((sampled_merge_kernel<G>), dim3(units), dim3(512), 0, st, p);
+  hipLaunchKernelGGL((sampled_merge_kernel<G>), dim3(units), dim3(512), 0, st, q);
   return hipGetLastError();
 }
 
