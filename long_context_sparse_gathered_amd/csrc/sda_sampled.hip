@@ -197,7 +197,7 @@ __device__ double budget_of(double z, double eps, double n_s, double varD, doubl
 // in wbase: m_b, S1, VD, TN at [h], [G + h], [2G + h], [3G + h], N1 at
 // [4G + h*d, 4G + (h+1)*d).
 template <typename T, int G>
-__device__ void sampled_base_role(const AttnParams& p, int u, double (&s_part)[kW][G][kD]) {
+__device__ void sampled_base_role(const AttnParams& p, int u, double (&s_part)[kW][G][kD], int (&s_A)[kSampMaxList]) {
   constexpr int NSB = 2;               // slots (of 4 rows) per wave per batch
   constexpr int STEP = 4 * kW * NSB;   // rows per batch
   constexpr double kInf = __builtin_huge_val();
@@ -206,7 +206,6 @@ __device__ void sampled_base_role(const AttnParams& p, int u, double (&s_part)[k
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int r16 = lane & 15, sub = lane >> 4;
 
-  __shared__ int s_A[kSampMaxList];
   __shared__ int s_bj[kSampMaxB0];
   __shared__ double s_wb[kSampMaxB0][G];  // base draws: logits, then weights e^{s - m_b}
   __shared__ double s_pm[kW][G];
@@ -468,9 +467,10 @@ __global__ __launch_bounds__(512) void sampled_exact_kernel(const AttnParams p) 
   constexpr int STEP = 4 * kW * NSB;   // rows per batch
   constexpr double kInf = __builtin_huge_val();
   __shared__ double s_part[kW][G][kD];
+  __shared__ int s_list[kSampMaxList];  // the base role's A[i]; the exact role's share of I_f
   const int units = p.B * p.Hkv;
   if ((int)blockIdx.x < units) {
-    sampled_base_role<T, G>(p, blockIdx.x, s_part);
+    sampled_base_role<T, G>(p, blockIdx.x, s_part, s_list);
     return;
   }
   const int u = (blockIdx.x - units) / p.splits;
@@ -508,16 +508,18 @@ __global__ __launch_bounds__(512) void sampled_exact_kernel(const AttnParams p) 
 #pragma unroll
     for (int i = 0; i < 8; ++i) Nf[h][i] = 0.0;
   }
+  // this workgroup's share of the list, staged in LDS at once (entries out
+  // of range count as row 0; the base-draw workgroup flags them)
+  for (int r = r0 + tid; r < r1; r += 512) {
+    const int j = p.idx[lbase + r];
+    s_list[r - r0] = (unsigned)j < (unsigned)p.n ? j : 0;
+  }
+  __syncthreads();
   // list entries of the next batch: lane l < 4*NSB holds row rb + 4*((l>>2)*kW + w) + (l&3)
   auto lane_row = [&](int rb) { return rb + 4 * ((lane >> 2) * kW + w) + (lane & 3); };
   auto list_at = [&](int rb) {
     const int r = lane_row(rb);
-    int j = -1;
-    if (lane < 4 * NSB && r < r1) {
-      j = p.idx[lbase + r];
-      if ((unsigned)j >= (unsigned)p.n) j = 0;  // flagged by the base-draw workgroup
-    }
-    return j;
+    return lane < 4 * NSB && r < r1 ? s_list[r - r0] : -1;
   };
   auto issue = [&](int lj, RowChunk<T> (&kc)[NSB], RowChunk<T> (&vc)[NSB]) {
 #pragma unroll
@@ -552,14 +554,25 @@ __global__ __launch_bounds__(512) void sampled_exact_kernel(const AttnParams p) 
         bm[h] = fmax(bm[h], x[k][h]);
       }
     }
+    {
+      // a new maximum rescales the running sums: lane r16 < G takes the one
+      // exponential of head r16 and the row group shares it (1 where the
+      // maximum stays)
+      double mo = 0.0, bo = 0.0;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      if (bm[h] > mh[h]) {
-        const double f = rescale_d(mh[h], bm[h]);
+      for (int h = 0; h < G; ++h)
+        if (r16 == h) {
+          mo = mh[h];
+          bo = bm[h];
+        }
+      const double fo = bo > mo ? rescale_d(mo, bo) : 1.0;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const double f = row_bcast(fo, h);
         Df[h] *= f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) Nf[h][i] *= f;
-        mh[h] = bm[h];
+        mh[h] = fmax(mh[h], bm[h]);
       }
     }
 #pragma unroll
@@ -577,11 +590,10 @@ __global__ __launch_bounds__(512) void sampled_exact_kernel(const AttnParams p) 
       widen8(vc[k], vd);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-#pragma clang fp contract(off)
         const double e = row_bcast(eo, h);
         Df[h] += e;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) Nf[h][i] += e * vd[i];
+        for (int i = 0; i < 8; ++i) Nf[h][i] = fma(e, vd[i], Nf[h][i]);
       }
     }
 #pragma unroll
