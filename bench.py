@@ -403,6 +403,39 @@ def gather_ceiling(a, copies, gstate, idx, w, waves, parts):
             "total_gbs": round((by + st) / (ms * 1e-3) / 1e9, 1)}
 
 
+def draws_gather_ceiling(a, copies, b_sum, slices=32, waves=8):
+    """A plain gather of as many uniformly random K/V rows as the sampled
+    tail's fresh draws read (b_sum row pairs spread over the whole cache), no
+    arithmetic: each (sequence, KV head) range of n rows is cut into `slices`
+    slices of n/slices rows, and every slice is a unit of the gather aid with
+    the same number of random rows (one workgroup of `waves` waves each)."""
+    import numpy as np
+    import torch
+
+    from long_context_sparse_gathered_amd import sda
+    K0 = copies[0][0]
+    B, Hkv, n, d = K0.shape
+    if not K0.is_contiguous() or n % slices:
+        return None
+    H2, n2 = Hkv * slices, n // slices
+    units = B * H2
+    m = -(-b_sum // units)
+    if m > waves * 4 * (12 if waves == 16 else 24):
+        return None
+    rng = np.random.default_rng(7)
+    idx = torch.from_numpy(rng.integers(0, n2, size=(B, H2, m), dtype=np.int32)).to(K0.device)
+    views = [(K.view(B, H2, n2, d), V.view(B, H2, n2, d)) for K, V in copies]
+    chk = torch.zeros(units * waves, dtype=torch.int32, device=K0.device)
+
+    def gstep(i):
+        Kv, Vv = views[i % len(views)]
+        sda.gather_rows(Kv, Vv, idx, waves=waves, parts=1, checksum=chk)
+    ms, _ = time_steps(gstep, 50, 5, graph=not a.no_graph, repeats=a.repeats)
+    by = units * m * 2 * d * K0.element_size()
+    return {"shape": f"{units} slices of {n2} rows, {m} random rows each, {waves} waves x 1 workgroup per slice",
+            "us": round(ms * 1e3, 3), "gathered_gbs": round(by / (ms * 1e-3) / 1e9, 1)}
+
+
 def measure_three_percent(a, dev, w, c, q, copies, out, lse, dense_ms):
     """The headline shape at 3% read (984 listed rows per KV head): the proxy
     tail on the long-list kernel, over the same KV-cache copies."""
@@ -540,6 +573,7 @@ def measure_rows(a, dev):
         ms, gathered, by, dms, m=w.m, mean_budget_b=round(b_sum / units, 1),
         repeats_us=[round(x * 1e3, 3) for x in per], max_rel_err=err, units_checked=units,
         budget_bit_exact=b_exact, draws_bit_exact=draws_exact, budget_ties=ties,
+        draws_gather_ceiling=draws_gather_ceiling(a, copies, b_sum),
         note="gathered = I_f, the b0 base draws and the b fresh draws (K and V rows)")
     B1 = 2
     name, rec = oracle_path(
