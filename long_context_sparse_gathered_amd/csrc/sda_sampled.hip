@@ -34,6 +34,8 @@
 // published 64-bit finaliser; Steele, Lea & Flood, OOPSLA 2014).  The draw
 // picks unread rank floor(x * n_s / 2^64), and rank r maps to the position
 // r + #{i : I_f[i] - i <= r} (binary search).
+#include <type_traits>
+
 #include "sda_device.hpp"
 #include "sda_kernels.hpp"
 
@@ -42,6 +44,7 @@ namespace sda {
 namespace {
 
 constexpr int kW = 8;  // waves per workgroup
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
 constexpr int kOOBs = kMaxUnitBytes;
 
@@ -770,10 +773,11 @@ __device__ __forceinline__ int list_len(const AttnParams& p, int u) {
 }
 
 // Exclusive prefix over the units of their work-item counts ceil(b_u / chunk)
-// into pref[0..units] (pref[units] = total), by a 256-thread workgroup.
+// into pref[0..units] (pref[units] = total), by a workgroup of NT threads.
+template <int NT>
 __device__ void work_item_prefix(const int32_t* wb, int units, int* pref, int* scratch) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int per = (units + 255) / 256;
+  const int per = (units + NT - 1) / NT;
   const int lo = min(units, tid * per), hi = min(units, lo + per);
   int run = 0;
   for (int u = lo; u < hi; ++u) run += (wb[u] + kDrawChunk - 1) / kDrawChunk;
@@ -793,13 +797,14 @@ __device__ void work_item_prefix(const int32_t* wb, int units, int* pref, int* s
     pref[u] = at;
     at += (wb[u] + kDrawChunk - 1) / kDrawChunk;
   }
-  if (tid == 255) pref[units] = base + v;
+  if (tid == NT - 1) pref[units] = base + v;
   __syncthreads();
 }
 
 template <typename T, int G>
-__global__ __launch_bounds__(256, (G * sizeof(T) >= 16 ? 1 : 3)) void sampled_draws_kernel(const AttnParams p) {
-  constexpr int W = 4;              // waves
+__global__ __launch_bounds__(512) void sampled_draws_kernel(const AttnParams p) {
+  constexpr int W = 8;              // waves
+  constexpr int NT = 64 * W;        // threads
   constexpr int NSB = 4;            // slots (of 4 rows) per wave per batch
   constexpr int STEP = 4 * W * NSB; // draws per batch
   const int units = p.B * p.Hkv;
@@ -807,15 +812,19 @@ __global__ __launch_bounds__(256, (G * sizeof(T) >= 16 ? 1 : 3)) void sampled_dr
   const int r16 = lane & 15, sub = lane >> 4;
 
   __shared__ int s_pref[kSampMaxUnits + 1];
-  __shared__ int s_A[kSampMaxList];
   __shared__ int s_scan[W];
   __shared__ float s_m[W][G], s_l[W][G];
-  __shared__ __attribute__((aligned(16))) float s_acc[W][G][kD];
+  // the list A[i] during a segment's draws, then the waves' partial sums:
+  // one array for both keeps the workgroup within 40 KB of LDS (four per CU)
+  constexpr int kBufBytes = kSampMaxList * 4 > W * G * kD * 4 ? kSampMaxList * 4 : W * G * kD * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char s_buf[kBufBytes];
+  int* const s_A = reinterpret_cast<int*>(s_buf);
+  auto s_acc = reinterpret_cast<float (*)[G][kD]>(s_buf);
 
-  work_item_prefix(p.wb, units, s_pref, s_scan);
+  work_item_prefix<NT>(p.wb, units, s_pref, s_scan);
   const int total = s_pref[units];
   if (blockIdx.x == 0)
-    for (int i = tid; i <= units; i += 256) p.wsched[i] = s_pref[i];
+    for (int i = tid; i <= units; i += NT) p.wsched[i] = s_pref[i];
   const int per = (total + (int)gridDim.x - 1) / (int)gridDim.x;
   int wi = blockIdx.x * per;
   const int wend = min(total, wi + per);
@@ -841,7 +850,7 @@ __global__ __launch_bounds__(256, (G * sizeof(T) >= 16 ? 1 : 3)) void sampled_dr
     const int mf = list_len(p, u);
     const int64_t lbase = (int64_t)u * p.m;
     __syncthreads();  // the previous segment's readers of s_A and s_acc are done
-    for (int i = tid; i < mf; i += 256) {
+    for (int i = tid; i < mf; i += NT) {
       int j = p.idx[lbase + i];
       if ((unsigned)j >= (unsigned)p.n) j = 0;
       s_A[i] = j - i;
@@ -867,12 +876,27 @@ __global__ __launch_bounds__(256, (G * sizeof(T) >= 16 ? 1 : 3)) void sampled_dr
     const int64_t kvoff = (int64_t)s * p.sb + (int64_t)g * p.sh;
     const rsrc_t rk = rsrc_of<T>(reinterpret_cast<const T*>(p.K) + kvoff, p.n, p.sn);
     const rsrc_t rv = rsrc_of<T>(reinterpret_cast<const T*>(p.V) + kvoff, p.n, p.sn);
+    // the query: bf16 rows keep it as bf16 pairs for the two-wide bf16 dot
+    // product (exact products, fp32 sums; the scale follows the sum), fp32
+    // rows as fp32 with the scale folded in
+    constexpr bool kBf = std::is_same<T, bf16_t>::value;
     float qf[G][8];
+    uint32_t qw[G][4];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      load_q8<T>(p.q, ((int64_t)s * p.Hq + (int64_t)g * G + h) * kD + 8 * r16, qf[h]);
+      const int64_t qoff = ((int64_t)s * p.Hq + (int64_t)g * G + h) * kD + 8 * r16;
+      if constexpr (kBf) {
+        RowChunk<bf16_t> c;
+        c.load_cached(reinterpret_cast<const bf16_t*>(p.q) + qoff);
+        qw[h][0] = c.raw.x;
+        qw[h][1] = c.raw.y;
+        qw[h][2] = c.raw.z;
+        qw[h][3] = c.raw.w;
+      } else {
+        load_q8<T>(p.q, qoff, qf[h]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) qf[h][i] *= p.qscale;
+        for (int i = 0; i < 8; ++i) qf[h][i] *= p.qscale;
+      }
     }
     float m[G], l[G], acc[G][8];
 #pragma unroll
@@ -911,14 +935,23 @@ __global__ __launch_bounds__(256, (G * sizeof(T) >= 16 ? 1 : 3)) void sampled_dr
       for (int h = 0; h < G; ++h) bm[h] = kNegInf;
 #pragma unroll
       for (int k = 0; k < NSB; ++k) {
-        float kf[8];
-        kc[k].unpack(kf);
 #pragma unroll
         for (int h = 0; h < G; ++h) {
           float a = 0.f;
+          if constexpr (kBf) {
+            const uint32_t kw[4] = {kc[k].raw.x, kc[k].raw.y, kc[k].raw.z, kc[k].raw.w};
 #pragma unroll
-          for (int i = 0; i < 8; ++i) a = fmaf(qf[h][i], kf[i], a);
-          a = sum16(a);
+            for (int i = 0; i < 4; ++i)
+              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[h][i]),
+                                                  __builtin_bit_cast(bf16x2_t, kw[i]), a, false);
+            a = sum16(a) * p.qscale;
+          } else {
+            float kf[8];
+            kc[k].unpack(kf);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a = fmaf(qf[h][i], kf[i], a);
+            a = sum16(a);
+          }
           x[k][h] = ok[k] ? a : kNegInf;
           bm[h] = fmaxf(bm[h], x[k][h]);
         }
@@ -947,6 +980,7 @@ __global__ __launch_bounds__(256, (G * sizeof(T) >= 16 ? 1 : 3)) void sampled_dr
     }
 
     // ---- merge the four row groups, then the waves; one record per head ----
+    __syncthreads();  // every wave is done with A[i]: its LDS takes the partial sums
 #pragma unroll
     for (int h = 0; h < G; ++h) {
 #pragma unroll
@@ -974,7 +1008,7 @@ __global__ __launch_bounds__(256, (G * sizeof(T) >= 16 ? 1 : 3)) void sampled_dr
     }
     __syncthreads();
     float* rec = p.part + ((int64_t)u * maxc + c) * G * kDrawRec;
-    for (int e = tid; e < G * kD; e += 256) {
+    for (int e = tid; e < G * kD; e += NT) {
       const int h = e / kD, dim = e - h * kD;
       float M = kNegInf;
 #pragma unroll
@@ -1113,7 +1147,7 @@ static hipError_t launch_sampled_g(const AttnParams& p, hipStream_t st) {
   // one round of draw workgroups: as many as the chip holds at once
   static const int resident = [] {
     int per_cu = 0, dev = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sampled_draws_kernel<T, G>, 256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sampled_draws_kernel<T, G>, 512, 0) != hipSuccess ||
         hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return 0;
@@ -1123,7 +1157,7 @@ static hipError_t launch_sampled_g(const AttnParams& p, hipStream_t st) {
   AttnParams q = p;
   q.draw_grid = std::min(kDrawGrid, resident);
   const int grid = std::min(q.draw_grid, units * sampled_max_items(p.n));
-  hipLaunchKernelGGL((sampled_draws_kernel<T, G>), dim3(grid), dim3(256), 0, st, q);
+  hipLaunchKernelGGL((sampled_draws_kernel<T, G>), dim3(grid), dim3(512), 0, st, q);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((sampled_merge_kernel<G>), dim3(units), dim3(512), 0, st, q);
