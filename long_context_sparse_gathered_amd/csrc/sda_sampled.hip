@@ -675,9 +675,11 @@ __global__ __launch_bounds__(512) void sampled_exact_kernel(const AttnParams p) 
 // workspace for the draw and merge kernels.
 template <int G>
 __global__ __launch_bounds__(256) void sampled_budget_kernel(const AttnParams p) {
-  constexpr double kInf = __builtin_huge_val();
+  constexpr int NE = (G * kD + 255) / 256;  // vector elements per thread
   const int u = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
+  // per head: the splits' (M_c, D_c), then the base draws' (m_b, S1, VD, TN)
+  __shared__ double s_sc[2 * kSampMaxSplits + 4][G];
   __shared__ double s_sf[kSampMaxSplits][G];  // the exact-part splits' scale factors to M
   __shared__ double s_M[G], s_fb[G], s_Df[G];
   __shared__ double s_hs[G][2];               // per head: two halves of |Nhat|^2
@@ -691,34 +693,59 @@ __global__ __launch_bounds__(256) void sampled_budget_kernel(const AttnParams p)
   const int64_t n_s = (int64_t)p.n - mf;
   const int b0 = n_s > 0 ? p.b0 : 0;
   const double inv = b0 > 0 ? 1.0 / (double)b0 : 0.0;
-  const double* rec = p.wexact + (int64_t)u * p.splits * G * (2 + kD);
+  const int splits = p.splits;
+  const double* rec = p.wexact + (int64_t)u * splits * G * (2 + kD);
   const double* bs = p.wbase + (int64_t)u * G * (4 + kD);
+
+  // every load in one round trip: the scalars to LDS, the vectors to registers
+  if (tid < (2 * splits + 4) * G) {
+    const int k = tid / G, h = tid - k * G;
+    s_sc[k][h] = k < 2 * splits ? rec[(int64_t)(k >> 1) * G * (2 + kD) + (k & 1) * G + h]
+                                : bs[(k - 2 * splits) * G + h];
+  }
+  double nv[NE][kSampMaxSplits], bv[NE];
+#pragma unroll
+  for (int j = 0; j < NE; ++j) {
+    const int e = tid + 256 * j;
+    bv[j] = e < G * kD ? bs[4 * G + e] : 0.0;
+#pragma unroll
+    for (int c = 0; c < kSampMaxSplits; ++c)
+      nv[j][c] = e < G * kD && c < splits ? rec[(int64_t)c * G * (2 + kD) + 2 * G + e] : 0.0;
+  }
+  __syncthreads();
   if (tid < G) {
-    double M = bs[tid];
-    for (int c = 0; c < p.splits; ++c) M = fmax(M, rec[(int64_t)c * G * (2 + kD) + tid]);
+    const double mb = s_sc[2 * splits][tid];
+    double M = mb;
+    for (int c = 0; c < splits; ++c) M = fmax(M, s_sc[2 * c][tid]);
     s_M[tid] = M;
-    for (int c = 0; c < p.splits; ++c) s_sf[c][tid] = rescale_d(rec[(int64_t)c * G * (2 + kD) + tid], M);
-    s_fb[tid] = rescale_d(bs[tid], M);
+    double d = 0.0;
+    for (int c = 0; c < splits; ++c) {
+      const double f = rescale_d(s_sc[2 * c][tid], M);
+      s_sf[c][tid] = f;
+      d += s_sc[2 * c + 1][tid] * f;
+    }
+    s_Df[tid] = d;
+    s_fb[tid] = rescale_d(mb, M);
   }
   __syncthreads();
   double* st = p.wstat + (int64_t)u * G * (2 + kD);
-  for (int e = tid; e < G * kD; e += 256) {  // a wave covers 64 dims of one head
+#pragma unroll
+  for (int j = 0; j < NE; ++j) {
+    const int e = tid + 256 * j;
+    if (e < G * kD) {  // a wave covers 64 dims of one head
 #pragma clang fp contract(off)
-    const int h = e / kD, i = e - h * kD;
-    double a = 0.0, d = 0.0;
-    for (int c = 0; c < p.splits; ++c) {
-      const double* rc = rec + (int64_t)c * G * (2 + kD);
-      const double f = s_sf[c][h];
-      a += rc[2 * G + e] * f;
-      d += rc[G + h] * f;
+      const int h = e / kD, i = e - h * kD;
+      double a = 0.0;
+#pragma unroll
+      for (int c = 0; c < kSampMaxSplits; ++c)
+        if (c < splits) a += nv[j][c] * s_sf[c][h];
+      st[2 * G + e] = a;
+      const double mN = s_fb[h] * bv[j] * inv;
+      const double nh = a + (double)n_s * mN;
+      double nn = nh * nh;
+      nn = sum_rowgroups_d(sum16_d(nn));
+      if (lane == 0) s_hs[h][i >> 6] = nn;
     }
-    st[2 * G + e] = a;
-    if (i == 0) s_Df[h] = d;
-    const double mN = s_fb[h] * bs[4 * G + e] * inv;
-    const double nh = a + (double)n_s * mN;
-    double nn = nh * nh;
-    nn = sum_rowgroups_d(sum16_d(nn));
-    if (lane == 0) s_hs[h][i >> 6] = nn;
   }
   __syncthreads();
   if (tid < G) {
@@ -727,9 +754,9 @@ __global__ __launch_bounds__(256) void sampled_budget_kernel(const AttnParams p)
     double bh = 0.0;
     if (b0 > 0) {
       const double fb = s_fb[h];
-      const double mD = fb * bs[G + h] * inv;
-      const double varD = fb * fb * bs[2 * G + h] / (double)(b0 - 1);
-      const double trN = fb * fb * bs[3 * G + h] / (double)(b0 - 1);
+      const double mD = fb * s_sc[2 * splits + 1][h] * inv;
+      const double varD = fb * fb * s_sc[2 * splits + 2][h] / (double)(b0 - 1);
+      const double trN = fb * fb * s_sc[2 * splits + 3][h] / (double)(b0 - 1);
       const double normN = sqrt(s_hs[h][0] + s_hs[h][1]);
       const double Dhat = s_Df[h] + (double)n_s * mD;
       bh = budget_of(p.z, p.eps, (double)n_s, varD, Dhat, trN, normN);
@@ -758,7 +785,6 @@ __global__ __launch_bounds__(256) void sampled_budget_kernel(const AttnParams p)
     if (p.samples_out && b > p.b_cap) flag_unit(p.flags, u, SDA_FLAG_SAMPLE_CAP);
     p.wb[u] = (int32_t)b;
   }
-  (void)kInf;
 }
 
 // the deterministic list as A[i] = I_f[i] - i (entries out of range count as
@@ -1036,11 +1062,12 @@ __global__ __launch_bounds__(512) void sampled_draws_kernel(const AttnParams p) 
 // segment: item S, and every item k*per in (S, S + nc).
 template <int G>
 __global__ __launch_bounds__(512) void sampled_merge_kernel(const AttnParams p) {
-  constexpr int kBlk = 128;  // records staged per round
+  constexpr int kBlk = 256;  // records staged per round
+  constexpr int NE = (G * kD + 511) / 512;
   const int u = blockIdx.x;
   const int s = u / p.Hkv;
   const int g = u - s * p.Hkv;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int units = p.B * p.Hkv;
   const int mf = list_len(p, u);
   const int64_t n_s = (int64_t)p.n - mf;
@@ -1060,41 +1087,73 @@ __global__ __launch_bounds__(512) void sampled_merge_kernel(const AttnParams p) 
   if (nc > 0) nrec = 1 + max(0, (S + nc - 1) / per - k0 + 1);
   auto rc = [&](int r) { return r == 0 ? 0 : (k0 + r - 1) * per - S; };
 
-  __shared__ float s_red[512];
+  __shared__ float s_pm[8][G];     // per wave: partial maxima
   __shared__ float s_md[G];
   __shared__ int s_c[kBlk];
-  __shared__ float s_f[kBlk][G], s_rl[kBlk][G];
+  __shared__ float s_rm[kBlk][G], s_rl[kBlk][G], s_f[kBlk][G];
 
-  // maximum of the record maxima per head (thread tid serves head tid % G)
+  // the exact part's values for this thread's outputs, loaded up front
+  double xM[NE], xD[NE], xN[NE];
+#pragma unroll
+  for (int k = 0; k < NE; ++k) {
+    const int e = tid + 512 * k;
+    const int h = (e < G * kD ? e : 0) / kD;
+    xM[k] = st[h];
+    xD[k] = st[G + h];
+    xN[k] = e < G * kD ? st[2 * G + e] : 0.0;
+  }
+
+  // maximum of the record maxima per head; the first round's (m, l) stay in LDS
   {
     float mx = kNegInf;
-    for (int e = tid; e < nrec * G; e += 512) mx = fmaxf(mx, rec[((int64_t)rc(e / G) * G + e % G) * kDrawRec]);
-    s_red[tid] = mx;
-    __syncthreads();
-    for (int span = 256; span >= G; span >>= 1) {
-      if (tid < span) s_red[tid] = fmaxf(s_red[tid], s_red[tid + span]);
-      __syncthreads();
+    for (int e = tid; e < nrec * G; e += 512) {
+      const int r = e / G, h = e - r * G;
+      const float* rh = rec + ((int64_t)rc(r) * G + h) * kDrawRec;
+      const float m = rh[0];
+      if (r < kBlk) {
+        s_rm[r][h] = m;
+        s_rl[r][h] = rh[1];
+        if (h == 0) s_c[r] = rc(r);
+      }
+      mx = fmaxf(mx, m);
     }
-    if (tid < G) s_md[tid] = s_red[tid];
+    // 512 is a multiple of G: thread tid serves head tid % G throughout
+    for (int d = G; d < 64; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+    if (lane < G) s_pm[w][lane] = mx;
+    __syncthreads();
+    if (tid < G) {
+      float m = kNegInf;
+#pragma unroll
+      for (int ww = 0; ww < 8; ++ww) m = fmaxf(m, s_pm[ww][tid]);
+      s_md[tid] = m;
+    }
     __syncthreads();
   }
 
-  float a[(G * kD + 511) / 512], L[(G * kD + 511) / 512];
+  float a[NE], L[NE];
 #pragma unroll
-  for (int k = 0; k < (G * kD + 511) / 512; ++k) a[k] = L[k] = 0.f;
+  for (int k = 0; k < NE; ++k) a[k] = L[k] = 0.f;
   for (int r0 = 0; r0 < nrec; r0 += kBlk) {
     const int nb = min(kBlk, nrec - r0);
     for (int e = tid; e < nb * G; e += 512) {
       const int r = e / G, h = e - r * G;
-      const int c = rc(r0 + r);
-      const float* rh = rec + ((int64_t)c * G + h) * kDrawRec;
-      if (h == 0) s_c[r] = c;
-      s_f[r][h] = rescale(rh[0], s_md[h]);
-      s_rl[r][h] = rh[1];
+      float m, l;
+      if (r0 == 0) {
+        m = s_rm[r][h];
+        l = s_rl[r][h];
+      } else {
+        const int c = rc(r0 + r);
+        const float* rh = rec + ((int64_t)c * G + h) * kDrawRec;
+        m = rh[0];
+        l = rh[1];
+        if (h == 0) s_c[r] = c;
+      }
+      s_f[r][h] = rescale(m, s_md[h]);
+      if (r0 != 0) s_rl[r][h] = l;
     }
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < (G * kD + 511) / 512; ++k) {
+    for (int k = 0; k < NE; ++k) {
       const int e = tid + 512 * k;
       if (e < G * kD) {
         const int h = e / kD, dim = e - h * kD;
@@ -1119,15 +1178,15 @@ __global__ __launch_bounds__(512) void sampled_merge_kernel(const AttnParams p) 
   }
 
 #pragma unroll
-  for (int k = 0; k < (G * kD + 511) / 512; ++k) {
+  for (int k = 0; k < NE; ++k) {
     const int e = tid + 512 * k;
     if (e < G * kD) {
       const int h = e / kD, dim = e - h * kD;
       // back to the fp64 shift M (natural units): exp(s - M) = 2^(x' - M log2 e)
-      const double M = st[h];
+      const double M = xM[k];
       const double sc = (L[k] > 0.f) ? exp2((double)s_md[h] - M * 1.4426950408889634) : 0.0;
-      const double num = st[2 * G + e] + fw * (double)a[k] * sc;
-      const double den = st[G + h] + fw * (double)L[k] * sc;
+      const double num = xN[k] + fw * (double)a[k] * sc;
+      const double den = xD[k] + fw * (double)L[k] * sc;
       const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
       p.out[qh * kD + dim] = den > 0.0 ? (float)(num / den) : 0.f;
       if (dim == 0 && p.lse) p.lse[qh] = den > 0.0 ? (float)(M + log(den)) : kNegInf;

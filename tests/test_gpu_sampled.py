@@ -112,3 +112,13 @@ def test_sampled_full_size_b8_n64k(orc):
             k = min(int(ref["b"][s, g]), 4096)
             np.testing.assert_array_equal(samples[s, g, :k], ref["samples"][s, g, :k])
     assert rel_err(got, ref["out"]) <= 2e-3
+
+
+def test_sampled_budget_reaches_whole_tail_one_unit(orc):
+    """One unit at 128K whose budget is the whole unread tail (b* far above
+    n_s, so b = n_s = 130,840 draws): 512 work items over the draw grid, one
+    record per item, so the merge stages its records in two rounds."""
+    w = synth.WORKLOADS["sampled_bf16_b8_n64k"].replace(B=1, Hq=4, Hkv=1, n=131072, n_top=100, eps=0.004)
+    c = synth.make_case(w)
+    tail, _, ref = _check(orc, c, w, 11, b_cap=1024, tol=2e-3)
+    assert int(tail.b.cpu().numpy()[0, 0]) == w.n - w.m
