@@ -67,11 +67,15 @@ __device__ __forceinline__ int tail_position(const int* A, int mf, int64_t rank)
   return (int)(rank + lo);
 }
 
+// Lane moves within 16-lane rows whose every lane reads a lane of its own
+// row (permutations and row broadcasts): no lane keeps an old value, so the
+// moves take none (an old operand costs two register initialisations per
+// move).
 template <int CTRL>
 __device__ __forceinline__ double dpp_d(double v) {
   const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), CTRL, 0xF, 0xF, false);
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
@@ -117,8 +121,8 @@ __device__ __forceinline__ double rescale_d(double m, double M) {
 template <int H>
 __device__ __forceinline__ double row_bcast_d(double v) {
   const uint64_t b = __builtin_bit_cast(uint64_t, v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, 0x150 + H, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), 0x150 + H, 0xF, 0xF, false);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)b, 0x150 + H, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), 0x150 + H, 0xF, 0xF, false);
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 __device__ __forceinline__ double row_bcast(double v, int h) {  // h folds to a constant when unrolled
