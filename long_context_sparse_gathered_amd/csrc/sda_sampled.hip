@@ -547,9 +547,11 @@ __global__ __launch_bounds__(512) void sampled_exact_kernel(const AttnParams p) 
     double x[NSB][G], bm[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) bm[h] = -kInf;
+    // every slot's logits unconditionally (a slot past the list holds zero
+    // rows), so that the NSB*G dot products and their row sums interleave;
+    // the empty slots are masked afterwards
 #pragma unroll
     for (int k = 0; k < NSB; ++k) {
-      const bool ok = __shfl(lj, 4 * k + sub, 64) >= 0;
       double kd[8];
       widen8(kc[k], kd);
 #pragma unroll
@@ -557,7 +559,19 @@ __global__ __launch_bounds__(512) void sampled_exact_kernel(const AttnParams p) 
         double a = 0.0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) a = fma((double)qr[h][i], kd[i], a);
-        x[k][h] = ok ? scale * sum16_d(a) : -kInf;
+        x[k][h] = a;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < NSB; ++k)
+#pragma unroll
+      for (int h = 0; h < G; ++h) x[k][h] = scale * sum16_d(x[k][h]);
+#pragma unroll
+    for (int k = 0; k < NSB; ++k) {
+      const bool ok = __shfl(lj, 4 * k + sub, 64) >= 0;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        x[k][h] = ok ? x[k][h] : -kInf;
         bm[h] = fmax(bm[h], x[k][h]);
       }
     }
