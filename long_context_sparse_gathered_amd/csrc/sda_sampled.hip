@@ -7,11 +7,12 @@
 // statistics estimated from b0 base draws.
 //
 // Four launches per call:
-//   sampled_exact_kernel  about 256 workgroups share the exact pass over I_f
-//                         (fp64 records per share); B*Hkv more workgroups,
-//                         one per (sequence, KV head), check the list and
-//                         take the b0 base draws' fp64 moments relative to
-//                         their own maximum.
+//   sampled_exact_kernel  `splits` workgroups per unit share the exact pass
+//                         over I_f (an fp64 record per share); B*Hkv more
+//                         workgroups, one per (sequence, KV head), check the
+//                         list and take the b0 base draws' fp64 moments
+//                         relative to their own maximum. About 256 in all,
+//                         one per CU.
 //   sampled_budget_kernel one workgroup per unit: the records merged at the
 //                         unit's maximum M, the base moments rescaled to it,
 //                         the budget b; leaves M, D_f, N_f and b in the
