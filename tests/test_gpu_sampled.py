@@ -122,3 +122,12 @@ def test_sampled_budget_reaches_whole_tail_one_unit(orc):
     c = synth.make_case(w)
     tail, _, ref = _check(orc, c, w, 11, b_cap=1024, tol=2e-3)
     assert int(tail.b.cpu().numpy()[0, 0]) == w.n - w.m
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 4), (32, 4)])
+def test_sampled_group_sizes(orc, hq, hkv):
+    """Two and eight query heads per KV head (the kernels' other register
+    shapes and draw-grid occupancies): budgets, draws and output."""
+    w = synth.WORKLOADS["sampled_bf16_b8_n64k"].replace(B=2, Hq=hq, Hkv=hkv, n=6000, n_top=60)
+    c = synth.make_case(w)
+    _check(orc, c, w, 5, b_cap=4096, tol=2e-3)
