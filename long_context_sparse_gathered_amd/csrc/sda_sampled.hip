@@ -847,7 +847,7 @@ __device__ void work_item_prefix(const int32_t* wb, int units, int* pref, int* s
 }
 
 template <typename T, int G>
-__global__ __launch_bounds__(512) void sampled_draws_kernel(const AttnParams p) {
+__global__ __launch_bounds__(512, (sizeof(T) == 2 && G <= 4 ? 4 : 2)) void sampled_draws_kernel(const AttnParams p) {
   constexpr int W = 8;              // waves
   constexpr int NT = 64 * W;        // threads
   constexpr int NSB = 4;            // slots (of 4 rows) per wave per batch
@@ -904,19 +904,27 @@ __global__ __launch_bounds__(512) void sampled_draws_kernel(const AttnParams p) 
     const uint64_t key = splitmix_at(p.seed, (uint64_t)u);
     __syncthreads();
 
-    // lane l < 4*NSB of wave w generates draw tb + 4*((l>>2)*W + w) + (l&3);
-    // slot k of row group sub takes the draw of lane 4k + sub
-    auto lane_draw = [&](int tb) { return tb + 4 * ((lane >> 2) * W + w) + (lane & 3); };
+    // Batch tb's slot k of row group sub takes draw tb + 4*(k*W + w) + sub.
+    // The positions of kPB batches are found at once, one draw per lane:
+    // lane LPB*i + 4k + sub holds slot k, row group sub of batch i (a binary
+    // search per draw, whose cost is per wave instruction, not per lane).
+    constexpr int LPB = 4 * NSB, kPB = 64 / LPB;
     auto position = [&](int t) {
       const int64_t rank = (int64_t)__umul64hi(splitmix_at(key, (uint64_t)(p.b0 + t)), (uint64_t)n_s);
       const int j = tail_position(s_A, mf, rank);
       return j < p.n ? j : p.n - 1;
     };
-    int pj = 0;
-    {
-      const int t = lane_draw(t0);
-      if (lane < 4 * NSB && t < t1) pj = position(t);
-    }
+    auto positions = [&](int tb) {  // of batches tb, tb + STEP, ...; the draws recorded here
+      const int ll = lane % LPB;
+      const int t = tb + (lane / LPB) * STEP + 4 * ((ll >> 2) * W + w) + (ll & 3);
+      int j = 0;
+      if (t < t1) {
+        j = position(t);
+        if (p.samples_out && t < p.b_cap) p.samples_out[(int64_t)u * p.b_cap + t] = j;
+      }
+      return j;
+    };
+    int pj = positions(t0);
 
     const int64_t kvoff = (int64_t)s * p.sb + (int64_t)g * p.sh;
     const rsrc_t rk = rsrc_of<T>(reinterpret_cast<const T*>(p.K) + kvoff, p.n, p.sn);
@@ -952,17 +960,14 @@ __global__ __launch_bounds__(512) void sampled_draws_kernel(const AttnParams p) 
       for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
     }
 
+    int bi = 0;  // this batch's place among the kPB whose positions pj holds
     for (int tb = t0; tb < t1; tb += STEP) {
-      const int t = lane_draw(tb);
-      const bool own = lane < 4 * NSB && t < t1;
-      if (own && p.samples_out && t < p.b_cap) p.samples_out[(int64_t)u * p.b_cap + t] = pj;
       int off[NSB];
       bool ok[NSB];
 #pragma unroll
       for (int k = 0; k < NSB; ++k) {
-        const int src = 4 * k + sub;
-        const int j = __shfl(pj, src, 64);
-        ok[k] = __shfl(own ? 1 : 0, src, 64) != 0;
+        ok[k] = tb + 4 * (k * W + w) + sub < t1;
+        const int j = __shfl(pj, LPB * bi + 4 * k + sub, 64);
         off[k] = ok[k] ? off_of<T>(j, p.sn, r16) : kOOBs;
       }
       RowChunk<T> kc[NSB], vc[NSB];
@@ -970,10 +975,10 @@ __global__ __launch_bounds__(512) void sampled_draws_kernel(const AttnParams p) 
       for (int k = 0; k < NSB; ++k) gather(kc[k], rk, off[k]);
 #pragma unroll
       for (int k = 0; k < NSB; ++k) gather(vc[k], rv, off[k]);
-      // next batch's positions while the rows are in flight
-      {
-        const int tn = lane_draw(tb + STEP);
-        if (lane < 4 * NSB && tn < t1) pj = position(tn);
+      // the next kPB batches' positions while the rows are in flight
+      if (++bi == kPB) {
+        bi = 0;
+        pj = positions(tb + STEP);
       }
       float x[NSB][G], bm[G];
 #pragma unroll
@@ -1003,12 +1008,14 @@ __global__ __launch_bounds__(512) void sampled_draws_kernel(const AttnParams p) 
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float mn = fmaxf(m[h], bm[h]);
-        const float al = rescale(m[h], mn);
-        m[h] = mn;
-        l[h] *= al;
+        if (__ballot(bm[h] > m[h])) {  // some row group's maximum grows (elsewhere al = 1)
+          const float mn = fmaxf(m[h], bm[h]);
+          const float al = rescale(m[h], mn);
+          m[h] = mn;
+          l[h] *= al;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[h][i] *= al;
+          for (int i = 0; i < 8; ++i) acc[h][i] *= al;
+        }
       }
 #pragma unroll
       for (int k = 0; k < NSB; ++k) {
