@@ -118,6 +118,30 @@ __device__ __forceinline__ double rescale_d(double m, double M) {
   return m == -__builtin_huge_val() ? 0.0 : exp(m - M);
 }
 
+// fp32 lane moves within 16-lane rows in which every lane reads a lane of
+// its own row (no old value is kept)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// Sums over the 16 lanes of a row group of four values a[0..3], reduce-
+// scattered: lane r16 returns the sum of a[r16 >> 2]. Partners r16 ^ 8
+// (row_ror:8; bit 3 keeps heads 2..3), r16 ^ 7 (row_half_mirror; bit 2 keeps
+// the odd one of the pair), then r16 ^ 1 and r16 ^ 2 (quad permutations):
+// the four partner sets together cover the row.
+__device__ __forceinline__ float sum16_scatter4(const float (&a)[4], int r16) {
+  const bool b3 = (r16 & 8) != 0, b2 = (r16 & 4) != 0;
+  const float s0 = b3 ? a[0] : a[2], k0 = b3 ? a[2] : a[0];
+  const float s1 = b3 ? a[1] : a[3], k1 = b3 ? a[3] : a[1];
+  const float c0 = k0 + dpp_f<0x128>(s0);
+  const float c1 = k1 + dpp_f<0x128>(s1);
+  const float sv = b2 ? c0 : c1, kv = b2 ? c1 : c0;
+  float d = kv + dpp_f<0x141>(sv);
+  d += dpp_f<0xB1>(d);
+  d += dpp_f<0x4E>(d);
+  return d;
+}
+
 // lane H's value, broadcast to the 16 lanes of each row group (row_newbcast)
 template <int H>
 __device__ __forceinline__ double row_bcast_d(double v) {
@@ -980,53 +1004,102 @@ __global__ __launch_bounds__(512, (sizeof(T) == 2 && G <= 4 ? 4 : 2)) void sampl
         bi = 0;
         pj = positions(tb + STEP);
       }
-      float x[NSB][G], bm[G];
+      if constexpr (kBf && G == 4) {
+        // the four heads' dot products reduce-scattered over the row group:
+        // lane r16 holds head ho = r16 >> 2's logit of each slot and takes its
+        // one exponential; the row group's lanes 4h hand head h's values on
+        const int ho = r16 >> 2;
+        float xo[NSB], bmo = kNegInf;
 #pragma unroll
-      for (int h = 0; h < G; ++h) bm[h] = kNegInf;
+        for (int k = 0; k < NSB; ++k) {
+          const uint32_t kw[4] = {kc[k].raw.x, kc[k].raw.y, kc[k].raw.z, kc[k].raw.w};
+          float a[4];
 #pragma unroll
-      for (int k = 0; k < NSB; ++k) {
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-          float a = 0.f;
-          if constexpr (kBf) {
-            const uint32_t kw[4] = {kc[k].raw.x, kc[k].raw.y, kc[k].raw.z, kc[k].raw.w};
+          for (int h = 0; h < 4; ++h) {
+            a[h] = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[h][i]),
-                                                  __builtin_bit_cast(bf16x2_t, kw[i]), a, false);
-            a = sum16(a) * p.qscale;
-          } else {
-            float kf[8];
-            kc[k].unpack(kf);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) a = fmaf(qf[h][i], kf[i], a);
-            a = sum16(a);
+              a[h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[h][i]),
+                                                     __builtin_bit_cast(bf16x2_t, kw[i]), a[h], false);
           }
-          x[k][h] = ok[k] ? a : kNegInf;
-          bm[h] = fmaxf(bm[h], x[k][h]);
+          xo[k] = ok[k] ? sum16_scatter4(a, r16) * p.qscale : kNegInf;
+          bmo = fmaxf(bmo, xo[k]);
         }
-      }
+        const float bm[4] = {dpp_f<0x150>(bmo), dpp_f<0x154>(bmo), dpp_f<0x158>(bmo), dpp_f<0x15C>(bmo)};
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        if (__ballot(bm[h] > m[h])) {  // some row group's maximum grows (elsewhere al = 1)
-          const float mn = fmaxf(m[h], bm[h]);
-          const float al = rescale(m[h], mn);
-          m[h] = mn;
-          l[h] *= al;
+        for (int h = 0; h < 4; ++h) {
+          if (__ballot(bm[h] > m[h])) {  // some row group's maximum grows (elsewhere al = 1)
+            const float mn = fmaxf(m[h], bm[h]);
+            const float al = rescale(m[h], mn);
+            m[h] = mn;
+            l[h] *= al;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[h][i] *= al;
+            for (int i = 0; i < 8; ++i) acc[h][i] *= al;
+          }
         }
-      }
+        const float mo = ho == 0 ? m[0] : ho == 1 ? m[1] : ho == 2 ? m[2] : m[3];
 #pragma unroll
-      for (int k = 0; k < NSB; ++k) {
-        float vf[8];
-        vc[k].unpack(vf);
+        for (int k = 0; k < NSB; ++k) {
+          float vf[8];
+          vc[k].unpack(vf);
+          const float eo = (mo == kNegInf) ? 0.f : fast_exp2(xo[k] - mo);
+          const float e[4] = {dpp_f<0x150>(eo), dpp_f<0x154>(eo), dpp_f<0x158>(eo), dpp_f<0x15C>(eo)};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            l[h] += e[h];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(e[h], vf[i], acc[h][i]);
+          }
+        }
+      } else {
+        float x[NSB][G], bm[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) bm[h] = kNegInf;
+#pragma unroll
+        for (int k = 0; k < NSB; ++k) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            float a = 0.f;
+            if constexpr (kBf) {
+              const uint32_t kw[4] = {kc[k].raw.x, kc[k].raw.y, kc[k].raw.z, kc[k].raw.w};
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[h][i]),
+                                                    __builtin_bit_cast(bf16x2_t, kw[i]), a, false);
+              a = sum16(a) * p.qscale;
+            } else {
+              float kf[8];
+              kc[k].unpack(kf);
+#pragma unroll
+              for (int i = 0; i < 8; ++i) a = fmaf(qf[h][i], kf[i], a);
+              a = sum16(a);
+            }
+            x[k][h] = ok[k] ? a : kNegInf;
+            bm[h] = fmaxf(bm[h], x[k][h]);
+          }
+        }
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float e = (m[h] == kNegInf) ? 0.f : fast_exp2(x[k][h] - m[h]);
-          l[h] += e;
+          if (__ballot(bm[h] > m[h])) {  // some row group's maximum grows (elsewhere al = 1)
+            const float mn = fmaxf(m[h], bm[h]);
+            const float al = rescale(m[h], mn);
+            m[h] = mn;
+            l[h] *= al;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(e, vf[i], acc[h][i]);
+            for (int i = 0; i < 8; ++i) acc[h][i] *= al;
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < NSB; ++k) {
+          float vf[8];
+          vc[k].unpack(vf);
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const float e = (m[h] == kNegInf) ? 0.f : fast_exp2(x[k][h] - m[h]);
+            l[h] += e;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[h][i] = fmaf(e, vf[i], acc[h][i]);
+          }
         }
       }
     }
