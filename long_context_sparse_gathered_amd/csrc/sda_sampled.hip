@@ -163,6 +163,30 @@ __device__ __forceinline__ double row_bcast(double v, int h) {  // h folds to a 
   }
 }
 
+// fp64 sums over the 16 lanes of a row group of four values, reduce-
+// scattered as in sum16_scatter4: lane r16 returns the sum of a[r16 >> 2]
+__device__ __forceinline__ double sum16_scatter4_d(const double (&a)[4], int r16) {
+  const bool b3 = (r16 & 8) != 0, b2 = (r16 & 4) != 0;
+  const double s0 = b3 ? a[0] : a[2], k0 = b3 ? a[2] : a[0];
+  const double s1 = b3 ? a[1] : a[3], k1 = b3 ? a[3] : a[1];
+  const double c0 = k0 + dpp_d<0x128>(s0);
+  const double c1 = k1 + dpp_d<0x128>(s1);
+  const double sv = b2 ? c0 : c1, kv = b2 ? c1 : c0;
+  double d = kv + dpp_d<0x141>(sv);
+  d += dpp_d<0xB1>(d);
+  d += dpp_d<0x4E>(d);
+  return d;
+}
+// lane 4h's value to the 16 lanes of each row group (h folds to a constant)
+__device__ __forceinline__ double row_bcast4(double v, int h) {
+  switch (h) {
+    case 0: return row_bcast_d<0>(v);
+    case 1: return row_bcast_d<4>(v);
+    case 2: return row_bcast_d<8>(v);
+    default: return row_bcast_d<12>(v);
+  }
+}
+
 template <typename T>
 __device__ __forceinline__ void widen8(const RowChunk<T>& c, double (&d)[8]) {
   float f[8];
@@ -572,74 +596,115 @@ __global__ __launch_bounds__(512) void sampled_exact_kernel(const AttnParams p) 
     double x[NSB][G], bm[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) bm[h] = -kInf;
-    // every slot's logits unconditionally (a slot past the list holds zero
-    // rows), so that the NSB*G dot products and their row sums interleave;
-    // the empty slots are masked afterwards
+    if constexpr (G == 4) {
+      // every slot's dot products unconditionally (a slot past the list
+      // holds zero rows), so that they and their row sums interleave; the
+      // empty slots are masked afterwards
 #pragma unroll
-    for (int k = 0; k < NSB; ++k) {
-      double kd[8];
-      widen8(kc[k], kd);
+      for (int k = 0; k < NSB; ++k) {
+        double kd[8];
+        widen8(kc[k], kd);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        double a = 0.0;
+        for (int h = 0; h < G; ++h) {
+          double a = 0.0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) a = fma((double)qr[h][i], kd[i], a);
-        x[k][h] = a;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < NSB; ++k)
-#pragma unroll
-      for (int h = 0; h < G; ++h) x[k][h] = scale * sum16_d(x[k][h]);
-#pragma unroll
-    for (int k = 0; k < NSB; ++k) {
-      const bool ok = __shfl(lj, 4 * k + sub, 64) >= 0;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        x[k][h] = ok ? x[k][h] : -kInf;
-        bm[h] = fmax(bm[h], x[k][h]);
-      }
-    }
-    {
-      // a new maximum rescales the running sums: lane r16 < G takes the one
-      // exponential of head r16 and the row group shares it (1 where the
-      // maximum stays)
-      double mo = 0.0, bo = 0.0;
-#pragma unroll
-      for (int h = 0; h < G; ++h)
-        if (r16 == h) {
-          mo = mh[h];
-          bo = bm[h];
+          for (int i = 0; i < 8; ++i) a = fma((double)qr[h][i], kd[i], a);
+          x[k][h] = a;
         }
-      const double fo = bo > mo ? rescale_d(mo, bo) : 1.0;
+      }
+      // the four heads' sums reduce-scattered over the row group: lane r16
+      // holds head ho = r16 >> 2's logit of each slot and takes its one
+      // exponential; lanes 4h of the row group hand head h's values on
+      const int ho = r16 >> 2;
+      double xo[NSB], bmo = -kInf;
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const double f = row_bcast(fo, h);
+      for (int k = 0; k < NSB; ++k) {
+        const bool ok = __shfl(lj, 4 * k + sub, 64) >= 0;
+        const double a4[4] = {x[k][0], x[k][1], x[k][2], x[k][3]};
+        xo[k] = ok ? scale * sum16_scatter4_d(a4, r16) : -kInf;
+        bmo = fmax(bmo, xo[k]);
+      }
+      const double mo = ho == 0 ? mh[0] : ho == 1 ? mh[1] : ho == 2 ? mh[2] : mh[3];
+      const double fo = bmo > mo ? rescale_d(mo, bmo) : 1.0;  // 1 where the maximum stays
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const double f = row_bcast4(fo, h);
         Df[h] *= f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) Nf[h][i] *= f;
-        mh[h] = fmax(mh[h], bm[h]);
+        mh[h] = fmax(mh[h], row_bcast4(bmo, h));
       }
-    }
+      const double mn = fmax(mo, bmo);
 #pragma unroll
-    for (int k = 0; k < NSB; ++k) {
-      // lane r16 < G evaluates exp for head r16; the row group shares it
-      double xo = -kInf, mo = 0.0;
+      for (int k = 0; k < NSB; ++k) {
+        const double eo = xo[k] == -kInf ? 0.0 : exp(xo[k] - mn);
+        double vd[8];
+        widen8(vc[k], vd);
 #pragma unroll
-      for (int h = 0; h < G; ++h)
-        if (r16 == h) {
-          xo = x[k][h];
-          mo = mh[h];
+        for (int h = 0; h < 4; ++h) {
+          const double e = row_bcast4(eo, h);
+          Df[h] += e;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) Nf[h][i] = fma(e, vd[i], Nf[h][i]);
         }
-      const double eo = xo == -kInf ? 0.0 : exp(xo - mo);
-      double vd[8];
-      widen8(vc[k], vd);
+      }
+    } else {
+      // (other group sizes: one head at a time, which keeps fewer values live)
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const double e = row_bcast(eo, h);
-        Df[h] += e;
+      for (int k = 0; k < NSB; ++k) {
+        const bool ok = __shfl(lj, 4 * k + sub, 64) >= 0;
+        double kd[8];
+        widen8(kc[k], kd);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) Nf[h][i] = fma(e, vd[i], Nf[h][i]);
+        for (int h = 0; h < G; ++h) {
+          double a = 0.0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a = fma((double)qr[h][i], kd[i], a);
+          x[k][h] = ok ? scale * sum16_d(a) : -kInf;
+          bm[h] = fmax(bm[h], x[k][h]);
+        }
+      }
+      {
+        // a new maximum rescales the running sums: lane r16 < G takes the one
+        // exponential of head r16 and the row group shares it (1 where the
+        // maximum stays)
+        double mo = 0.0, bo = 0.0;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          if (r16 == h) {
+            mo = mh[h];
+            bo = bm[h];
+          }
+        const double fo = bo > mo ? rescale_d(mo, bo) : 1.0;
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const double f = row_bcast(fo, h);
+          Df[h] *= f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) Nf[h][i] *= f;
+          mh[h] = fmax(mh[h], bm[h]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NSB; ++k) {
+        // lane r16 < G evaluates exp for head r16; the row group shares it
+        double xo = -kInf, mo = 0.0;
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+          if (r16 == h) {
+            xo = x[k][h];
+            mo = mh[h];
+          }
+        const double eo = xo == -kInf ? 0.0 : exp(xo - mo);
+        double vd[8];
+        widen8(vc[k], vd);
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const double e = row_bcast(eo, h);
+          Df[h] += e;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) Nf[h][i] = fma(e, vd[i], Nf[h][i]);
+        }
       }
     }
 #pragma unroll
