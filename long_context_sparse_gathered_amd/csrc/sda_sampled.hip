@@ -119,10 +119,16 @@ __device__ __forceinline__ double rescale_d(double m, double M) {
 }
 
 // fp32 lane moves within 16-lane rows in which every lane reads a lane of
-// its own row (no old value is kept)
+// its own row (the zero old value lets the compiler fold a move into the
+// add that consumes it)
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// lane H's value to the 16 lanes of each row group (a plain move, no old value)
+template <int H>
+__device__ __forceinline__ float bcast_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + H, 0xF, 0xF, false));
 }
 // Sums over the 16 lanes of a row group of four values a[0..3], reduce-
 // scattered: lane r16 returns the sum of a[r16 >> 2]. Partners r16 ^ 8
@@ -1090,7 +1096,7 @@ __global__ __launch_bounds__(512, (sizeof(T) == 2 && G <= 4 ? 4 : 2)) void sampl
           xo[k] = ok[k] ? sum16_scatter4(a, r16) * p.qscale : kNegInf;
           bmo = fmaxf(bmo, xo[k]);
         }
-        const float bm[4] = {dpp_f<0x150>(bmo), dpp_f<0x154>(bmo), dpp_f<0x158>(bmo), dpp_f<0x15C>(bmo)};
+        const float bm[4] = {bcast_f<0>(bmo), bcast_f<4>(bmo), bcast_f<8>(bmo), bcast_f<12>(bmo)};
 #pragma unroll
         for (int h = 0; h < 4; ++h) {
           if (__ballot(bm[h] > m[h])) {  // some row group's maximum grows (elsewhere al = 1)
@@ -1108,7 +1114,7 @@ __global__ __launch_bounds__(512, (sizeof(T) == 2 && G <= 4 ? 4 : 2)) void sampl
           float vf[8];
           vc[k].unpack(vf);
           const float eo = (mo == kNegInf) ? 0.f : fast_exp2(xo[k] - mo);
-          const float e[4] = {dpp_f<0x150>(eo), dpp_f<0x154>(eo), dpp_f<0x158>(eo), dpp_f<0x15C>(eo)};
+          const float e[4] = {bcast_f<0>(eo), bcast_f<4>(eo), bcast_f<8>(eo), bcast_f<12>(eo)};
 #pragma unroll
           for (int h = 0; h < 4; ++h) {
             l[h] += e[h];
