@@ -76,11 +76,14 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 // Split-K shape for the streaming kernels: enough workgroups to fill the chip
-// several times over, chunks a multiple of one batch of rows of either kernel.
-void stream_shape(int units, int len, int min_chunk, int target_wgs, int* splits, int* chunk) {
+// several times over, chunks a multiple of one batch of rows of either kernel
+// and at most max_chunk entries.
+void stream_shape(int units, int len, int min_chunk, int target_wgs, int* splits, int* chunk,
+                  int max_chunk = 1 << 30) {
   int sp = ceil_div(target_wgs, units);
   const int max_sp = len > 0 ? ceil_div(len, min_chunk) : 1;
   if (sp > max_sp) sp = max_sp;
+  if (len > 0 && sp < ceil_div(len, max_chunk)) sp = ceil_div(len, max_chunk);
   if (sp < 1) sp = 1;
   int ch = ceil_div(len > 0 ? len : 1, sp);
   ch = ceil_div(ch, kStreamMfmaStep) * kStreamMfmaStep;
@@ -170,7 +173,7 @@ sda_status plan_sparse(const Resolved& r, int kind, int m, int C, SparsePlan* pl
     // the matrix-core kernel runs two workgroups per CU: one round of long
     // workgroups beats several rounds of short ones
     const bool mfma = r.dtype == SDA_BF16 && (kind == SDA_TAIL_NONE || 3 * r.G <= 16);
-    stream_shape(units, m, 256, mfma ? 512 : 2048, &pl->splits, &pl->chunk);
+    stream_shape(units, m, 256, mfma ? 512 : 2048, &pl->splits, &pl->chunk, mfma ? kStreamDmaMaxChunk : 1 << 30);
     if (pl->splits > 1) pl->ws = (size_t)units * pl->splits * r.G * kPartStride * sizeof(float);
     return SDA_OK;
   }

@@ -2610,6 +2610,457 @@ __global__ __launch_bounds__(256) void stream_mfma_kernel(const AttnParams p) {
     }
   }
 }
+// LDS accesses of a wave whose direct-to-LDS loads stay in flight, written
+// out: the compiler cannot tell the tiles those loads fill from the other LDS
+// arrays, and would wait for every one of them before any LDS access. A
+// wave's LDS operations execute in order, so these need no waits between
+// them; each read waits for its own results inside its statement, and every
+// output is early-clobber (the reads complete after later ones issue).
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+__device__ __forceinline__ void lds_st_f32(float* p, float v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(lds_addr(p)), "v"(v) : "memory");
+}
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// Sixteen bytes at ax (and at ay when TWO) and the eight transposed 64-bit
+// reads of a value tile at at[0..7].
+template <bool TWO>
+__device__ __forceinline__ void lds_tile_reads(unsigned ax, unsigned ay, const unsigned (&at)[8], f32x4_t& x,
+                                               f32x4_t& y, u32x2_t (&b)[8]) {
+  if constexpr (TWO) {
+    asm volatile(
+        "ds_read_b128 %0, %10\n\tds_read_b128 %1, %11\n\t"
+        "ds_read_b64_tr_b16 %2, %12\n\tds_read_b64_tr_b16 %3, %13\n\t"
+        "ds_read_b64_tr_b16 %4, %14\n\tds_read_b64_tr_b16 %5, %15\n\t"
+        "ds_read_b64_tr_b16 %6, %16\n\tds_read_b64_tr_b16 %7, %17\n\t"
+        "ds_read_b64_tr_b16 %8, %18\n\tds_read_b64_tr_b16 %9, %19\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x), "=&v"(y), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4]), "=&v"(b[5]),
+          "=&v"(b[6]), "=&v"(b[7])
+        : "v"(ax), "v"(ay), "v"(at[0]), "v"(at[1]), "v"(at[2]), "v"(at[3]), "v"(at[4]), "v"(at[5]), "v"(at[6]),
+          "v"(at[7])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %9\n\t"
+        "ds_read_b64_tr_b16 %1, %10\n\tds_read_b64_tr_b16 %2, %11\n\t"
+        "ds_read_b64_tr_b16 %3, %12\n\tds_read_b64_tr_b16 %4, %13\n\t"
+        "ds_read_b64_tr_b16 %5, %14\n\tds_read_b64_tr_b16 %6, %15\n\t"
+        "ds_read_b64_tr_b16 %7, %16\n\tds_read_b64_tr_b16 %8, %17\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(x), "=&v"(b[0]), "=&v"(b[1]), "=&v"(b[2]), "=&v"(b[3]), "=&v"(b[4]), "=&v"(b[5]), "=&v"(b[6]),
+          "=&v"(b[7])
+        : "v"(ax), "v"(at[0]), "v"(at[1]), "v"(at[2]), "v"(at[3]), "v"(at[4]), "v"(at[5]), "v"(at[6]), "v"(at[7])
+        : "memory");
+    y = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 split-K streaming kernel with the value rows staged straight from HBM
+// into LDS: plain lists, dense rows and the rank-1 prior.
+//
+// The products are those of stream_mfma_kernel (logits with the G heads, and
+// for the prior the mean-query rows, in one A operand; weighted values from
+// transposed LDS reads), but each wave keeps two batches in flight instead of
+// one. A batch's keys go to one of two register sets and its values, by
+// direct-to-LDS buffer loads, to one of two sets of swizzled value tiles, so
+// no register holds a value row. Once a batch's keys have gone through the
+// logit products their registers take the keys of the batch two ahead; once
+// its value products have read its tiles, the tiles take that batch's values.
+// Every load is issued unconditionally (entries past the chunk get an offset
+// outside the buffer, which returns zeros), so the number of loads issued
+// after a batch's value tiles is fixed, and the wait for those tiles (an
+// explicit vmcnt) leaves the later batches' loads in flight.
+template <int G, int MODE, int NT>
+__global__ __launch_bounds__(256, 2) void stream_dma_kernel(const AttnParams p) {
+  constexpr int W = 4;
+  constexpr bool DENSE = (MODE == kModeDense);
+  constexpr bool PRIOR = (MODE == kModePrior);
+  static_assert(MODE == kModeSparse || DENSE || PRIOR, "plain, dense and prior modes only");
+  constexpr int RA = PRIOR ? 3 * G : G;  // A rows of the logits
+  constexpr int RP = PRIOR ? 2 * G : G;  // A rows of the weighted values
+  static_assert(RA <= 16, "the logit rows fit one 16-row block");
+  constexpr int KB = 16 * NT;   // entries per wave per batch
+  constexpr int STEP = W * KB;  // entries per workgroup per batch
+  constexpr int NS = 4 * NT;    // value loads per wave per batch (four rows each)
+  static_assert(RP * kD * 4 <= NT * kVTile, "a wave's partial sums fit its value tiles");
+  // loads issued after a batch's value tiles until they are read: the next
+  // batch's keys and values, then the keys of the batch two ahead
+  constexpr int kAfterV = 2 * 4 * NT + NS;
+  static_assert(kAfterV < 64, "the wait count fits vmcnt");
+  constexpr int kWaitV = 0x0F70 | (kAfterV & 15) | ((kAfterV >> 4) << 14);
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  const int u = blockIdx.x / p.splits;
+  const int split = blockIdx.x - u * p.splits;
+  const int s = u / p.Hkv;
+  const int g = u - s * p.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int r16 = lane & 15, sub = lane >> 4;
+  const int hr = r16 < G ? r16 : 0;
+
+  __shared__ __attribute__((aligned(16))) float s_x[W][RA][KB];
+  __shared__ float s_m[W][G], s_l[W][G], s_sp[W][G];
+  __shared__ float s_c[G];
+  // value tiles of the two batches in flight: per wave NT tiles of 16 rows x
+  // 256 bytes, 16-byte chunks swizzled (vt_chunk)
+  __shared__ __attribute__((aligned(16))) unsigned char s_v0[W][NT][kVTile];
+  __shared__ __attribute__((aligned(16))) unsigned char s_v1[W][NT][kVTile];
+
+  // ---- A operand: row r16, dims 32*st + 8*sub .. +8 ---------------------------
+  const int64_t qrow0 = (int64_t)s * p.Hq + (int64_t)g * G;
+  uint4 qa[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    qa[st] = make_uint4(0, 0, 0, 0);
+    if (r16 < G) {
+      qa[st] = *reinterpret_cast<const uint4*>(reinterpret_cast<const bf16_t*>(p.q) + (qrow0 + r16) * kD + 32 * st +
+                                                8 * sub);
+    } else if (PRIOR && r16 < 3 * G) {
+      const int h = (r16 - G) % G;
+      float mq[8];
+      load8f(p.mu_Q + (qrow0 + h) * kD + 32 * st + 8 * sub, mq);
+      bf16x8_t v;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const __bf16 hi = (__bf16)mq[i];
+        v[i] = r16 < 2 * G ? hi : (__bf16)(mq[i] - (float)hi);
+      }
+      qa[st] = __builtin_bit_cast(uint4, v);
+    }
+  }
+  // prior shift maxP (log2 units) of the operand-layout head r16 - G
+  float mPa = 0.f;
+  if (PRIOR && r16 >= G && r16 < 2 * G) mPa = p.maxP[qrow0 + r16 - G] * kLog2e;
+
+  int len = DENSE ? p.n : p.m;
+  if (!DENSE && p.idx_len) {
+    int L = p.idx_len[u];
+    if (L < 0 || L > p.m) {
+      if (tid == 0 && split == 0) flag_unit(p.flags, u, SDA_FLAG_LEN);
+      L = L < 0 ? 0 : p.m;
+    }
+    len = L;
+  }
+  const int t0 = split * p.chunk;
+  const int t1 = min(len, t0 + p.chunk);
+  const int64_t lbase = (int64_t)u * p.m;
+  const int64_t kvoff = (int64_t)s * p.sb + (int64_t)g * p.sh;
+  const rsrc_t rk = make_rsrc<bf16_t>(reinterpret_cast<const bf16_t*>(p.K) + kvoff, p.n, p.sn);
+  const rsrc_t rv = make_rsrc<bf16_t>(reinterpret_cast<const bf16_t*>(p.V) + kvoff, p.n, p.sn);
+
+  // This wave's list entries of every batch of the chunk, staged in LDS before
+  // any row load (a chunk holds at most kStreamDmaMaxChunk entries): row b
+  // holds the entry before the wave's block of batch b (for the order check),
+  // then the block's KB entries; the log-weights beside them. Read back
+  // while row loads are in flight, so no loop-carried register waits on a
+  // list load.
+  constexpr int MB = kStreamDmaMaxChunk / STEP;  // batches per chunk, at most
+  __shared__ int s_li[DENSE ? 1 : W][DENSE ? 1 : MB][KB + 1];
+  __shared__ float s_lw[DENSE ? 1 : W][DENSE ? 1 : MB][KB];
+  const int nbatch = t0 < t1 ? (t1 - t0 + STEP - 1) / STEP : 0;
+  if constexpr (!DENSE) {
+    for (int b = 0; b < nbatch; ++b) {
+      const int e = t0 + b * STEP + w * KB - 1 + lane;  // entry of slot `lane`
+      if (lane <= KB) s_li[w][b][lane] = (e >= 0 && e < t1) ? p.idx[lbase + e] : -1;
+      if (lane >= 1 && lane <= KB) s_lw[w][b][lane - 1] = (p.logw && e < t1) ? p.logw[lbase + e] : 0.f;
+    }
+  }
+  int bad = 0;  // list errors seen by this lane, flagged once at the end
+  // (li, lp, log-weight) of this lane's entry of batch b from LDS
+  auto read_list = [&](int b, int& li, int& lp, float& lw) {
+    const int bb = b < nbatch ? b : 0;  // batches past the chunk: any row (not live)
+    const int k = lane < KB ? lane : 0;
+    asm volatile(
+        "ds_read_b32 %0, %3\n\tds_read_b32 %1, %4\n\tds_read_b32 %2, %5\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(li), "=&v"(lp), "=&v"(lw)
+        : "v"(lds_addr(&s_li[0][0][0] + (w * MB + bb) * (KB + 1) + k + 1)),
+          "v"(lds_addr(&s_li[0][0][0] + (w * MB + bb) * (KB + 1) + k)),
+          "v"(lds_addr(&s_lw[0][0][0] + (w * MB + bb) * KB + k))
+        : "memory");
+  };
+
+  floatx4_t oacc[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) oacc[nb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float m_a = kNegInf;                                  // running max of head r16
+  float m_d[4] = {kNegInf, kNegInf, kNegInf, kNegInf};  // running max of rows 4*sub + i
+  float lsum = 0.f, spsum = 0.f;
+
+  // the two batches in flight: keys in registers; this lane's entry row (-1 if
+  // absent) until the batch's value loads go out; the entry state
+  uint4 kt0[NT][4], kt1[NT][4];
+  int vr0 = -1, vr1 = -1;
+  float lw0 = kNegInf, lw1 = kNegInf;  // log-weight of the entry (log2 units), -inf if absent
+  bool cv0 = false, cv1 = false;       // the prior covers the entry's row
+
+  // Batch b: entry state from its list entries and its key loads.
+  auto issue_keys = [&](int b, uint4 (&kt)[NT][4], int& vrow, float& b_lw, bool& b_cov) {
+    const int e = t0 + b * STEP + w * KB + lane;
+    int row;
+    bool b_valid;
+    if constexpr (DENSE) {
+      b_valid = lane < KB && e < t1;
+      row = b_valid ? e : 0;
+      b_lw = b_valid ? 0.f : kNegInf;
+    } else {
+      int li, lp;
+      float lwv;
+      read_list(b, li, lp, lwv);
+      const bool live = lane < KB && e < t1;
+      b_valid = live && (unsigned)li < (unsigned)p.n;
+      row = li;
+      b_lw = b_valid ? lwv * kLog2e : kNegInf;
+      if constexpr (PRIOR) b_cov = b_valid && li < p.prior_n;
+      if (live && (unsigned)li >= (unsigned)p.n) bad |= SDA_FLAG_IDX_RANGE;
+      if (PRIOR && live && e > 0 && lp >= li) bad |= SDA_FLAG_IDX_ORDER;
+    }
+    int koff[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int src = 16 * t + r16;
+      const int j = shfl_i(row, src);
+      const bool ok = shfl_i(b_valid ? 1 : 0, src) != 0;
+      koff[t] = ok ? (int)(((int64_t)j * p.sn + 8 * sub) * 2) : kOOB;
+    }
+    vrow = b_valid ? row : -1;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        auto v = __builtin_amdgcn_raw_buffer_load_b128(rk, koff[t] + 64 * st, 0, kLoadNT);
+        kt[t][st] = make_uint4(v[0], v[1], v[2], v[3]);
+      }
+  };
+  // Its value loads: load k = 4t + kq fills rows 4kq .. 4kq+3 of tile t;
+  // lane (sub, r16) lands at row 4kq + sub, chunk position r16, so it fetches
+  // the chunk of entry 16t + 4kq + sub that the swizzle puts there.
+  auto issue_values = [&](unsigned char (&tiles)[W][NT][kVTile], int vrow) {
+    int vo[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int j = shfl_i(vrow, 4 * k + sub);
+      vo[k] = j >= 0 ? (int)((int64_t)j * p.sn * 2) + 16 * vt_chunk(4 * (k & 3) + sub, r16) : kOOB;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int off = vo[k];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void*)&tiles[w][k >> 2][(k & 3) * 1024], 16, off, 0, 0, kLoadNT);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // this lane's transposed reads of a value tile: row tr = 4*sub + r16/4,
+  // dims 16*nb + 4*(r16 & 3) .. +3, i.e. chunk 2*nb + q (q = (r16 & 3) / 2)
+  // at position vt_chunk(tr, 2*nb + q) = 2*(nb ^ xh) + q with xh the odd
+  // bits of the row's swizzle: byte tbase + 32*(nb ^ xh)
+  const int tr_row = 4 * sub + (r16 >> 2);
+  const unsigned tbase = tr_row * 256 + 16 * ((r16 & 3) >> 1) + 8 * (r16 & 1);
+  const unsigned txh = (unsigned)(vt_chunk(tr_row, 0) >> 1);
+
+  // One batch: logits from its key registers, which then take the keys of
+  // the batch two ahead; online rescale; weighted values from its tiles, which
+  // then take that batch's values.
+  auto process = [&](int b, uint4 (&kt)[NT][4], int& vrow, float& b_lw, bool& b_cov,
+                     unsigned char (&tiles)[W][NT][kVTile]) {
+    // ---- logits ---------------------------------------------------------------
+    float bmx[4] = {kNegInf, kNegInf, kNegInf, kNegInf};
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      floatx4_t d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, qa[st]),
+                                                    __builtin_bit_cast(bf16x8_t, kt[t][st]), d, 0, 0, 0);
+      const int kk = 16 * t + r16;
+      const float lwk = shfl_f(b_lw, kk);
+      const bool cvk = PRIOR && shfl_i(b_cov ? 1 : 0, kk) != 0;  // the prior covers this key
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * sub + i;
+        if (r < G) {
+          const float xv = d[i] * p.qscale + lwk;
+          lds_st_f32(&s_x[w][r][kk], xv);
+          bmx[i] = fmaxf(bmx[i], xv);
+        } else if (r < RA) {
+          lds_st_f32(&s_x[w][r][kk], cvk ? d[i] : kNegInf);
+        }
+      }
+    }
+    // batch maxima: every lane of row group sub holds those of rows 4*sub + i
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bmx[i] = max16(bmx[i]);
+    // ---- the keys two batches ahead --------------------------------------------
+    issue_keys(b + 2, kt, vrow, b_lw, b_cov);
+    // ---- online rescale (same values in both layouts) --------------------------
+    {
+      // head hr's batch maximum from the row group that holds it
+      float own = bmx[0];
+#pragma unroll
+      for (int i = 1; i < 4; ++i) own = (hr & 3) == i ? bmx[i] : own;
+      const float bm_h = shfl_f(own, 16 * (hr >> 2) + r16);
+      const float mn = fmaxf(m_a, bm_h);
+      const float al = rescale(m_a, mn);
+      lsum *= al;
+      m_a = mn;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * sub + i;
+        if (r < G) {
+          const float mnd = fmaxf(m_d[i], bmx[i]);
+          const float ad = rescale(m_d[i], mnd);
+          m_d[i] = mnd;
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) oacc[nb][i] *= ad;
+        }
+      }
+    }
+    // ---- weighted values ------------------------------------------------------
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitV);  // this batch's value tiles have landed
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      unsigned xh = txh;
+      asm volatile("" : "+v"(xh));  // computed per tile, not held across the loop
+      unsigned at[8];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) at[nb] = lds_addr(&tiles[w][t][0]) + tbase + 32 * (nb ^ xh);
+      f32x4_t x4, y4;
+      u32x2_t bt[8];
+      lds_tile_reads<PRIOR>(lds_addr(&s_x[w][r16 < RP ? r16 : 0][16 * t + 4 * sub]),
+                            lds_addr(&s_x[w][r16 >= G && r16 < 2 * G ? r16 + G : 0][16 * t + 4 * sub]), at, x4, y4,
+                            bt);
+      const float xs[4] = {x4[0], x4[1], x4[2], x4[3]};
+      const float ys[4] = {y4[0], y4[1], y4[2], y4[3]};
+      bf16x8_t a;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // one exp per lane: softmax rows (r16 < G) and prior rows (G <= r16 < 2G)
+        float arg;
+        if constexpr (PRIOR) {
+          arg = r16 < G ? xs[j] - m_a : (xs[j] + ys[j]) * p.qscale - mPa;
+        } else {
+          arg = xs[j] - m_a;
+        }
+        float wv = fast_exp2(arg);  // exp2(-inf) = 0 for absent keys
+        if (r16 >= RP || (r16 < G && m_a == kNegInf)) wv = 0.f;
+        if (r16 < G) lsum += wv;
+        if (PRIOR && r16 >= G) spsum += wv;
+        const __bf16 hi = (__bf16)wv;
+        a[j] = hi;
+        a[4 + j] = (__bf16)(wv - (float)hi);
+      }
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const bf16x4_t b4 = __builtin_bit_cast(bf16x4_t, bt[nb]);
+        const bf16x8_t b = {b4[0], b4[1], b4[2], b4[3], b4[0], b4[1], b4[2], b4[3]};
+        oacc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, oacc[nb], 0, 0, 0);
+      }
+    }
+    // ---- the values two batches ahead, into the tiles just read ---------------
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): every tile read has returned
+    issue_values(tiles, vrow);
+  };
+
+  // two batches in flight from the start
+  if (nbatch > 0) {
+    issue_keys(0, kt0, vr0, lw0, cv0);
+    issue_values(s_v0, vr0);
+    issue_keys(1, kt1, vr1, lw1, cv1);
+    issue_values(s_v1, vr1);
+  }
+  // batches in pairs (register sets and tiles alternate), then an odd last one
+  int i = 0;
+  for (; i + 1 < nbatch; i += 2) {
+    process(i, kt0, vr0, lw0, cv0, s_v0);
+    process(i + 1, kt1, vr1, lw1, cv1, s_v1);
+  }
+  if (i < nbatch) process(i, kt0, vr0, lw0, cv0, s_v0);
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // the loads past the end have landed too
+  if (__ballot(bad != 0)) {
+    int any = bad;
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) any |= __shfl_xor(any, sh, 64);
+    if (lane == 0) flag_unit(p.flags, u, any);
+  }
+
+  // ---- wave results -------------------------------------------------------------
+  float* red = reinterpret_cast<float*>(&s_v0[w][0][0]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * sub + i;
+    if (r < RP) {
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) red[r * kD + 16 * nb + r16] = oacc[nb][i];
+    }
+  }
+  lsum = sum_rowgroups(lsum);
+  spsum = sum_rowgroups(spsum);
+  if (sub == 0 && r16 < G) {
+    s_l[w][r16] = lsum;
+    s_m[w][r16] = m_a;
+  }
+  if (PRIOR && sub == 0 && r16 >= G && r16 < 2 * G) s_sp[w][r16 - G] = spsum;
+  if constexpr (PRIOR) {
+    if (split == 0 && w == 0) {
+      float qf[G][8];
+      load_query<bf16_t, G>(p.q, qrow0, r16, p.qscale, qf);
+      float c[G];
+      bias_shift<G>(p, s, g, r16, qf, c);
+      if (lane == 0) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) s_c[h] = c[h];
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int ei = tid; ei < G * kD; ei += 256) {
+    const int h = ei / kD, dim = ei - h * kD;
+    float M = kNegInf;
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww) M = fmaxf(M, s_m[ww][h]);
+    float a = 0.f, L = 0.f, SP = 0.f, SPV = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww) {
+      const float* rw = reinterpret_cast<const float*>(&s_v0[ww][0][0]);
+      const float f = rescale(s_m[ww][h], M);
+      a = fmaf(rw[h * kD + dim], f, a);
+      L = fmaf(s_l[ww][h], f, L);
+      if constexpr (PRIOR) {
+        SP += s_sp[ww][h];
+        SPV += rw[(G + h) * kD + dim];
+      }
+    }
+    const int64_t qh = qrow0 + h;
+    if (p.splits > 1) {
+      float* rec = p.part + (((int64_t)u * p.splits + split) * G + h) * kPartStride;
+      if (dim == 0) {
+        rec[0] = M;
+        rec[1] = L;
+        rec[2] = SP;
+        rec[3] = (PRIOR && split == 0) ? s_c[h] : 0.f;
+      }
+      rec[4 + dim] = a;
+      if constexpr (PRIOR) rec[4 + kD + dim] = SPV;
+    } else if constexpr (PRIOR) {
+      const Fin f = finalize_prior(M, L, a, s_c[h], p.maxP[qh] * kLog2e, p.sumP[qh], p.O_est[qh * kD + dim],
+                                   SP, SPV, p.lambda);
+      p.out[qh * kD + dim] = f.out;
+      if (dim == 0 && p.lse) p.lse[qh] = f.lse;
+    } else {
+      const Fin f = finalize_plain(M, L, a);
+      p.out[qh * kD + dim] = f.out;
+      if (dim == 0 && p.lse) p.lse[qh] = f.lse;
+    }
+  }
+}
+
 // Merge of split partials: one workgroup per unit, fixed split order.
 template <int G, int MODE>
 __global__ __launch_bounds__(512) void merge_kernel(const AttnParams p) {
@@ -2881,12 +3332,14 @@ static hipError_t launch_stream_t(const AttnParams& p, int G, int mode, hipStrea
 template <int G>
 static hipError_t launch_stream_mfma_g(const AttnParams& p, int mode, hipStream_t st) {
   const dim3 grid(p.B * p.Hkv * p.splits), block(256);
+  // the list of a plain or prior chunk is staged in LDS
+  if ((mode == kModeSparse || mode == kModePrior) && p.chunk > kStreamDmaMaxChunk) return hipErrorInvalidValue;
   switch (mode) {
-    case kModeSparse: hipLaunchKernelGGL((stream_mfma_kernel<G, kModeSparse, kStreamMfmaTiles>), grid, block, 0, st, p); break;
-    case kModeDense: hipLaunchKernelGGL((stream_mfma_kernel<G, kModeDense, kStreamMfmaTiles>), grid, block, 0, st, p); break;
+    case kModeSparse: hipLaunchKernelGGL((stream_dma_kernel<G, kModeSparse, kStreamMfmaTiles>), grid, block, 0, st, p); break;
+    case kModeDense: hipLaunchKernelGGL((stream_dma_kernel<G, kModeDense, kStreamMfmaTiles>), grid, block, 0, st, p); break;
     case kModePrior:
       if constexpr (3 * G <= 16) {
-        hipLaunchKernelGGL((stream_mfma_kernel<G, kModePrior, kStreamMfmaTiles>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((stream_dma_kernel<G, kModePrior, kStreamMfmaTiles>), grid, block, 0, st, p);
         break;
       }
       return hipErrorInvalidValue;

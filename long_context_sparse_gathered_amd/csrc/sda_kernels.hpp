@@ -111,6 +111,9 @@ hipError_t launch_merge(const AttnParams& p, int G, int mode, hipStream_t st);
 // are 64 * kStreamMfmaTiles; the prior needs 3G <= 16.
 constexpr int kStreamMfmaTiles = 2;
 constexpr int kStreamMfmaStep = 64 * kStreamMfmaTiles;
+// entries of a chunk of the direct-to-LDS streaming kernel (plain lists and the
+// prior), whose list is staged in LDS
+constexpr int kStreamDmaMaxChunk = 1024;
 hipError_t launch_stream_mfma(const AttnParams& p, int G, int mode, hipStream_t st);
 hipError_t launch_sampled(const AttnParams& p, int dtype, int G, hipStream_t st);
 
