@@ -1229,20 +1229,15 @@ __global__ __launch_bounds__(512, (sizeof(T) == 2 && G <= 4 ? 4 : 2)) void sampl
 
 // One workgroup per unit. The unit's draws are items [S, S + nc) of the
 // numbering; a record exists for the first item of each draw workgroup's
-// segment: item S, and every item k*per in (S, S + nc).  Each thread owns one
-// (head, dim) output and folds the unit's records into it in one pass with a
-// running maximum (every thread of a head sees the same records in the same
-// order, so they agree on the maximum and the normaliser); the loads of
-// kMergeRB records are in flight at a time, so a unit with up to that many
-// records costs one round trip after its schedule is known.
+// segment: item S, and every item k*per in (S, S + nc).
 template <int G>
 __global__ __launch_bounds__(512) void sampled_merge_kernel(const AttnParams p) {
-  constexpr int kMergeRB = 16;
+  constexpr int kBlk = 256;  // records staged per round
   constexpr int NE = (G * kD + 511) / 512;
   const int u = blockIdx.x;
   const int s = u / p.Hkv;
   const int g = u - s * p.Hkv;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int units = p.B * p.Hkv;
   const int mf = list_len(p, u);
   const int64_t n_s = (int64_t)p.n - mf;
@@ -1262,42 +1257,110 @@ __global__ __launch_bounds__(512) void sampled_merge_kernel(const AttnParams p) 
   if (nc > 0) nrec = 1 + max(0, (S + nc - 1) / per - k0 + 1);
   auto rc = [&](int r) { return r == 0 ? 0 : (k0 + r - 1) * per - S; };
 
+  __shared__ float s_pm[8][G];     // per wave: partial maxima
+  __shared__ float s_md[G];
+  __shared__ int s_c[kBlk];
+  __shared__ float s_rm[kBlk][G], s_rl[kBlk][G], s_f[kBlk][G];
+
+  // the exact part's values for this thread's outputs, loaded up front
+  double xM[NE], xD[NE], xN[NE];
 #pragma unroll
   for (int k = 0; k < NE; ++k) {
     const int e = tid + 512 * k;
-    if (e >= G * kD) break;
-    const int h = e / kD, dim = e - h * kD;
-    // the exact part's values for this output (fp64, natural-log shift xM)
-    const double xM = st[h], xD = st[G + h], xN = st[2 * G + e];
-    float M = kNegInf, a = 0.f, L = 0.f;  // M in log2 units, as the records
-    for (int r0 = 0; r0 < nrec; r0 += kMergeRB) {
-      float mv[kMergeRB], lv[kMergeRB], av[kMergeRB];
-#pragma unroll
-      for (int j = 0; j < kMergeRB; ++j) {
-        const int r = r0 + j;
-        const float* rh = rec + ((int64_t)rc(r < nrec ? r : 0) * G + h) * kDrawRec;  // record 0 always exists
-        mv[j] = rh[0];
-        lv[j] = rh[1];
-        av[j] = rh[4 + dim];
+    const int h = (e < G * kD ? e : 0) / kD;
+    xM[k] = st[h];
+    xD[k] = st[G + h];
+    xN[k] = e < G * kD ? st[2 * G + e] : 0.0;
+  }
+
+  // maximum of the record maxima per head; the first round's (m, l) stay in LDS
+  {
+    float mx = kNegInf;
+    for (int e = tid; e < nrec * G; e += 512) {
+      const int r = e / G, h = e - r * G;
+      const float* rh = rec + ((int64_t)rc(r) * G + h) * kDrawRec;
+      const float m = rh[0];
+      if (r < kBlk) {
+        s_rm[r][h] = m;
+        s_rl[r][h] = rh[1];
+        if (h == 0) s_c[r] = rc(r);
       }
+      mx = fmaxf(mx, m);
+    }
+    // 512 is a multiple of G: thread tid serves head tid % G throughout
+    for (int d = G; d < 64; d <<= 1) mx = fmaxf(mx, __shfl_xor(mx, d, 64));
+    if (lane < G) s_pm[w][lane] = mx;
+    __syncthreads();
+    if (tid < G) {
+      float m = kNegInf;
 #pragma unroll
-      for (int j = 0; j < kMergeRB; ++j) {
-        if (r0 + j < nrec) {
-          const float mn = fmaxf(M, mv[j]);
-          const float fo = rescale(M, mn), fs = rescale(mv[j], mn);
-          a = a * fo + av[j] * fs;
-          L = L * fo + lv[j] * fs;
-          M = mn;
+      for (int ww = 0; ww < 8; ++ww) m = fmaxf(m, s_pm[ww][tid]);
+      s_md[tid] = m;
+    }
+    __syncthreads();
+  }
+
+  float a[NE], L[NE];
+#pragma unroll
+  for (int k = 0; k < NE; ++k) a[k] = L[k] = 0.f;
+  for (int r0 = 0; r0 < nrec; r0 += kBlk) {
+    const int nb = min(kBlk, nrec - r0);
+    for (int e = tid; e < nb * G; e += 512) {
+      const int r = e / G, h = e - r * G;
+      float m, l;
+      if (r0 == 0) {
+        m = s_rm[r][h];
+        l = s_rl[r][h];
+      } else {
+        const int c = rc(r0 + r);
+        const float* rh = rec + ((int64_t)c * G + h) * kDrawRec;
+        m = rh[0];
+        l = rh[1];
+        if (h == 0) s_c[r] = c;
+      }
+      s_f[r][h] = rescale(m, s_md[h]);
+      if (r0 != 0) s_rl[r][h] = l;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NE; ++k) {
+      const int e = tid + 512 * k;
+      if (e < G * kD) {
+        const int h = e / kD, dim = e - h * kD;
+        int r = 0;
+        for (; r + 8 <= nb; r += 8) {
+          float v[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = rec[((int64_t)s_c[r + j] * G + h) * kDrawRec + 4 + dim];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            a[k] = fmaf(v[j], s_f[r + j][h], a[k]);
+            L[k] = fmaf(s_rl[r + j][h], s_f[r + j][h], L[k]);
+          }
+        }
+        for (; r < nb; ++r) {
+          a[k] = fmaf(rec[((int64_t)s_c[r] * G + h) * kDrawRec + 4 + dim], s_f[r][h], a[k]);
+          L[k] = fmaf(s_rl[r][h], s_f[r][h], L[k]);
         }
       }
     }
-    // back to the fp64 shift xM (natural units): exp(s - xM) = 2^(x' - xM log2 e)
-    const double sc = (L > 0.f) ? exp2((double)M - xM * 1.4426950408889634) : 0.0;
-    const double num = xN + fw * (double)a * sc;
-    const double den = xD + fw * (double)L * sc;
-    const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
-    p.out[qh * kD + dim] = den > 0.0 ? (float)(num / den) : 0.f;
-    if (dim == 0 && p.lse) p.lse[qh] = den > 0.0 ? (float)(xM + log(den)) : kNegInf;
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int k = 0; k < NE; ++k) {
+    const int e = tid + 512 * k;
+    if (e < G * kD) {
+      const int h = e / kD, dim = e - h * kD;
+      // back to the fp64 shift M (natural units): exp(s - M) = 2^(x' - M log2 e)
+      const double M = xM[k];
+      const double sc = (L[k] > 0.f) ? exp2((double)s_md[h] - M * 1.4426950408889634) : 0.0;
+      const double num = xN[k] + fw * (double)a[k] * sc;
+      const double den = xD[k] + fw * (double)L[k] * sc;
+      const int64_t qh = (int64_t)s * p.Hq + (int64_t)g * G + h;
+      p.out[qh * kD + dim] = den > 0.0 ? (float)(num / den) : 0.f;
+      if (dim == 0 && p.lse) p.lse[qh] = den > 0.0 ? (float)(M + log(den)) : kNegInf;
+    }
   }
 }
 
