@@ -67,7 +67,9 @@ def _load():
         "orc_draw_rank": (i64, [u64, i64, i64]),
         "orc_tail_pos": (i64, [_P, i32, i64]),
         "orc_budget_from_terms": (f64, [i32, i32, _P, _P, f64, _P, i64, f64, f64]),
+        "orc_budget_verified_from_terms": (f64, [i32, i32, _P, _P, f64, _P, i64, f64, i32, _P]),
         "orc_sampled": (i32, [D, _P, _P, _P, _P, _P, i32, f64, f64, i32, u64, _P, _P, _P, i32, _P, _P]),
+        "orc_sampled_verified": (i32, [D, _P, _P, _P, _P, _P, i32, f64, i32, _P, i32, u64, _P, _P, _P, i32, _P, _P]),
         "orc_sampled_fixed_b": (i32, [D, _P, _P, _P, _P, _P, i32, i32, i32, u64, _P, _P]),
         "orc_set_threads": (None, [i32]),
         "orc_get_threads": (i32, []),
@@ -250,6 +252,34 @@ def budget_from_terms(rD, rN, Df, Nf, n_s, eps, z):
     assert rN.shape == (b0, d)
     return float(_load().orc_budget_from_terms(d, b0, _ptr(rD), _ptr(rN), float(Df), _ptr(Nf),
                                                int(n_s), float(eps), float(z)))
+
+
+def budget_verified_from_terms(rD, rN, Df, Nf, n_s, eps, z_split):
+    """The verified budget of one head: z_split is an (nz, 2) array of
+    (Phi^-1(1 - d_N/2), Phi^-1(1 - d_D/2)) for splits d_N + d_D = delta."""
+    rD, rN, Nf = _c(rD), _c(rN), _c(Nf)
+    zs = _c(np.asarray(z_split, np.float64).reshape(-1, 2))
+    b0, d = rN.shape
+    return float(_load().orc_budget_verified_from_terms(d, b0, _ptr(rD), _ptr(rN), float(Df), _ptr(Nf),
+                                                        int(n_s), float(eps), zs.shape[0], _ptr(zs)))
+
+
+def sampled_verified(q, K, V, idx, eps, z_split, b0, seed, b_cap, idx_len=None, scale=None):
+    """The sampled estimator with the verified budget (see
+    budget_verified_from_terms); returns what sampled() returns."""
+    q, K, V = _c(q), _c(K), _c(V)
+    idx, idx_len = _c(idx, np.int32), _c(idx_len, np.int32)
+    zs = _c(np.asarray(z_split, np.float64).reshape(-1, 2))
+    D = _dims(q, K, scale)
+    out, lse = _out(D)
+    b = np.zeros((D.B, D.Hkv), np.int32)
+    bstar = np.zeros((D.B, D.Hkv), np.float64)
+    samples = np.full((D.B, D.Hkv, max(b_cap, 1)), -1, np.int32)
+    _check(_load().orc_sampled_verified(ctypes.byref(D), _ptr(q), _ptr(K), _ptr(V), _ptr(idx), _ptr(idx_len),
+                                        idx.shape[-1], float(eps), zs.shape[0], _ptr(zs), int(b0), int(seed),
+                                        _ptr(b), _ptr(bstar), _ptr(samples), int(b_cap), _ptr(out), _ptr(lse)),
+           "sampled_verified")
+    return {"b": b, "bstar": bstar, "samples": samples[..., :b_cap], "out": out, "lse": lse}
 
 
 def sampled(q, K, V, idx, eps, z, b0, seed, b_cap, idx_len=None, scale=None):

@@ -627,9 +627,13 @@ int64_t orc_tail_pos(const int32_t* If, int mf, int64_t u) {
   return prev + u;
 }
 
-double orc_budget_from_terms(int d, int b0, const double* rD, const double* rN,
-                             double Df, const double* Nf, int64_t n_s,
-                             double eps, double z) {
+/* The base sample's statistics for one head: the denominator terms'
+ * variance varD and estimate Dhat, the numerator terms' covariance trace trN
+ * and the estimate's norm normN (unbiased sample moments over b0 draws). */
+static void budget_stats(int d, int b0, const double* rD, const double* rN,
+                         double Df, const double* Nf, int64_t n_s,
+                         double* varD_out, double* Dhat_out, double* trN_out,
+                         double* normN_out) {
   double mD = 0.0;
   for (int k = 0; k < b0; ++k) mD += rD[k];
   mD /= (double)b0;
@@ -650,8 +654,17 @@ double orc_budget_from_terms(int d, int b0, const double* rD, const double* rN,
     normN2 += Nhat_i * Nhat_i;
   }
   trN /= (double)(b0 - 1);
-  double Dhat = Df + (double)n_s * mD;
-  double normN = sqrt(normN2);
+  *varD_out = varD;
+  *Dhat_out = Df + (double)n_s * mD;
+  *trN_out = trN;
+  *normN_out = sqrt(normN2);
+}
+
+double orc_budget_from_terms(int d, int b0, const double* rD, const double* rN,
+                             double Df, const double* Nf, int64_t n_s,
+                             double eps, double z) {
+  double varD, Dhat, trN, normN;
+  budget_stats(d, b0, rD, rN, Df, Nf, n_s, &varD, &Dhat, &trN, &normN);
 
   /* CLT lemma with tau = eps * |estimate|, for the denominator and the
    * numerator; the budget is the larger of the two (Lemma 4.2). */
@@ -671,6 +684,37 @@ double orc_budget_from_terms(int d, int b0, const double* rD, const double* rN,
   return bD > bN ? bD : bN;
 }
 
+double orc_budget_verified_from_terms(int d, int b0, const double* rD,
+                                      const double* rN, double Df,
+                                      const double* Nf, int64_t n_s, double eps,
+                                      int nz, const double* z_split) {
+  double varD, Dhat, trN, normN;
+  budget_stats(d, b0, rD, rN, Df, Nf, n_s, &varD, &Dhat, &trN, &normN);
+  /* The CLT lemma's budget for a target tau_X = e_X |X| at confidence
+   * 1 - d_X is (z_X n_s sigma_X / (e_X |X|))^2, z_X = Phi^-1(1 - d_X/2):
+   * with a = n_s sqrt(Tr) / |N| and c = n_s sigma_D / D, b_N = (z_N a / e_N)^2
+   * and b_D = (z_D c / e_D)^2.  Lemma 4.2 turns (e_N, d_N) and (e_D, d_D)
+   * into a relative error 2 (e_N + e_D) of the output with probability at
+   * least 1 - (d_N + d_D), so the output's (eps, delta) needs
+   * e_N + e_D = eps / 2 and d_N + d_D = delta.  For one split of delta,
+   * max(b_N, b_D) over e_N + e_D = eps / 2 is smallest where the two are
+   * equal, e_N / e_D = z_N a / (z_D c), which gives
+   * (2 (z_N a + z_D c) / eps)^2; the budget is the smallest of these over
+   * the given splits of delta (Theorem 4.3: the budget minimised over the
+   * allocation of (eps', delta')). */
+  double a = 0.0, c = 0.0;
+  if (trN > 0.0) a = normN > 0.0 ? (double)n_s * sqrt(trN) / normN : INFINITY;
+  if (varD > 0.0) c = (double)n_s * sqrt(varD) / Dhat;
+  double best = INFINITY;
+  for (int k = 0; k < nz; ++k) {
+    double t = 2.0 * (z_split[2 * k] * a + z_split[2 * k + 1] * c) / eps;
+    double v = t * t;
+    if (v < best) best = v;
+  }
+  if (a == 0.0 && c == 0.0) best = 0.0;
+  return best;
+}
+
 static int64_t budget_round(double bstar, int64_t n_s) {
   if (!(bstar < (double)n_s)) return n_s;  /* also catches inf / nan */
   double c = ceil(bstar);
@@ -688,13 +732,15 @@ static int check_sorted_set(const orc_dims* D, const int32_t* I, int len) {
   return 0;
 }
 
-int orc_sampled(const orc_dims* D, const void* q, const void* K, const void* V,
-                const int32_t* idx, const int32_t* idx_len, int m,
-                double eps, double z, int b0, uint64_t seed,
-                int32_t* b_out, double* bstar_out, int32_t* samples_out,
-                int b_cap, double* out, double* lse) {
-  if (check_dims(D) || m < 0 || b0 < 2 || !(eps > 0.0) || !(z > 0.0) || b_cap < 0)
-    return -1;
+static int sampled_impl(const orc_dims* D, const void* q, const void* K,
+                        const void* V, const int32_t* idx,
+                        const int32_t* idx_len, int m, double eps, double z,
+                        int nz, const double* z_split, int b0, uint64_t seed,
+                        int32_t* b_out, double* bstar_out, int32_t* samples_out,
+                        int b_cap, double* out, double* lse) {
+  if (check_dims(D) || m < 0 || b0 < 2 || !(eps > 0.0) || b_cap < 0) return -1;
+  if (nz == 0 && !(z > 0.0)) return -1;
+  if (nz < 0 || (nz > 0 && (!z_split || !(eps < 1.0)))) return -1;
   int G = D->Hq / D->Hkv, d = D->d;
   int U = D->B * D->Hkv;
   int err = 0;
@@ -760,7 +806,9 @@ int orc_sampled(const orc_dims* D, const void* q, const void* K, const void* V,
         for (int i = 0; i < d; ++i)
           rN[(int64_t)k * d + i] = e * elem(D->dtype, V, kv_row(D, s, g, jb[k]) + i);
       }
-      double bh = orc_budget_from_terms(d, b0, rD, rN, Df, Nf, n_s, eps, z);
+      double bh = nz > 0 ? orc_budget_verified_from_terms(d, b0, rD, rN, Df, Nf,
+                                                          n_s, eps, nz, z_split)
+                         : orc_budget_from_terms(d, b0, rD, rN, Df, Nf, n_s, eps, z);
       if (bh > bstar || bh != bh) bstar = bh;
     }
     int64_t b = budget_round(bstar, n_s);
@@ -792,6 +840,27 @@ int orc_sampled(const orc_dims* D, const void* q, const void* K, const void* V,
     free(jb); free(rD); free(rN); free(Nf);
   }
   return err ? -2 : 0;
+}
+
+int orc_sampled(const orc_dims* D, const void* q, const void* K, const void* V,
+                const int32_t* idx, const int32_t* idx_len, int m,
+                double eps, double z, int b0, uint64_t seed,
+                int32_t* b_out, double* bstar_out, int32_t* samples_out,
+                int b_cap, double* out, double* lse) {
+  return sampled_impl(D, q, K, V, idx, idx_len, m, eps, z, 0, NULL, b0, seed,
+                      b_out, bstar_out, samples_out, b_cap, out, lse);
+}
+
+int orc_sampled_verified(const orc_dims* D, const void* q, const void* K,
+                         const void* V, const int32_t* idx,
+                         const int32_t* idx_len, int m, double eps, int nz,
+                         const double* z_split, int b0, uint64_t seed,
+                         int32_t* b_out, double* bstar_out,
+                         int32_t* samples_out, int b_cap, double* out,
+                         double* lse) {
+  if (nz < 1) return -1;
+  return sampled_impl(D, q, K, V, idx, idx_len, m, eps, 0.0, nz, z_split, b0,
+                      seed, b_out, bstar_out, samples_out, b_cap, out, lse);
 }
 
 int orc_sampled_fixed_b(const orc_dims* D, const void* q, const void* K,

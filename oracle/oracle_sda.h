@@ -155,6 +155,18 @@ double orc_budget_from_terms(int d, int b0, const double* rD, const double* rN,
                              double Df, const double* Nf, int64_t n_s,
                              double eps, double z);
 
+/* Verified budget [vATT, verified-SDPA: Lemma 4.2 and Theorem 4.3] for one
+ * head from the same statistics: the output's relative error eps (< 1) at
+ * confidence 1 - delta, the smallest over the nz given splits
+ * delta = d_N + d_D of (2 (z_N a + z_D c) / eps)^2 with
+ * z_split[2k] = Phi^-1(1 - d_N/2), z_split[2k+1] = Phi^-1(1 - d_D/2),
+ * a = n_s sqrt(Tr Sigma_N) / |N_hat|, c = n_s sigma_D / D_hat (the eps split
+ * that balances b_N and b_D for each delta split). Returns the real budget. */
+double orc_budget_verified_from_terms(int d, int b0, const double* rD,
+                                      const double* rN, double Df,
+                                      const double* Nf, int64_t n_s, double eps,
+                                      int nz, const double* z_split);
+
 /* Full sampled estimator.  idx/idx_len carry the deterministic set I_f
  * (sorted ascending, distinct).  Per unit: b0 base draws give the budget
  * b = min(n_s, max(1, ceil(max over the group's heads of b*))); draws
@@ -167,6 +179,16 @@ int orc_sampled(const orc_dims* D, const void* q, const void* K, const void* V,
                 double eps, double z, int b0, uint64_t seed,
                 int32_t* b_out, double* bstar_out, int32_t* samples_out,
                 int b_cap, double* out, double* lse);
+
+/* The same with the verified budget (orc_budget_verified_from_terms per
+ * head; z_split holds nz >= 1 pairs, eps < 1). */
+int orc_sampled_verified(const orc_dims* D, const void* q, const void* K,
+                         const void* V, const int32_t* idx,
+                         const int32_t* idx_len, int m, double eps, int nz,
+                         const double* z_split, int b0, uint64_t seed,
+                         int32_t* b_out, double* bstar_out,
+                         int32_t* samples_out, int b_cap, double* out,
+                         double* lse);
 
 /* Estimator terms for a forced budget b (the unbiasedness study):
  * returns per query head the unnormalised, unshifted estimates

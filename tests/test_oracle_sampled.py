@@ -171,3 +171,126 @@ def test_ratio_error_coverage_is_reported(orc):
         err = np.linalg.norm(r["out"] - o_d, axis=-1) / np.linalg.norm(o_d, axis=-1)
         miss += int((err > 4 * w.eps).any())
     assert miss / S <= 3 * 2 * w.delta
+
+
+# ---------------------------------------------------------------------------
+# Verified budget (vAttention page, verified-SDPA: Lemma 4.2 composes the
+# numerator's (e_N, d_N) and the denominator's (e_D, d_D) guarantees into an
+# output error 2 (e_N + e_D) at confidence 1 - (d_N + d_D); Theorem 4.3
+# minimises the budget over that allocation).
+
+def _z_split(delta, K=32):
+    from statistics import NormalDist
+    nd = NormalDist()
+    s = np.arange(1, K) / K
+    return np.stack([[nd.inv_cdf(1 - x * delta / 2) for x in s],
+                     [nd.inv_cdf(1 - (1 - x) * delta / 2) for x in s]], axis=1)
+
+
+def _stats(rD, rN, Df, Nf, n_s):
+    """The base sample's statistics, from numpy's sample moments."""
+    varD = np.var(rD, ddof=1)
+    Dhat = Df + n_s * rD.mean()
+    trN = np.var(rN, axis=0, ddof=1).sum()
+    normN = np.linalg.norm(Nf + n_s * rN.mean(axis=0))
+    return varD, Dhat, trN, normN
+
+
+def _random_terms(rng, b0=64, d=16, spread=1.0):
+    rD = np.exp(rng.normal(-2.0, spread, size=b0))
+    rN = rD[:, None] * rng.normal(0.0, 1.0, size=(b0, d))
+    Df = float(np.exp(rng.normal(0.0, 0.5, size=8)).sum())
+    Nf = rng.normal(0.0, 1.0, size=d) * Df
+    return rD, rN, Df, Nf
+
+
+def test_verified_budget_is_the_best_allocation(orc):
+    """Brute force over the allocation: for every split of delta and a fine
+    grid of e_N in (0, eps/2) (e_D = eps/2 - e_N), the larger of the two CLT
+    budgets (the lemma as printed: b >= (z n_s sqrt(Tr) / tau)^2 with
+    tau = e |X|); the smallest over the grid is the oracle's budget from
+    above, to the grid's resolution."""
+    rng = np.random.default_rng(7)
+    for trial in range(12):
+        rD, rN, Df, Nf = _random_terms(rng, spread=0.5 + 0.2 * trial)
+        n_s, eps, delta = int(rng.integers(1000, 200000)), float(rng.uniform(0.02, 0.3)), 0.05
+        zs = _z_split(delta)
+        b = orc.budget_verified_from_terms(rD, rN, Df, Nf, n_s, eps, zs)
+        varD, Dhat, trN, normN = _stats(rD, rN, Df, Nf, n_s)
+        eN = np.linspace(0, eps / 2, 40001)[1:-1]
+        eD = eps / 2 - eN
+        brute = np.inf
+        for zN, zD in zs:
+            bN = (zN * n_s * np.sqrt(trN) / (eN * normN)) ** 2
+            bD = (zD * n_s * np.sqrt(varD) / (eD * Dhat)) ** 2
+            brute = min(brute, np.maximum(bN, bD).min())
+        assert b <= brute * (1 + 1e-9), trial
+        assert brute <= b * (1 + 2e-3), trial
+
+
+def test_verified_budget_with_one_part_exact(orc):
+    """Equal denominator terms (no variance): only the numerator needs draws,
+    and the best split gives it the largest share of delta, so the budget is
+    (2 z n_s sqrt(Tr) / (eps |N|))^2 at the smallest z of the table."""
+    rng = np.random.default_rng(8)
+    rD, rN, Df, Nf = _random_terms(rng)
+    rD = np.full_like(rD, 0.25)
+    n_s, eps = 50000, 0.1
+    zs = _z_split(0.05)
+    b = orc.budget_verified_from_terms(rD, rN, Df, Nf, n_s, eps, zs)
+    _, _, trN, normN = _stats(rD, rN, Df, Nf, n_s)
+    expect = (2 * zs[:, 0].min() * n_s * np.sqrt(trN) / (eps * normN)) ** 2
+    assert b == pytest.approx(expect, rel=1e-12)
+    # and a single draw when every term is the same (the sample moments'
+    # rounding leaves a trace many orders of magnitude below one draw)
+    rN1 = np.broadcast_to(rN[:1], rN.shape).copy()
+    assert orc.budget_verified_from_terms(rD, rN1, Df, Nf, n_s, eps, zs) < 1e-12
+
+
+def test_verified_budget_exceeds_the_per_part_budget(orc):
+    """Each part's guarantee is tighter than (eps, delta) itself (e_X <
+    eps/2, d_X < delta), so the verified budget is at least four times the
+    plain max(b_N, b_D) at (eps, Phi^-1(1 - delta/2))."""
+    from statistics import NormalDist
+    rng = np.random.default_rng(9)
+    for _ in range(10):
+        rD, rN, Df, Nf = _random_terms(rng)
+        n_s, eps, delta = 30000, 0.05, 0.05
+        z = NormalDist().inv_cdf(1 - delta / 2)
+        plain = orc.budget_from_terms(rD, rN, Df, Nf, n_s, eps, z)
+        ver = orc.budget_verified_from_terms(rD, rN, Df, Nf, n_s, eps, _z_split(delta))
+        assert ver >= 4 * plain
+
+
+def test_sampled_verified_follows_the_per_head_budget(orc):
+    """The estimator with the verified budget: b is the rounded maximum over
+    the group's heads of the per-head verified budget, the samples are the
+    same stream, and b is at least the plain estimator's."""
+    w = _small_workload()
+    c = synth.make_case(w)
+    zs = _z_split(w.delta)
+    r = orc.sampled_verified(c.q, c.K, c.V, c.idx, w.eps, zs, w.b0, w.sampler_seed, b_cap=64)
+    rp = orc.sampled(c.q, c.K, c.V, c.idx, w.eps, w.z, w.b0, w.sampler_seed, b_cap=64)
+    n_s = w.n - w.m
+    qf = synth.bf16_bits_to_f32(c.q).astype(np.float64)
+    Kf = synth.bf16_bits_to_f32(c.K).astype(np.float64)
+    Vf = synth.bf16_bits_to_f32(c.V).astype(np.float64)
+    scale = np.float64(np.float32(1 / np.sqrt(w.d)))
+    for g in range(w.Hkv):
+        key = orc.unit_key(w.sampler_seed, g)
+        If = c.idx[0, g]
+        jb = [orc.tail_pos(If, orc.draw_rank(key, k, n_s)) for k in range(w.b0)]
+        best = 0.0
+        for hh in range(w.G):
+            h = g * w.G + hh
+            sI = Kf[0, g, If] @ qf[0, h] * scale
+            sB = Kf[0, g, jb] @ qf[0, h] * scale
+            M = max(sI.max(), sB.max())
+            eI, eB = np.exp(sI - M), np.exp(sB - M)
+            best = max(best, orc.budget_verified_from_terms(eB, eB[:, None] * Vf[0, g, jb], eI.sum(),
+                                                             eI @ Vf[0, g, If], n_s, w.eps, zs))
+        assert r["bstar"][0, g] == pytest.approx(best, rel=1e-12)
+        assert int(r["b"][0, g]) == min(n_s, max(1, int(np.ceil(best))))
+        assert r["b"][0, g] >= rp["b"][0, g]
+        k = min(64, int(r["b"][0, g]), int(rp["b"][0, g]))
+        assert (r["samples"][0, g, :k] == rp["samples"][0, g, :k]).all()
