@@ -164,7 +164,23 @@ typedef struct {
   double* bstar_out;             /* [B,Hkv] real budget before rounding, or
                                     NULL                                     */
   int32_t* samples_out;          /* [B,Hkv,b_cap] drawn positions, or NULL  */
+
+  /* SAMPLED, verified budget ("vAttention: Verified Sparse Attention via
+   * Sampling", method section 3, verified-SDPA: Lemma 4.2 turns the
+   * numerator's (e_N, d_N) and the denominator's (e_D, d_D) guarantees into
+   * an output error 2 (e_N + e_D) |N/D| at confidence 1 - (d_N + d_D), and
+   * Theorem 4.3 minimises the budget over that allocation).  With nz > 0,
+   * eps and delta bound the output itself: per head the budget is the
+   * smallest over the nz given splits delta = d_N + d_D of
+   * (2 (z_N a + z_D c) / eps)^2, a = n_s sqrt(Tr Sigma_N) / |N_hat|,
+   * c = n_s sigma_D / D_hat (the split of eps / 2 that balances b_N and b_D),
+   * with z_split[2k] = Phi^-1(1 - d_N/2) and z_split[2k+1] =
+   * Phi^-1(1 - d_D/2) for the k-th split; eps < 1, every entry > 0, z is
+   * ignored.  nz = 0 keeps the budget above. */
+  int32_t nz;                    /* 0..SDA_MAX_Z_SPLITS                      */
+  const double* z_split;         /* HOST array [nz][2], read during the call */
 } sda_tail;
+#define SDA_MAX_Z_SPLITS 64
 
 typedef enum {
   SDA_OP_SPARSE = 0,

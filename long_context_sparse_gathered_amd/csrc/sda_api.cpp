@@ -443,7 +443,20 @@ sda_status sparse_decode(const sda_dims* dims, const void* q, const void* K, con
     p.lambda = tail->lambda;
     p.prior_n = tail->prior_n > 0 ? tail->prior_n : r.n;
   } else if (kind == SDA_TAIL_SAMPLED) {
-    if (!(tail->eps > 0.0) || !(tail->z > 0.0) || !isfinite(tail->eps) || !isfinite(tail->z)) return SDA_EINVAL;
+    if (!(tail->eps > 0.0) || !isfinite(tail->eps)) return SDA_EINVAL;
+    if (tail->nz < 0 || tail->nz > SDA_MAX_Z_SPLITS) return SDA_EINVAL;
+    if (tail->nz == 0) {
+      if (!(tail->z > 0.0) || !isfinite(tail->z)) return SDA_EINVAL;
+    } else {
+      // the verified budget: eps bounds the output's relative error (< 1)
+      if (!tail->z_split || !(tail->eps < 1.0)) return SDA_EINVAL;
+      for (int k = 0; k < 2 * tail->nz; ++k) {
+        const double zk = tail->z_split[k];
+        if (!(zk > 0.0) || !isfinite(zk)) return SDA_EINVAL;
+        p.zs[k] = zk;
+      }
+      p.nz = tail->nz;
+    }
     if (tail->b0 < 2 || tail->b0 > kSampMaxB0) return SDA_EUNSUPPORTED;
     if (tail->b_cap < 0 || (tail->samples_out && tail->b_cap == 0)) return SDA_EINVAL;
     p.scale = r.scale;

@@ -55,6 +55,8 @@ struct AttnParams {
   int32_t* b_out;              // [B,Hkv] or null
   double* bstar_out;           // [B,Hkv] or null
   int32_t* samples_out;        // [B,Hkv,b_cap] or null
+  int32_t nz;                  // verified budget: splits of delta (0 = the plain budget)
+  double zs[2 * SDA_MAX_Z_SPLITS];  // per split (Phi^-1(1 - d_N/2), Phi^-1(1 - d_D/2))
   double* wstat;               // workspace: [units, G*(2 + d)] fp64 M, D_f, N_f of the exact part
   double* wexact;              // workspace: [units, splits, G*(2 + d)] fp64 records of the I_f shares
   double* wbase;               // workspace: [units, G*(4 + d)] fp64 moments of the base draws

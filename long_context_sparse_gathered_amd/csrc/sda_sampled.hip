@@ -25,6 +25,8 @@
 //   sampled_merge_kernel  one workgroup per unit: log-sum-exp merge of the
 //                         draw partials, then num = N_f + (n_s/b) N_dyn and
 //                         den = D_f + (n_s/b) D_dyn in fp64.
+// With a table of delta splits (nz > 0) the budget is the verified one
+// (budget_verified: eps and delta bound the output, not each sum).
 // Everything the budget depends on -- logits, weights, sums, variances -- is
 // fp64, so the integer budget matches an fp64 reference up to the summation
 // order.  The fresh draws feed only the output.
@@ -246,6 +248,27 @@ __device__ double budget_of(double z, double eps, double n_s, double varD, doubl
     }
   }
   return bD > bN ? bD : bN;
+}
+
+// The verified budget of one head ("vAttention", verified-SDPA: Lemma 4.2
+// and Theorem 4.3): for each given split delta = d_N + d_D the split of eps/2
+// that balances the numerator's and the denominator's CLT budgets gives
+// (2 (z_N a + z_D c) / eps)^2, with a = n_s sqrt(Tr) / |N_hat| and
+// c = n_s sigma_D / D_hat; the budget is the smallest over the splits.
+__device__ double budget_verified(const double* zs, int nz, double eps, double n_s, double varD, double Dhat,
+                                  double trN, double normN) {
+#pragma clang fp contract(off)
+  double a = 0.0, c = 0.0;
+  if (trN > 0.0) a = normN > 0.0 ? n_s * sqrt(trN) / normN : __builtin_huge_val();
+  if (varD > 0.0) c = n_s * sqrt(varD) / Dhat;
+  double best = __builtin_huge_val();
+  for (int k = 0; k < nz; ++k) {
+    const double t = 2.0 * (zs[2 * k] * a + zs[2 * k + 1] * c) / eps;
+    const double v = t * t;
+    if (v < best) best = v;
+  }
+  if (a == 0.0 && c == 0.0) best = 0.0;
+  return best;
 }
 
 }  // namespace
@@ -873,7 +896,8 @@ __global__ __launch_bounds__(256) void sampled_budget_kernel(const AttnParams p)
       const double trN = fb * fb * s_sc[2 * splits + 3][h] / (double)(b0 - 1);
       const double normN = sqrt(s_hs[h][0] + s_hs[h][1]);
       const double Dhat = s_Df[h] + (double)n_s * mD;
-      bh = budget_of(p.z, p.eps, (double)n_s, varD, Dhat, trN, normN);
+      bh = p.nz > 0 ? budget_verified(p.zs, p.nz, p.eps, (double)n_s, varD, Dhat, trN, normN)
+                    : budget_of(p.z, p.eps, (double)n_s, varD, Dhat, trN, normN);
     }
     s_bh[h] = bh;
     st[h] = s_M[h];

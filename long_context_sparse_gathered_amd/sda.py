@@ -56,7 +56,7 @@ class Tail(ctypes.Structure):
                 ("lam", ctypes.c_float), ("prior_n", ctypes.c_int32),
                 ("eps", ctypes.c_double), ("z", ctypes.c_double), ("b0", ctypes.c_int32),
                 ("seed", ctypes.c_uint64), ("b_cap", ctypes.c_int32), ("b_out", _vp), ("bstar_out", _vp),
-                ("samples_out", _vp)]
+                ("samples_out", _vp), ("nz", ctypes.c_int32), ("z_split", _vp)]
 
 
 class Selector(ctypes.Structure):
@@ -261,9 +261,19 @@ class SampledTail:
     bstar: Optional[torch.Tensor] = None     # [B,Hkv] float64 (output)
     samples: Optional[torch.Tensor] = None   # [B,Hkv,b_cap] int32 (output)
 
+    verified: bool = False                   # eps, delta bound the output (verified budget)
+    splits: int = 32                         # delta split into d_N = k delta / splits, k = 1 .. splits-1
+
     @property
     def z(self) -> float:
         return NormalDist().inv_cdf(1.0 - self.delta / 2.0)
+
+    @property
+    def z_split(self):
+        """(Phi^-1(1 - d_N/2), Phi^-1(1 - d_D/2)) per split of delta."""
+        nd = NormalDist()
+        fr = [k / self.splits for k in range(1, self.splits)]
+        return [(nd.inv_cdf(1.0 - f * self.delta / 2.0), nd.inv_cdf(1.0 - (1.0 - f) * self.delta / 2.0)) for f in fr]
 
 
 def _tail_struct(tail, idx_cluster, cluster_id, lam, keep, B, Hq, Hkv, n, d, m, device) -> Tail:
@@ -297,6 +307,11 @@ def _tail_struct(tail, idx_cluster, cluster_id, lam, keep, B, Hq, Hkv, n, d, m, 
         _opt(tail.samples, "samples", dtype=torch.int32, shape=(B, Hkv, tail.b_cap), device=device)
         t.eps, t.z, t.b0, t.seed, t.b_cap = tail.eps, tail.z, tail.b0, tail.seed & (2**64 - 1), tail.b_cap
         t.b_out, t.bstar_out, t.samples_out = _ptr(tail.b), _ptr(tail.bstar), _ptr(tail.samples)
+        if tail.verified:
+            zs = [v for pair in tail.z_split for v in pair]
+            buf = (ctypes.c_double * len(zs))(*zs)
+            keep.append(buf)  # host table, read during the call
+            t.nz, t.z_split = len(zs) // 2, ctypes.cast(buf, _vp)
     else:
         raise TypeError("tail must be None, ProxyState, PriorState or SampledTail")
     keep.append(t)

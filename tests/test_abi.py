@@ -245,3 +245,26 @@ def test_gather_rows_validation(L):
     assert call(_dims(), state=FAKE, sbytes=24) == sda.SDA_EINVAL      # not a multiple of 16
     assert call(_dims(), state=MISALIGNED, sbytes=32) == sda.SDA_EINVAL
     assert call(_dims(), m=-1) == sda.SDA_ESHAPE
+
+
+def test_verified_budget_validation(L):
+    """The verified sampled budget's host checks (nothing launches): a split
+    count outside 0..SDA_MAX_Z_SPLITS, a missing table, eps >= 1 (the
+    output's relative error), a table entry that is not a positive z."""
+    dims = _dims()
+    zs = (ctypes.c_double * 4)(2.2, 2.0, 2.0, 2.2)
+
+    def call(nz, table, eps=0.05, z=0.0):
+        t = sda.Tail()
+        t.kind, t.eps, t.z, t.b0 = sda.TAIL_SAMPLED, eps, z, 64
+        t.nz, t.z_split = nz, (ctypes.cast(table, ctypes.c_void_p) if table is not None else None)
+        return _sparse(L, dims, tail=t, m=16)
+    assert call(-1, zs) == sda.SDA_EINVAL
+    assert call(65, zs) == sda.SDA_EINVAL
+    assert call(2, None) == sda.SDA_EINVAL
+    assert call(2, zs, eps=1.0) == sda.SDA_EINVAL
+    bad = (ctypes.c_double * 4)(2.2, 0.0, 2.0, 2.2)
+    assert call(2, bad) == sda.SDA_EINVAL
+    nan = (ctypes.c_double * 4)(2.2, float("nan"), 2.0, 2.2)
+    assert call(2, nan) == sda.SDA_EINVAL
+    assert call(0, None, z=0.0) == sda.SDA_EINVAL  # the plain budget still needs z

@@ -131,3 +131,37 @@ def test_sampled_group_sizes(orc, hq, hkv):
     w = synth.WORKLOADS["sampled_bf16_b8_n64k"].replace(B=2, Hq=hq, Hkv=hkv, n=6000, n_top=60)
     c = synth.make_case(w)
     _check(orc, c, w, 5, b_cap=4096, tol=2e-3)
+
+
+@pytest.mark.parametrize("eps", [0.2, 0.4])
+def test_sampled_verified_budget(orc, eps):
+    """The verified budget ("vAttention", verified-SDPA: eps and delta bound
+    the output through Lemma 4.2, the budget minimised over the allocation as
+    Theorem 4.3 states): budgets, draws and output against the oracle's
+    verified estimator, and every budget at least the plain one."""
+    from statistics import NormalDist
+    w = synth.WORKLOADS["sampled_bf16_b8_n64k"].replace(B=2, n=8192, n_top=82, eps=eps)
+    c = synth.make_case(w)
+    d = case_to_dev(c)
+    tail = sda.SampledTail(eps=w.eps, delta=w.delta, b0=w.b0, seed=w.sampler_seed, b_cap=8192, verified=True)
+    nd = NormalDist()
+    zs = np.array([(nd.inv_cdf(1 - k / 32 * w.delta / 2), nd.inv_cdf(1 - (1 - k / 32) * w.delta / 2))
+                   for k in range(1, 32)])
+    assert np.array_equal(np.array(tail.z_split), zs)
+    out, lse = sda.sparse_decode_attn(d["q"], d["K"], d["V"], d["idx"], tail=tail)
+    torch.cuda.synchronize()
+    ref = orc.sampled_verified(c.q, c.K, c.V, c.idx, w.eps, zs, w.b0, w.sampler_seed, 8192)
+    assert not _ties(ref["bstar"]).any()
+    np.testing.assert_array_equal(tail.b.cpu().numpy(), ref["b"])
+    np.testing.assert_allclose(tail.bstar.cpu().numpy(), ref["bstar"], rtol=1e-12, atol=1e-9)
+    got = tail.samples.cpu().numpy()
+    for s in range(w.B):
+        for g in range(w.Hkv):
+            k = min(int(ref["b"][s, g]), 8192)
+            np.testing.assert_array_equal(got[s, g, :k], ref["samples"][s, g, :k])
+    assert rel_err(out, ref["out"]) <= 2e-3
+    assert lse_err(lse, ref["lse"]) <= 1e-3
+    plain = sda.SampledTail(eps=w.eps, delta=w.delta, b0=w.b0, seed=w.sampler_seed)
+    sda.sparse_decode_attn(d["q"], d["K"], d["V"], d["idx"], tail=plain)
+    torch.cuda.synchronize()
+    assert (tail.b.cpu().numpy() >= plain.b.cpu().numpy()).all()
