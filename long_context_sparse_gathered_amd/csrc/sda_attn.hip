@@ -12,13 +12,17 @@
 //  sparse_unit_mfma_kernel the same for bf16 rows with eight query heads per
 //                          KV head: value tiles staged in LDS.
 //  stream_kernel,          split-K streaming kernels with an online softmax;
-//  stream_mfma_kernel      they serve plain sparse lists, the rank-1 prior
-//                          ("RESA", Online Aggregator), dense decode and the
+//  stream_dma_kernel,      they serve plain sparse lists, the rank-1 prior
+//  stream_mfma_kernel      ("RESA", Online Aggregator), dense decode and the
 //                          prior build ("RESA", Prior Estimator: one extra
-//                          query over the whole cache); the matrix-core one
-//                          also takes proxy-tail lists longer than one
-//                          workgroup holds, each split keeping per-cluster
-//                          listed counts, logit sums and value sums.
+//                          query over the whole cache). stream_kernel: fp32
+//                          rows and the build; stream_dma_kernel: bf16 plain
+//                          lists, prior and dense on the matrix cores, values
+//                          staged by direct-to-LDS loads, two batches in
+//                          flight per wave; stream_mfma_kernel: bf16
+//                          proxy-tail lists longer than one workgroup holds,
+//                          each split keeping per-cluster listed counts,
+//                          logit sums and value sums.
 //  merge_kernel            log-sum-exp merge of split partials + the prior's
 //                          delta merge.
 //  merge_proxy_kernel      merge of proxy-mode splits: adds the per-cluster
