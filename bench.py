@@ -564,6 +564,28 @@ def measure_rows(a, dev):
                                                  ref["samples"][s, g, :int(ref["b"][s, g])])
                                   for s in range(w.B) for g in range(w.Hkv))
     err = rel_err(o.cpu().double().numpy(), ref["out"])
+    # the verified budget (eps and delta bound the output; the smallest budget
+    # over 31 splits of delta): timed on the same step, budgets and draws
+    # of every unit against the oracle's verified estimator
+    vt = sda.SampledTail(eps=w.eps, delta=w.delta, b0=w.b0, seed=w.sampler_seed, b_cap=b_cap, verified=True)
+    sda.sparse_decode_attn(q, K, V, idx, tail=vt, out=o, lse=lse, ws=ws)
+    torch.cuda.synchronize()
+    vref = oracle.sampled_verified(c.q, c.K, c.V, c.idx, w.eps, vt.z_split, w.b0, w.sampler_seed, b_cap)
+    vb = vt.b.cpu().numpy()
+    vsamp = vt.samples.cpu().numpy()
+    v_exact = bool(np.array_equal(vb, vref["b"])) and all(
+        np.array_equal(vsamp[s, g, :int(vb[s, g])], vref["samples"][s, g, :int(vb[s, g])])
+        for s in range(w.B) for g in range(w.Hkv))
+    v_err = rel_err(o.cpu().double().numpy(), vref["out"])
+    vtime = sda.SampledTail(eps=w.eps, delta=w.delta, b0=w.b0, seed=w.sampler_seed, b_cap=0, verified=True)
+    vms, vper = time_steps(lambda i: sda.sparse_decode_attn(q, copies[i % ncopy][0], copies[i % ncopy][1], idx,
+                                                            tail=vtime, out=o, ws=ws), 20, 3, graph=not a.no_graph,
+                           repeats=a.repeats)
+    verified = {"us_per_step": round(vms * 1e3, 3), "mean_budget_b": round(float(vb.mean()), 1),
+                "units_reading_whole_tail": int((vb >= w.n - w.m).sum()),
+                "budget_and_draws_bit_exact": v_exact, "max_rel_err": v_err,
+                "note": "eps = delta = 0.05 on the attention output (Lemma 4.2 + Theorem 4.3 allocation)"}
+    del vref, vsamp
     dms = None if a.no_dense else dense_time(dev, q, copies, w.Hq, 5, o, lse)
     units = w.B * w.Hkv
     rows = units * (w.m + w.b0) * 2 + b_sum * 2
@@ -573,7 +595,7 @@ def measure_rows(a, dev):
         ms, gathered, by, dms, m=w.m, mean_budget_b=round(b_sum / units, 1),
         repeats_us=[round(x * 1e3, 3) for x in per], max_rel_err=err, units_checked=units,
         budget_bit_exact=b_exact, draws_bit_exact=draws_exact, budget_ties=ties,
-        draws_gather_ceiling=draws_gather_ceiling(a, copies, b_sum),
+        draws_gather_ceiling=draws_gather_ceiling(a, copies, b_sum), verified_budget=verified,
         note="gathered = I_f, the b0 base draws and the b fresh draws (K and V rows)")
     B1 = 2
     name, rec = oracle_path(
