@@ -309,7 +309,11 @@ sda_status sda_build_qgc_clusters(const sda_dims* dims, const void* K, const flo
  * second moment).  For every row: y_j = U^T k_j, summed over d in order in
  * fp64 (each product is exact); kmax [B,Hkv,32] fp64 = max_j |y_ji|;
  * codes [B,Hkv,n,32] int8 = rint(127 y_ji / kmax_i), half to even, 0 where
- * kmax_i = 0.  K and codes 16-byte aligned.  Workspace: SDA_OP_BUILD_QGS. */
+ * kmax_i = 0.  K and codes 16-byte aligned.  Workspace: SDA_OP_BUILD_QGS
+ * gives the size with room for the fp64 projections (B*Hkv*n*32*8 bytes
+ * beyond the chunk maxima), which spares the quantizing pass recomputing
+ * them; a workspace of only the chunk maxima's size (rounded up to 256 bytes)
+ * is accepted and recomputes them (the same codes, bit for bit). */
 sda_status sda_build_qgs_codes(const sda_dims* dims, const void* K, const float* U,
                                int8_t* codes, double* kmax, void* ws, size_t ws_bytes,
                                void* stream);

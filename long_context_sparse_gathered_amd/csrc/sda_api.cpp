@@ -210,8 +210,13 @@ size_t proxy_ws(const Resolved& r, int C) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The chunk maxima (required), then room for the fp64 projections, which
+// spares the second pass their recomputation when the workspace holds them.
+size_t qgs_build_ws_min(const Resolved& r) {
+  return align256((size_t)r.B * r.Hkv * qgs_chunks(r.n) * kQgsRank * sizeof(double));
+}
 size_t qgs_build_ws(const Resolved& r) {
-  return (size_t)r.B * r.Hkv * qgs_chunks(r.n) * kQgsRank * sizeof(double);
+  return qgs_build_ws_min(r) + (size_t)r.B * r.Hkv * r.n * kQgsRank * sizeof(double);
 }
 
 struct QgsSelectWs {
@@ -580,7 +585,7 @@ SDA_EXPORT sda_status sda_build_qgs_codes(const sda_dims* dims, const void* K, c
   if (st != SDA_OK) return st;
   if (!K || !U || !codes || !kmax) return SDA_EINVAL;
   if (!aligned16(K) || !aligned16(codes)) return SDA_EINVAL;
-  const size_t need = qgs_build_ws(r);
+  const size_t need = qgs_build_ws_min(r);
   if (!ws || ws_bytes < need) return SDA_EWORKSPACE;
   QgsBuildParams p;
   memset(&p, 0, sizeof(p));
@@ -593,6 +598,7 @@ SDA_EXPORT sda_status sda_build_qgs_codes(const sda_dims* dims, const void* K, c
   p.n = r.n;
   p.chunks = qgs_chunks(r.n);
   p.part = reinterpret_cast<double*>(ws);
+  p.y = ws_bytes >= qgs_build_ws(r) ? reinterpret_cast<double*>(reinterpret_cast<char*>(ws) + need) : nullptr;
   p.codes = codes;
   p.kmax = kmax;
   return hip_status(launch_qgs_build(p, r.dtype, r.B * r.Hkv, reinterpret_cast<hipStream_t>(stream)));

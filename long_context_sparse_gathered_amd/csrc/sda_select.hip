@@ -110,9 +110,11 @@ __device__ __forceinline__ double wave_max_f64(double v) {
 
 // ---------------------------------------------------------------------------
 // Build: projections y_j = U^T k_j and their int8 codes, in three launches:
-// pass 1 (QUANT = false) writes each (unit, chunk)'s maxima of |y_i|; a small
-// kernel reduces them to kmax_i per unit; pass 2 recomputes the projections
-// and writes code_ji = rint(127 y_ji / kmax_i).  The basis sits in LDS in
+// pass 1 (QUANT = false) writes each (unit, chunk)'s maxima of |y_i| and,
+// when the workspace holds them, the projections themselves (fp64); a small
+// kernel reduces the maxima to kmax_i per unit; pass 2 reads the kept
+// projections (or recomputes them, bit for bit the same) and writes
+// code_ji = rint(127 y_ji / kmax_i).  The basis sits in LDS in
 // fp64; the chunk's keys pass through LDS 32 dimensions at a time (read from
 // HBM once, coalesced).  A lane owns 4 rows x 8 coordinates (lane & 3 picks
 // the coordinates), so every LDS read serves several products; each
@@ -132,16 +134,29 @@ __global__ __launch_bounds__(256) void qgs_code_kernel(const QgsBuildParams p) {
   const int cg = tid & 3, rg = tid >> 2;    // coordinates 8cg..8cg+7, rows 4rg..4rg+3 of the chunk
 
   const float* Uu = p.U + (int64_t)u * kD * kQgsRank;
-  for (int i = tid; i < kD * kQgsRank; i += 256) s_u[i] = (double)Uu[i];
+  if (!(QUANT && p.y))
+    for (int i = tid; i < kD * kQgsRank; i += 256) s_u[i] = (double)Uu[i];
   if (QUANT && tid < kQgsRank) s_kmax[tid] = p.kmax[(int64_t)u * kQgsRank + tid];
 
   const int row0 = ch * kQgsRows;
+  const int j0 = row0 + 4 * rg;
   const T* kbase = reinterpret_cast<const T*>(p.K) + (int64_t)s * p.sb + (int64_t)g * p.sh;
   double acc[4][8];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[r][i] = 0.0;
+  if (QUANT && p.y) {
+    // the projections pass 1 kept
+    __syncthreads();  // s_kmax in place
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int j = min(j0 + r, p.n - 1);
+      const double* yr = p.y + ((int64_t)u * p.n + j) * kQgsRank + 8 * cg;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[r][i] = __builtin_nontemporal_load(yr + i);
+    }
+  } else {
   for (int d0 = 0; d0 < kD; d0 += kCodeDims) {
     __syncthreads();   // the previous step's keys are consumed (and the basis is in place)
     // 256 rows x 32 dims: four lanes per row, 8 elements each, in 4 sweeps of 64 rows
@@ -172,9 +187,18 @@ __global__ __launch_bounds__(256) void qgs_code_kernel(const QgsBuildParams p) {
       }
     }
   }
+  }  // projections computed
 
-  const int j0 = row0 + 4 * rg;
   if constexpr (!QUANT) {
+    if (p.y) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (j0 + r >= p.n) break;
+        double* yr = p.y + ((int64_t)u * p.n + j0 + r) * kQgsRank + 8 * cg;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) __builtin_nontemporal_store(acc[r][i], yr + i);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       double v = 0.0;

@@ -31,6 +31,7 @@ struct QgsBuildParams {
   int32_t Hkv, n;
   int32_t chunks;              // row chunks of kQgsRows per unit
   double* part;                // [units, chunks, r] chunk maxima of |y|
+  double* y;                   // [units, n, r] projections kept by pass 1 for pass 2, or null (recomputed)
   int8_t* codes;               // [units, n, r]
   double* kmax;                // [units, r]
 };

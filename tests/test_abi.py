@@ -171,8 +171,11 @@ def test_selector_validation(L):
     assert L.sda_build_qgs_codes(ctypes.byref(dims), MISALIGNED, FAKE, FAKE, FAKE, FAKE, 1 << 30,
                                  None) == sda.SDA_EINVAL
     need = L.sda_workspace_bytes(ctypes.byref(dims), sda.OP_BUILD_QGS, 0, 0, 0)
-    assert need == 2 * 2 * (1024 // 256) * 32 * 8          # fp64 chunk maxima per (unit, chunk, coordinate)
-    assert L.sda_build_qgs_codes(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, need - 1,
+    # fp64 chunk maxima per (unit, chunk, coordinate), rounded up to 256
+    # bytes, then the fp64 projections per (unit, row, coordinate)
+    least = (2 * 2 * (1024 // 256) * 32 * 8 + 255) // 256 * 256
+    assert need == least + 2 * 2 * 1024 * 32 * 8
+    assert L.sda_build_qgs_codes(ctypes.byref(dims), FAKE, FAKE, FAKE, FAKE, FAKE, least - 1,
                                  None) == sda.SDA_EWORKSPACE
 
     def sel(**kw):

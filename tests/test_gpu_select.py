@@ -102,6 +102,35 @@ def test_codes_and_maxima_bit_exact():
             np.testing.assert_array_equal(codes[s, g], oc)
 
 
+def test_codes_without_room_for_the_projections():
+    """A workspace that holds only the chunk maxima: the quantizing pass
+    recomputes the projections and the codes and kmax are the same bits as
+    with the projections kept (and as the oracle's)."""
+    import ctypes
+    w = _workload(B=2, Hkv=2, Hq=8, n=3001, n_top=40, C=8)
+    c = synth.make_case(w)
+    K, U = to_dev(c.K), to_dev(c.U)
+    full = sda.build_qgs_codes(K, U)
+    dims = sda.make_dims(K, 1)
+    dims.Hq = dims.Hkv
+    need = sda.workspace_bytes(dims, sda.OP_BUILD_QGS)
+    small = need - w.B * w.Hkv * w.n * sda.QGS_RANK * 8
+    assert 0 < small < need
+    ws = torch.empty(small, dtype=torch.uint8, device=dev())
+    codes = torch.empty_like(full.codes)
+    kmax = torch.empty_like(full.kmax)
+    L = sda.lib()
+    assert L.sda_build_qgs_codes(ctypes.byref(dims), K.data_ptr(), U.data_ptr(), codes.data_ptr(), kmax.data_ptr(),
+                                 ws.data_ptr(), small - 1, None) == sda.SDA_EWORKSPACE
+    rc = L.sda_build_qgs_codes(ctypes.byref(dims), K.data_ptr(), U.data_ptr(), codes.data_ptr(), kmax.data_ptr(),
+                               ws.data_ptr(), small, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert rc == 0
+    _sync()
+    assert torch.equal(codes, full.codes) and torch.equal(kmax, full.kmax)
+    oc, ok = qgs.codes(c.K[1, 1], c.U[1, 1])
+    np.testing.assert_array_equal(codes[1, 1].cpu().numpy(), oc)
+
+
 def test_codes_fp32_keys():
     w = _workload(B=1, Hkv=2, Hq=2, n=700, n_top=20, C=4, dtype="f32")
     c = synth.make_case(w)
